@@ -1,0 +1,81 @@
+"""Build libkda.so (HIP, gfx950) in-tree: gated_delta_rule_04_amd/lib/libkda.so.
+
+    python -m gated_delta_rule_04_amd.build        # from the repository root
+
+Each csrc/*.hip file is compiled by hipcc for gfx950 in parallel, then linked
+into one shared library.  Packed-fp32 instructions are disabled for the device
+code (hipcc's host pass warns that it does not know the feature: harmless).
+"""
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBDIR = os.path.join(PKG, "lib")
+LIB = os.path.join(LIBDIR, "libkda.so")
+ARCH = "gfx950"
+
+COMMON = [
+    "--offload-arch=" + ARCH,
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", CSRC,
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _compile(src, objdir, extra):
+    obj = os.path.join(objdir, os.path.basename(src)[:-4] + ".o")
+    cmd = [hipcc()] + COMMON + extra + ["-c", src, "-o", obj]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    noise = "is not a recognized feature for this target"
+    out = "\n".join(l for l in r.stdout.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), out))
+    return obj, out
+
+
+def build(verbose=False, extra=None, out=LIB):
+    """Compile every HIP source and link libkda.so; returns the library path."""
+    extra = list(extra or [])
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = list(ex.map(lambda s: _compile(s, objdir, extra), srcs))
+    objs = [o for o, _ in results]
+    if verbose:
+        for _, msg in results:
+            if msg.strip():
+                print(msg)
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stdout))
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,137 @@
+// C-ABI entry points of libkda.so: argument validation and kernel launches.
+// Every check runs on the host before the first HIP call; see include/kda.h.
+
+#include <limits.h>
+#include <stdint.h>
+
+#include "kda.h"
+#include "kda_common.h"
+#include "kda_launch.h"
+
+
+namespace {
+
+bool head_dims_ok(int Dk, int Dv, int g_group) {
+  const bool d_ok = (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
+  const bool g_ok = (g_group == 1 || g_group == 64) && Dk % g_group == 0;
+  return d_ok && g_ok;
+}
+
+// a*b*... <= limit in int64 without overflow
+bool prod_fits(std::initializer_list<long long> xs, long long limit) {
+  long long p = 1;
+  for (long long x : xs) {
+    if (x < 0) return false;
+    if (x != 0 && p > limit / x) return false;
+    p *= x;
+  }
+  return true;
+}
+
+size_t varlen_workspace(int num_seqs) { return ((size_t)num_seqs * sizeof(int) + 255) / 256 * 256; }
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK: success";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: invalid or inconsistent sizes";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown element type";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head size, decay grouping or dtype combination not supported";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
+  }
+  return "KDA: unknown status";
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs, int varlen, kda_dtype dt) {
+  (void)Dk;
+  (void)Dv;
+  (void)dt;
+  if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return 0;
+  return varlen ? varlen_workspace(num_seqs) : 0;
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T,
+                         int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
+  if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
+  const bool bf = dt == KDA_BF16;
+  if (!kda::prefill_supported(bf, Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen) {
+    if (B != 1) return KDA_ERR_SHAPE;
+  } else if (num_seqs != B) {
+    return KDA_ERR_SHAPE;
+  }
+  const int N = num_seqs;
+  // element counts must fit in int64 and units in int32
+  if (!prod_fits({B, T, H, Dk > Dv ? Dk : Dv}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  if (!prod_fits({N, H, Dk, Dv}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  if (!prod_fits({B, T}, INT_MAX)) return KDA_ERR_SHAPE;
+  if (!prod_fits({N, H}, INT_MAX / 16)) return KDA_ERR_SHAPE;
+  const bool has_tokens = (long long)B * T > 0;
+  if (has_tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+  const size_t need = kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, N, varlen, dt);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long long units = (long long)N * H;
+  if (units == 0) return KDA_OK;
+  if (!has_tokens && !ht) return KDA_OK;
+
+  int* order = nullptr;
+  if (varlen) {
+    order = static_cast<int*>(workspace);
+    if (kda::launch_varlen_order(cu_seqlens, N, T, order, s) != hipSuccess) return KDA_ERR_HIP;
+  }
+  kda::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.h0 = h0;
+  a.o = o;
+  a.ht = ht;
+  a.cu_seqlens = cu_seqlens;
+  a.order = order;
+  a.num_units = (int)units;
+  a.H = H;
+  a.T = T;
+  const int vs = kda::prefill_slice_width(bf, Dk, Dv, units, device_cus());
+  if (kda::launch_prefill(bf, Dk, Dv, g_group, vs, a, s) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              float* state, void* o, int N, int H, int Dk, int Dv, int g_group, kda_dtype dt,
+                              void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
+  if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
+  if (!prod_fits({N, H}, INT_MAX)) return KDA_ERR_SHAPE;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+  if (kda::launch_decode(dt == KDA_BF16, Dk, Dv, g_group, q, k, v, g, beta, state, o, N * H,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// KDA recurrent decode step (one token per sequence, every head), gfx950.
+//
+// The decode form of the miniKimiK3 card's Kimi Delta Attention bullet
+// ("Architecture" section): a fixed d_k x d_v state per head, constant cost
+// per token.  Per (sequence, head), with alpha = exp(g):
+//
+//     S'  = Diag(alpha) S                      decay (key channels = rows)
+//     e   = S'^T k,  y = S'^T q                 two reductions over the rows
+//     u   = beta (v - e)                        delta-rule correction
+//     o   = y + (q . k) u                       = (S' + k u^T)^T q
+//     S  <- S' + k u^T                          written back in place
+//
+// The step is bound by HBM: the float32 state is read once and written once
+// (2 * 4 * Dk * Dv bytes per head); everything else is a few hundred bytes.
+// One workgroup of 256 threads owns one (sequence, head) state and keeps it in
+// registers between the read and the write, so the identity for o needs no
+// second pass.  Each thread owns 4 adjacent value columns (one 16-byte load
+// per row) and a strided set of rows; a wavefront's loads cover whole
+// contiguous rows, so every access is a fully coalesced 16-byte load/store.
+// The two column reductions run through cross-lane shuffles and a 4-wave LDS
+// exchange.
+
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <int DK, int DV, typename T, int GG>
+__global__ __launch_bounds__(256) void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          const T* __restrict__ v, const T* __restrict__ g,
+                                                          const T* __restrict__ beta, float* __restrict__ state,
+                                                          T* __restrict__ o) {
+  constexpr int NT = 256;
+  constexpr int CG = DV / 4;         // column groups of 4 floats
+  constexpr int RG = NT / CG;        // row groups
+  constexpr int RPT = DK / RG;       // rows per thread
+  constexpr int WAVES = NT / kWave;
+  static_assert(RG * CG == NT && RPT * RG == DK, "tile does not cover the state");
+  static_assert(kWave % CG == 0, "a column group must not straddle wavefronts");
+
+  __shared__ float s_q[DK], s_k[DK], s_a[DK];
+  __shared__ float s_red[WAVES][2][DV];
+  __shared__ float s_qk;
+
+  const int tid = threadIdx.x;
+  const size_t u = blockIdx.x;  // (sequence, head) pair
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+
+  // Issue the state loads first: they are the whole cost of the step.
+  float* S = state + u * (size_t)DK * DV;
+  f32x4 s[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int r = rg + RG * m;
+    s[m] = *reinterpret_cast<const f32x4*>(S + (size_t)r * DV + 4 * cg);
+  }
+
+  // Stage q, k and alpha = exp(g) for the key channels.
+  if (tid < DK) {
+    s_q[tid] = to_f32(q[u * DK + tid]);
+    s_k[tid] = to_f32(k[u * DK + tid]);
+    s_a[tid] = fast_exp2(kLog2e * to_f32(g[u * (DK / GG) + tid / GG]));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float p = 0.f;
+    for (int i = lane; i < DK; i += kWave) p += s_q[i] * s_k[i];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
+    if (lane == 0) s_qk = p;
+  }
+
+  // Decay in registers and accumulate the two partial column reductions.
+  f32x4 e = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int r = rg + RG * m;
+    s[m] *= s_a[r];
+    e += s[m] * s_k[r];
+    y += s[m] * s_q[r];
+  }
+  // Reduce over the row groups that share this wavefront ...
+#pragma unroll
+  for (int off = CG; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      e[c] += __shfl_xor(e[c], off);
+      y[c] += __shfl_xor(y[c], off);
+    }
+  }
+  // ... then across wavefronts through LDS.
+  if (lane < CG) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s_red[wave][0][4 * cg + c] = e[c];
+      s_red[wave][1][4 * cg + c] = y[c];
+    }
+  }
+  __syncthreads();
+  f32x4 et = {0.f, 0.f, 0.f, 0.f}, yt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      et[c] += s_red[w][0][4 * cg + c];
+      yt[c] += s_red[w][1][4 * cg + c];
+    }
+  }
+
+  const float b = to_f32(beta[u]);
+  f32x4 vv;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[u * DV + 4 * cg + c]);
+  const f32x4 uu = b * (vv - et);
+
+  if (rg == 0) {
+    const f32x4 out = yt + s_qk * uu;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[u * DV + 4 * cg + c] = from_f32<T>(out[c]);
+  }
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int r = rg + RG * m;
+    *reinterpret_cast<f32x4*>(S + (size_t)r * DV + 4 * cg) = s[m] + s_k[r] * uu;
+  }
+}
+
+template <int DK, int DV, typename T, int GG>
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                  float* state, void* o, int NH, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, GG>), dim3(NH), dim3(256), 0, stream, (const T*)q, (const T*)k,
+                     (const T*)v, (const T*)g, (const T*)beta, state, (T*)o);
+  return hipGetLastError();
+}
+
+template <typename T, int GG>
+static hipError_t launch_decode_g(int Dk, int Dv, const void* q, const void* k, const void* v, const void* g,
+                                  const void* beta, float* state, void* o, int NH, hipStream_t stream) {
+  if (Dk == 64 && Dv == 64) return launch_decode_t<64, 64, T, GG>(q, k, v, g, beta, state, o, NH, stream);
+  if (Dk == 64 && Dv == 128) return launch_decode_t<64, 128, T, GG>(q, k, v, g, beta, state, o, NH, stream);
+  if (Dk == 128 && Dv == 64) return launch_decode_t<128, 64, T, GG>(q, k, v, g, beta, state, o, NH, stream);
+  return launch_decode_t<128, 128, T, GG>(q, k, v, g, beta, state, o, NH, stream);
+}
+
+hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream) {
+  if (bf16_io) {
+    return g_group == 1 ? launch_decode_g<bf16, 1>(Dk, Dv, q, k, v, g, beta, state, o, NH, stream)
+                        : launch_decode_g<bf16, 64>(Dk, Dv, q, k, v, g, beta, state, o, NH, stream);
+  }
+  return g_group == 1 ? launch_decode_g<float, 1>(Dk, Dv, q, k, v, g, beta, state, o, NH, stream)
+                      : launch_decode_g<float, 64>(Dk, Dv, q, k, v, g, beta, state, o, NH, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,34 @@
+// Internal interface between the C-ABI layer (kda_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kda {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const float* h0;
+  void* o;
+  float* ht;
+  const int* cu_seqlens;  // NULL: batch mode
+  const int* order;       // varlen: documents by decreasing length (or NULL)
+  int num_units;          // N * H
+  int H;
+  int T;                  // batch mode: tokens per sequence; varlen: total tokens
+};
+
+hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream);
+hipError_t launch_prefill(bool bf16_io, int Dk, int Dv, int g_group, int VS, const PrefillArgs& a,
+                          hipStream_t stream);
+hipError_t launch_varlen_order(const int* cu, int N, int T, int* order, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
+int prefill_slice_width(bool bf16_io, int Dk, int Dv, long long units, int num_cus);
+bool prefill_supported(bool bf16_io, int Dk, int Dv);
+
+}  // namespace kda

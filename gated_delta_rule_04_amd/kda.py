@@ -1,0 +1,152 @@
+"""Python binding of libkda.so (ctypes): argument marshalling only.
+
+Every step of the computation runs in the HIP library; PyTorch provides device
+memory and the current HIP stream.  There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+
+    o, ht = chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=False,
+                      cu_seqlens=None)
+    o = recurrent_step(q, k, v, g, beta, state)      # state updated in place
+
+Shapes (see include/kda.h): q, k [B, T, H, Dk]; v [B, T, H, Dv];
+g [B, T, H, Dk // g_group] (g_group inferred from g's last dim); beta [B, T, H];
+states [N, H, Dk, Dv] float32.  Decode: q, k [N, H, Dk]; v [N, H, Dv];
+g [N, H, Dk // g_group]; beta [N, H].
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+_STATUS = {
+    0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+    4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
+}
+EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step", "kda_status_str",
+            "kda_abi_version"]
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().kda_status_str(status).decode()
+        super().__init__("%s failed: %s" % (where, msg))
+
+
+def lib():
+    """Load libkda.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libkda.so not found at %s; build it with "
+                           "`python -m gated_delta_rule_04_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.kda_abi_version.restype = i
+    L.kda_abi_version.argtypes = []
+    L.kda_status_str.restype = ctypes.c_char_p
+    L.kda_status_str.argtypes = [i]
+    L.kda_chunk_fwd_workspace_bytes.restype = sz
+    L.kda_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    L.kda_chunk_fwd.restype = i
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    L.kda_recurrent_step.restype = i
+    L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_bytes(B, T, H, Dk, Dv, num_seqs, varlen, dtype):
+    return int(lib().kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, int(bool(varlen)),
+                                                   KDA_BF16 if dtype == torch.bfloat16 else KDA_F32))
+
+
+def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=False, cu_seqlens=None, out=None,
+              final_state=None, workspace=None):
+    """Chunked KDA prefill.  Returns (o, ht) -- ht is None unless requested."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
+        raise ValueError("g's last dim must divide Dk")
+    g_group = Dk // g.shape[-1]
+    dt = _dt(q)
+    for t in (k, v, g, beta):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, g, beta must share one dtype")
+    if initial_state is not None and initial_state.dtype != torch.float32:
+        raise TypeError("initial_state must be float32")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _check_dev(q, k, v, g, beta, initial_state, cu_seqlens)
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    ht = final_state
+    if output_final_state and ht is None:
+        ht = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _check_dev(o, ht)
+    need = workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, q.dtype)
+    ws = workspace
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                             _ptr(ht), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, g_group, dt, _ptr(ws),
+                             0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd")
+    return o, ht
+
+
+def recurrent_step(q, k, v, g, beta, state, out=None):
+    """One KDA decode step; `state` [N, H, Dk, Dv] float32 is updated in place."""
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
+        raise ValueError("g's last dim must divide Dk")
+    g_group = Dk // g.shape[-1]
+    dt = _dt(q)
+    if state.dtype != torch.float32:
+        raise TypeError("state must be float32")
+    _check_dev(q, k, v, g, beta, state)
+    o = out if out is not None else torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
+    st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H, Dk,
+                                  Dv, g_group, dt, _stream())
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_step")
+    return o

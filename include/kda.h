@@ -1,0 +1,122 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * The method (miniKimiK3 model card, section "Architecture", Kimi Delta
+ * Attention bullet): a linear-attention mixer whose per-head state S
+ * (d_k x d_v) takes, for every token, a per-channel decay followed by one
+ * gradient-descent step on the squared read-out error of v under key k;
+ * it trains through a chunked parallel form and decodes as a fixed-size
+ * recurrence.  In matrix form, per head and token t:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,           alpha_t = exp(g_t),  g_t <= 0 per key channel
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is DEVICE memory owned by the caller.  The library
+ *   never allocates, frees or keeps a pointer after the call returns.
+ * - Tensors are dense, contiguous, row-major with the shapes given below
+ *   (token-major [B, T, H, D]; states [N, H, Dk, Dv] with Dv contiguous).
+ * - Element type of q, k, v, g, beta and o is `dt` (KDA_F32 or KDA_BF16);
+ *   states (h0, ht, state) are always float32.  bf16 is bfloat16 with
+ *   round-to-nearest-even on output.
+ * - Supported head sizes: Dk, Dv in {64, 128}.  g_group in {1, 64} is the
+ *   number of consecutive key channels that share one log-decay value
+ *   (1 = per-channel KDA decay; 64 = the "decay-g64" ablation of the
+ *   Mini-K3-1H-decay-g64 card); it must divide Dk.
+ * - All argument checks run on the host BEFORE any HIP call; a failed check
+ *   returns its status and launches nothing.  A launch error is reported as
+ *   KDA_ERR_HIP (from hipGetLastError, which also clears it).
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *   stream): no host synchronisation and no library state, so concurrent
+ *   calls from several threads are safe as long as their buffers differ.
+ * - Results are bitwise deterministic run to run (no atomics).
+ * - No query scaling: pre-scale q if a scale is wanted (o is linear in q).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  KDA_ERR_SHAPE = 2,       /* negative size, mismatched sizes, or size overflow   */
+  KDA_ERR_DTYPE = 3,       /* dt is not a kda_dtype value                         */
+  KDA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required          */
+  KDA_ERR_UNSUPPORTED = 5, /* Dk, Dv or g_group outside the supported set         */
+  KDA_ERR_HIP = 6          /* a HIP launch failed                                 */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 when no
+ * workspace is needed: without cu_seqlens).  num_seqs is the number of
+ * documents when cu_seqlens is used, else pass B.  Returns 0 for invalid
+ * sizes (kda_chunk_fwd then reports the error). */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs, int varlen,
+                                     kda_dtype dt);
+
+/* Chunked prefill (the chunked parallel form of the miniKimiK3 card's KDA
+ * bullet; chunk size 64 internally).  Computes o_t for every token and,
+ * optionally, each sequence's final state.
+ *
+ *   q, k   [B, T, H, Dk]        dt
+ *   v      [B, T, H, Dv]        dt
+ *   g      [B, T, H, Dk/g_group] dt   log(alpha) <= 0
+ *   beta   [B, T, H]            dt   write strength, in [0, 1] for a contraction
+ *   h0     [N, H, Dk, Dv] f32 or NULL (NULL = zero initial state)
+ *   o      [B, T, H, Dv]        dt   output (written for every token)
+ *   ht     [N, H, Dk, Dv] f32 or NULL (final states; may alias h0)
+ *   cu_seqlens  device int32 [num_seqs + 1] or NULL.  Non-NULL selects packed
+ *          documents (Mini-K3-1H-mamba2 README, packed-document paragraph:
+ *          state flow resets at every document boundary): B must be 1,
+ *          document n is tokens cu[n] .. cu[n+1]-1 and starts from h0[n] (or
+ *          zeros).  The caller guarantees cu[0] = 0, non-decreasing, cu[N] = T;
+ *          values are clamped into [0, T] on the device so that no access
+ *          leaves the buffers even if that is violated.  A zero-length
+ *          document gets ht[n] = h0[n] (or zeros).
+ *   num_seqs   N: number of documents with cu_seqlens, else must equal B.
+ *   workspace  device memory of at least kda_chunk_fwd_workspace_bytes(...)
+ *          bytes (may be NULL when that is 0); contents are scratch.
+ *
+ * Input domain: the chunked form references decay to the start of each
+ * 64-token chunk; per key channel the summed log-decay over any chunk must
+ * stay above -80 (a chunk decay of at least e^-80), otherwise outputs may be
+ * non-finite.  Outside that domain use kda_recurrent_step token by token.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B,
+                         int T, int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* One recurrent decode step for N sequences x H heads (the recurrence of the
+ * miniKimiK3 card's KDA bullet: constant cost per token), state in place.
+ *
+ *   q, k   [N, H, Dk]  dt;   v [N, H, Dv] dt;   g [N, H, Dk/g_group] dt;
+ *   beta   [N, H]      dt;
+ *   state  [N, H, Dk, Dv] f32, read and overwritten with S_t;
+ *   o      [N, H, Dv]  dt.
+ * N = 0 is a no-op.  Valid for any g (no chunk-decay domain limit).
+ */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              float* state, void* o, int N, int H, int Dk, int Dv, int g_group, kda_dtype dt,
+                              void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_str(kda_status s);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

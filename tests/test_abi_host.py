@@ -1,0 +1,89 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+rejects invalid arguments with its status codes before any HIP call (so these
+run without a GPU and make no compute call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_04_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL, SHAPE, DTYPE, WORKSPACE, UNSUPPORTED = 0, 1, 2, 3, 4, 5
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH), reason="libkda.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTED), names
+    L = ctypes.CDLL(kda.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = kda.lib()
+    assert L.kda_abi_version() == 1
+    for s in range(7):
+        assert L.kda_status_str(s).decode().startswith(("KDA_OK", "KDA_ERR"))
+    assert L.kda_status_str(99)
+
+
+P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def fwd(q=P, k=P, v=P, g=P, beta=P, h0=None, o=P, ht=None, cu=None, N=1, B=1, T=64, H=1, Dk=64, Dv=64, gg=1, dt=1,
+        ws=None, wsb=0):
+    return kda.lib().kda_chunk_fwd(q, k, v, g, beta, h0, o, ht, cu, N, B, T, H, Dk, Dv, gg, dt, ws, wsb, None)
+
+
+def test_chunk_fwd_validation():
+    assert fwd(dt=7) == DTYPE
+    assert fwd(T=-1) == SHAPE
+    assert fwd(H=0) == SHAPE
+    assert fwd(Dk=96) == UNSUPPORTED
+    assert fwd(Dv=256) == UNSUPPORTED
+    assert fwd(gg=32) == UNSUPPORTED
+    assert fwd(dt=0, Dk=128) == UNSUPPORTED           # float32 prefill supports Dk = 64
+    assert fwd(N=2, B=1) == SHAPE                     # without cu_seqlens N must equal B
+    assert fwd(cu=P, B=2, N=2) == SHAPE               # varlen needs B == 1
+    assert fwd(q=None) == NULL
+    assert fwd(o=None) == NULL
+    assert fwd(cu=P, N=3, ws=None, wsb=0) == WORKSPACE
+    need = kda.lib().kda_chunk_fwd_workspace_bytes(1, 64, 1, 64, 64, 3, 1, 1)
+    assert need >= 3 * 4
+    assert fwd(cu=P, N=3, ws=P, wsb=need - 1) == WORKSPACE
+    assert kda.lib().kda_chunk_fwd_workspace_bytes(1, 64, 1, 64, 64, 1, 0, 1) == 0
+    assert fwd(B=2 ** 30, T=2 ** 30, N=2 ** 30) == SHAPE  # size overflow
+
+
+def test_chunk_fwd_nothing_to_do_is_ok_without_gpu():
+    # no sequences: nothing is launched
+    assert fwd(N=0, B=0, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+    # tokens absent and no final state requested: nothing to launch
+    assert fwd(N=2, B=2, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+
+
+def test_recurrent_step_validation():
+    L = kda.lib()
+    step = lambda q=P, state=P, N=1, H=1, Dk=64, Dv=64, gg=1, dt=1: L.kda_recurrent_step(
+        q, P, P, P, P, state, P, N, H, Dk, Dv, gg, dt, None)
+    assert step(dt=2) == DTYPE
+    assert step(N=-1) == SHAPE
+    assert step(H=0) == SHAPE
+    assert step(Dk=32) == UNSUPPORTED
+    assert step(gg=2) == UNSUPPORTED
+    assert step(q=None) == NULL
+    assert step(state=None) == NULL
+    assert step(N=0, q=None, state=None) == OK
