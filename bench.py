@@ -1,0 +1,281 @@
+"""KDA hot-path benchmark on one MI355X.
+
+One step = one pass of the whole hot path at Kimi-K3 head scale (96 KDA heads
+x 128, bf16 inputs, fp32 state):
+  * chunked prefill of one 32,768-token sequence (final state requested), and
+  * one recurrent decode step for 256 sequences (state carried across steps).
+`value` is the step's whole-job throughput, (32,768 + 256) tokens / step time;
+the prefill and decode legs are also reported separately.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+
+Prints one JSON line.  Inputs are synthetic and seeded (see
+gated_delta_rule_04_amd/inputs.py) and resident in HBM before timing starts.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import resource
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunked-prefill tokens/s + decode tokens/s; % MFMA peak, % HBM GB/s"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc", "kda_prefill.hip")
+DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc", "kda_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+
+
+def alg_prefill(B, T, H, dk, dv, g_group, elem=2, final_state=True, C=64):
+    """Algorithmic bytes and flops of one prefill call.
+    Bytes per head-token: q, k, v, g in, o out (elem bytes each), beta in;
+    plus the final fp32 state once per (sequence, head).
+    Flops per head-token: 6 dk dv (state pass: Kt S, Qt S, Kb^T U) + (C-1) dk
+    (k-k block) + (C+1) dk (q-k block) + 2 (C+1) dv (P U, Tm R) + C^2/3
+    (triangular solve), masked triangles counted at half."""
+    ht = B * T * H
+    per_tok_bytes = elem * (2 * dk + dv + dk // g_group + 1 + dv)
+    nbytes = ht * per_tok_bytes + (B * H * dk * dv * 4 if final_state else 0)
+    flops = ht * (6 * dk * dv + (C - 1) * dk + (C + 1) * dk + 2 * (C + 1) * dv + C * C / 3.0)
+    return nbytes, flops
+
+
+def alg_decode(N, H, dk, dv, g_group, elem=2):
+    """Bytes of one decode step: fp32 state read and written, inputs and o."""
+    per = 8 * dk * dv + elem * (2 * dk + dv + dk // g_group + 1 + dv)
+    return N * H * per
+
+
+def sha256_file(p):
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE,
+    valid only while the kernel source is unchanged since the counters."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = PREFILL_SRC if kernel == "prefill" else DECODE_SRC
+    want = sha256_file(src)
+    rec = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get(kernel + "_source_sha256") != want:
+        return None
+    try:
+        return float(rec[kernel + "_traffic_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(pre, dec, budget_s=12.0):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same
+    workload and scale to the step's tokens/s."""
+    import numpy as np
+    import oracle.kda_oracle as orc
+
+    f64 = lambda t: t.double().numpy()
+    wall0 = time.perf_counter()
+    cpu0 = time.process_time()
+    # prefill sample: the first 8 heads, tokens until about half the budget
+    Hs = 8
+    q, k, v, g, beta = (pre[n][0, :, :Hs] for n in ("q", "k", "v", "g", "beta"))
+    S = np.zeros((Hs, q.shape[-1], v.shape[-1]))
+    t0 = time.perf_counter()
+    ntok = 0
+    blk = 256
+    while ntok < q.shape[0] and time.perf_counter() - t0 < budget_s / 2:
+        sl = slice(ntok, ntok + blk)
+        _, S = orc.kda_sequence(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(g[sl]), f64(beta[sl]), S)
+        ntok += min(blk, q.shape[0] - ntok)
+    t_pre = time.perf_counter() - t0
+    pre_headtok_s = ntok * Hs / t_pre
+    # decode sample: 16 sequences x all heads, repeated steps
+    st = dec["steps"][0]
+    Ns = 16
+    Sd = f64(dec["state"][:Ns])
+    t0 = time.perf_counter()
+    nstep = 0
+    while time.perf_counter() - t0 < budget_s / 2:
+        Sd, _ = orc.kda_decode_step(Sd, *(f64(st[n][:Ns]) for n in ("q", "k", "v", "g", "beta")))
+        nstep += 1
+    t_dec = time.perf_counter() - t0
+    dec_pairs_s = nstep * Ns * Sd.shape[1] / t_dec
+    wall = time.perf_counter() - wall0
+    cores = max(1, round((time.process_time() - cpu0) / wall))
+    B, T, H = pre["q"].shape[:3]
+    N = dec["state"].shape[0]
+    t_step = B * T * H / pre_headtok_s + N * H / dec_pairs_s
+    return {
+        "value": (B * T + N) / t_step,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": ("fp64 numpy oracle: prefill on %d of %d heads x %d tokens (%.1f s), decode step on %d of %d "
+                   "sequences x %d heads x %d steps (%.1f s); step time scaled to all heads and sequences"
+                   % (Hs, H, ntok, t_pre, Ns, N, H, nstep, t_dec)),
+        "prefill_tokens_per_s": pre_headtok_s / H,
+        "decode_tokens_per_s": dec_pairs_s / H,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run one plain device copy of this many MiB (scale for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the KDA hot path shards by sequences and heads with no exchange, "
+              "so only --gpus 1 is supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_04_amd import inputs, kda
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "read_bytes": n, "write_bytes": n}), flush=True)
+        return
+
+    t_gen = time.perf_counter()
+    pre = inputs.workload_prefill("k3_prefill_bf16")
+    dec = inputs.workload_decode("k3_decode_bf16")
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    P = {n: pre[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+    B, T, H, dk = pre["q"].shape
+    dv = pre["v"].shape[-1]
+    g_group = pre["g_group"]
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    state = dec["state"].to(dev)
+    N = state.shape[0]
+    D = [{n: st[n].to(dev) for n in st} for st in dec["steps"]]
+    od = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        kda.chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], output_final_state=True, out=o, final_state=ht)
+        if ev is not None:
+            ev[1].record()
+        s = D[i % len(D)]
+        kda.recurrent_step(s["q"], s["k"], s["v"], s["g"], s["beta"], state, out=od)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    mean = lambda x: sum(x) / len(x)
+    ms_step = wall * 1e3 / args.steps
+    pre_avg, dec_avg = mean(pre_ms), mean(dec_ms)
+
+    pre_bytes, pre_flops = alg_prefill(B, T, H, dk, dv, g_group)
+    dec_bytes = alg_decode(N, H, dk, dv, g_group)
+    pre_gbs = pre_bytes / (pre_avg * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+    pre_tfs = pre_flops / (pre_avg * 1e-3) / 1e12
+    tokens = B * T + N
+    traffic_p = read_traffic("prefill")
+    traffic_d = read_traffic("decode")
+
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "kimi_k3_heads: prefill B=1 T=32768 H=96 dk=dv=128 + decode N=256 H=96 dk=dv=128",
+            "prefill": {"B": B, "T": T, "H": H, "dk": dk, "dv": dv, "g_group": g_group, "final_state": True},
+            "decode": {"N": N, "H": H, "dk": dk, "dv": dv, "g_group": g_group, "state": "fp32"},
+            "io_dtype": "bf16", "state_dtype": "fp32", "accumulate": "fp32",
+        },
+        "roofline": {
+            "kernel": "chunk_fwd_kernel (prefill)",
+            "bound": "hbm",
+            "achieved": pre_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": pre_gbs / PEAK_HBM_GBS,
+            "traffic": traffic_p,
+            "alg_bytes_per_launch": pre_bytes,
+            "avg_launch_ms": pre_avg,
+        },
+        "roofline_decode": {
+            "kernel": "decode_step_kernel",
+            "bound": "hbm",
+            "achieved": dec_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": dec_gbs / PEAK_HBM_GBS,
+            "traffic": traffic_d,
+            "alg_bytes_per_launch": dec_bytes,
+            "avg_launch_ms": dec_avg,
+        },
+        "prefill": {
+            "tokens_per_s": B * T / (pre_avg * 1e-3),
+            "ms": pre_avg,
+            "ms_min": min(pre_ms),
+            "alg_tflops": pre_tfs,
+            "mfma_frac_alg": pre_tfs / PEAK_BF16_TFLOPS,
+            "hbm_frac_alg": pre_gbs / PEAK_HBM_GBS,
+        },
+        "decode": {
+            "tokens_per_s": N / (dec_avg * 1e-3),
+            "ms_per_step": dec_avg,
+            "ms_min": min(dec_ms),
+            "hbm_frac_alg": dec_gbs / PEAK_HBM_GBS,
+        },
+        "event_ms_per_step": mean(step_ms),
+        "input_gen_s": t_gen,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pre, dec)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

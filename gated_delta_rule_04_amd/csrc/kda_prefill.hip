@@ -153,6 +153,52 @@ __device__ __forceinline__ f32x4 load4<float>(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
+
+template <typename T>
+struct Pair;
+template <>
+struct Pair<bf16> {
+  typedef bf16x2 type;
+};
+template <>
+struct Pair<float> {
+  typedef f32x2 type;
+};
+__device__ __forceinline__ f32x2 unpack2(bf16x2 x) { return f32x2{(float)x[0], (float)x[1]}; }
+__device__ __forceinline__ f32x2 unpack2(f32x2 x) { return x; }
+
+// Store N consecutive values (a contiguous run) with the widest aligned stores.
+template <typename E, int N>
+__device__ __forceinline__ void store_run(E* p, const float (&x)[N]) {
+  if constexpr (sizeof(E) == 2) {
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N; i += 8) {
+        bf16x8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (bf16)x[i + j];
+        *reinterpret_cast<bf16x8*>(p + i) = v;
+      }
+    } else if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < N; i += 4)
+        *reinterpret_cast<bf16x4*>(p + i) = bf16x4{(bf16)x[i], (bf16)x[i + 1], (bf16)x[i + 2], (bf16)x[i + 3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; i += 2) *reinterpret_cast<bf16x2*>(p + i) = bf16x2{(bf16)x[i], (bf16)x[i + 1]};
+    }
+  } else {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < N; i += 4)
+        *reinterpret_cast<f32x4*>(p + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; i += 2) *reinterpret_cast<f32x2*>(p + i) = f32x2{x[i], x[i + 1]};
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launch geometry and LDS layout.
 // ---------------------------------------------------------------------------
@@ -279,60 +325,87 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(PrefillArgs args) {
     }
   }
 
+  // ---- raw inputs of one chunk, held in registers (prefetched) ----
+  // Gating map: thread = (channel pair, block of RPB consecutive tokens).
+  // V map: thread = (value-column pair, block of VRPT consecutive tokens).
+  constexpr int RPB = Cfg::RPB;
+  constexpr int VP = VS / 2, VRG = Cfg::NT / VP, VRPT = C / VRG;
+  typedef typename Pair<T>::type P2;
+  const int pr = tid % Cfg::PAIRS, rb = tid / Cfg::PAIRS;
+  const int ch = 2 * pr;
+  const int vcp = tid % VP, vrg = tid / VP;
+  P2 rq[RPB], rk[RPB], rg[GG == 1 ? RPB : 1], rv[VRPT];
+  T rgs[GG == 1 ? 1 : RPB], rbeta;
+  // Loads are clamped to the last valid token so that they are branch-free
+  // and can all be in flight together; out-of-range rows are zeroed at use.
+  auto load_raw = [&](int ck) {
+    const int cbase = ck * C;
+#pragma unroll
+    for (int j = 0; j < RPB; ++j) {
+      const int pos = min(cbase + rb * RPB + j, len - 1);
+      const size_t tk = (size_t)(tok0 + pos) * H + h;
+      rq[j] = *reinterpret_cast<const P2*>(gq + tk * DK + ch);
+      rk[j] = *reinterpret_cast<const P2*>(gk + tk * DK + ch);
+      if constexpr (GG == 1)
+        rg[j] = *reinterpret_cast<const P2*>(gg + tk * DK + ch);
+      else
+        rgs[j] = gg[tk * (DK / GG) + ch / GG];
+    }
+#pragma unroll
+    for (int j = 0; j < VRPT; ++j) {
+      const int pos = min(cbase + vrg * VRPT + j, len - 1);
+      rv[j] = *reinterpret_cast<const P2*>(gv + ((size_t)(tok0 + pos) * H + h) * DV + col0 + 2 * vcp);
+    }
+    if (tid < C) rbeta = gb[(size_t)(tok0 + min(cbase + tid, len - 1)) * H + h];
+  };
+
   const int nchunks = (len + C - 1) / C;
+  if (nchunks > 0) load_raw(0);
   for (int ck = 0; ck < nchunks; ++ck) {
     const int cbase = ck * C;  // token offset of the chunk within the sequence
     __syncthreads();           // previous chunk's readers are done
 
-    // ================= phase 1: load, cumulative decay, gated operands ======
+    // ================= phase 1: cumulative decay, gated operands ============
     {
-      const int pr = tid % Cfg::PAIRS, rb = tid / Cfg::PAIRS;
-      const int ch = 2 * pr;
-      f32x2 qv[Cfg::RPB], kv[Cfg::RPB], G[Cfg::RPB];
+      f32x2 qv[RPB], kv[RPB], G[RPB];
       float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < Cfg::RPB; ++j) {
-        const int r = rb * Cfg::RPB + j;
-        const int pos = cbase + r;
-        f32x2 gx = {0.f, 0.f};
-        qv[j] = f32x2{0.f, 0.f};
-        kv[j] = f32x2{0.f, 0.f};
-        if (pos < len) {
-          const size_t tk = (size_t)(tok0 + pos) * H + h;
-          qv[j] = load2(gq + tk * DK + ch);
-          kv[j] = load2(gk + tk * DK + ch);
-          if (GG == 1) {
-            gx = load2(gg + tk * DK + ch);
-          } else {
-            const float gs = to_f32(gg[tk * (DK / GG) + ch / GG]);
-            gx = f32x2{gs, gs};
-          }
+      for (int j = 0; j < RPB; ++j) {
+        const bool ok = cbase + rb * RPB + j < len;
+        f32x2 gx;
+        if constexpr (GG == 1) {
+          gx = unpack2(rg[j]);
+        } else {
+          const float gs = to_f32(rgs[j]);
+          gx = f32x2{gs, gs};
         }
+        const f32x2 z = {0.f, 0.f};
+        qv[j] = ok ? unpack2(rq[j]) : z;
+        kv[j] = ok ? unpack2(rk[j]) : z;
+        gx = ok ? gx : z;
         acc0 += gx[0] * kLog2e;
         acc1 += gx[1] * kLog2e;
         G[j] = f32x2{acc0, acc1};
       }
       sm.gsum[rb][ch] = acc0;
       sm.gsum[rb][ch + 1] = acc1;
-      // V slice, transposed: vr[col][token]
+      // V slice, transposed: vr[col][token], one contiguous run per column
       {
-        constexpr int VP = VS / 2, VRG = Cfg::NT / VP, VRPT = C / VRG;
-        const int cp = tid % VP, vrg = tid / VP;
+        float v0[VRPT], v1[VRPT];
 #pragma unroll
         for (int j = 0; j < VRPT; ++j) {
-          const int r = vrg + VRG * j;
-          const int pos = cbase + r;
-          f32x2 x = {0.f, 0.f};
-          if (pos < len) x = load2(gv + ((size_t)(tok0 + pos) * H + h) * DV + col0 + 2 * cp);
-          sm.vr[2 * cp][r] = from_f32<E>(x[0]);
-          sm.vr[2 * cp + 1][r] = from_f32<E>(x[1]);
+          const bool ok = cbase + vrg * VRPT + j < len;
+          const f32x2 x = unpack2(rv[j]);
+          v0[j] = ok ? x[0] : 0.f;
+          v1[j] = ok ? x[1] : 0.f;
         }
+        store_run<E, VRPT>(&sm.vr[2 * vcp][vrg * VRPT], v0);
+        store_run<E, VRPT>(&sm.vr[2 * vcp + 1][vrg * VRPT], v1);
       }
-      if (tid < C) {
-        const int pos = cbase + tid;
-        sm.beta[tid] = pos < len ? to_f32(gb[(size_t)(tok0 + pos) * H + h]) : 0.f;
-      }
+      if (tid < C) sm.beta[tid] = cbase + tid < len ? to_f32(rbeta) : 0.f;
       __syncthreads();
+      // the next chunk's raw loads fly while this chunk is computed
+      if (ck + 1 < nchunks) load_raw(ck + 1);
       float off0 = 0.f, off1 = 0.f, tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
       for (int b = 0; b < Cfg::NRB; ++b) {
@@ -349,18 +422,22 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(PrefillArgs args) {
         sm.gam[ch] = eT0;
         sm.gam[ch + 1] = eT1;
       }
+      float kb0[RPB], kb1[RPB];
 #pragma unroll
-      for (int j = 0; j < Cfg::RPB; ++j) {
-        const int r = rb * Cfg::RPB + j;
+      for (int j = 0; j < RPB; ++j) {
+        const int r = rb * RPB + j;
         const float G0 = off0 + G[j][0], G1 = off1 + G[j][1];
         const float e0 = fast_exp2(G0), e1 = fast_exp2(G1);
         const float n0 = fast_exp2(-G0), n1 = fast_exp2(-G1);
         store2(&sm.q[r][ch], qv[j][0] * e0, qv[j][1] * e1);
         store2(&sm.k[r][ch], kv[j][0] * e0, kv[j][1] * e1);
-        store2(&sm.u1.kh[r][ch], kv[j][0] * n0, kv[j][1] * n1);
-        sm.kbt[ch][r] = from_f32<E>(kv[j][0] * n0 * eT0);
-        sm.kbt[ch + 1][r] = from_f32<E>(kv[j][1] * n1 * eT1);
+        const float h0v = kv[j][0] * n0, h1v = kv[j][1] * n1;
+        store2(&sm.u1.kh[r][ch], h0v, h1v);
+        kb0[j] = h0v * eT0;
+        kb1[j] = h1v * eT1;
       }
+      store_run<E, RPB>(&sm.kbt[ch][rb * RPB], kb0);
+      store_run<E, RPB>(&sm.kbt[ch + 1][rb * RPB], kb1);
     }
     __syncthreads();
 
