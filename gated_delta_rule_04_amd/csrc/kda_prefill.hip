@@ -49,28 +49,6 @@ struct Mma;
 
 template <>
 struct Mma<bf16> {
-  static constexpr int KSTEP = 32;
-  // acc += A[16 x K] * B[K x 16]
-  template <int K>
-  __device__ __forceinline__ static void run(f32x4& acc, const bf16* A, int lda, const bf16* Bt, int ldb, int lane) {
-    const int r = lane & 15, kg = lane >> 4;
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 32) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k0 + 8 * kg);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + k0 + 8 * kg);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-    }
-  }
-  // Runtime K (multiple of 32).
-  __device__ __forceinline__ static void run_n(f32x4& acc, const bf16* A, int lda, const bf16* Bt, int ldb, int K,
-                                               int lane) {
-    const int r = lane & 15, kg = lane >> 4;
-    for (int k0 = 0; k0 < K; k0 += 32) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k0 + 8 * kg);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + k0 + 8 * kg);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-    }
-  }
   // acc += A[16 x 16] * B[16 x 16], A given in float32 (converted), B transposed.
   __device__ __forceinline__ static void run16_fa(f32x4& acc, const float* A, int lda, const bf16* Bt, int ldb,
                                                   int lane) {
@@ -96,30 +74,31 @@ struct Mma<bf16> {
 
 template <>
 struct Mma<float> {
-  static constexpr int KSTEP = 4;
-  template <int K>
-  __device__ __forceinline__ static void run(f32x4& acc, const float* A, int lda, const float* Bt, int ldb,
-                                             int lane) {
+  // acc += A[16 x 16] * B[16 x 16] (B transposed), four 16x16x4 steps.
+  template <typename TA>
+  __device__ __forceinline__ static void run16_any(f32x4& acc, const TA* A, int lda, const float* Bt, int ldb,
+                                                   int lane) {
     const int r = lane & 15, kg = lane >> 4;
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + kg], Bt[r * ldb + k0 + kg], acc, 0, 0, 0);
-  }
-  __device__ __forceinline__ static void run_n(f32x4& acc, const float* A, int lda, const float* Bt, int ldb, int K,
-                                               int lane) {
-    const int r = lane & 15, kg = lane >> 4;
-    for (int k0 = 0; k0 < K; k0 += 4)
+    for (int k0 = 0; k0 < 16; k0 += 4)
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + kg], Bt[r * ldb + k0 + kg], acc, 0, 0, 0);
   }
   __device__ __forceinline__ static void run16_fa(f32x4& acc, const float* A, int lda, const float* Bt, int ldb,
                                                   int lane) {
-    run<16>(acc, A, lda, Bt, ldb, lane);
+    run16_any(acc, A, lda, Bt, ldb, lane);
   }
   __device__ __forceinline__ static void run16(f32x4& acc, const float* A, int lda, const float* Bt, int ldb,
                                                int lane) {
-    run<16>(acc, A, lda, Bt, ldb, lane);
+    run16_any(acc, A, lda, Bt, ldb, lane);
   }
 };
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// traffic, not for its global loads/stores, so prefetched global loads stay
+// in flight across it (the compiler waits for them at their first use).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Completes this wave's own LDS writes before it reads them back.
+__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Two adjacent elements, loaded as one 4- or 8-byte access.
 __device__ __forceinline__ f32x2 load2(const bf16* p) {
@@ -139,7 +118,8 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, const f32x4& v) {
 }
 template <>
 __device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
-  *reinterpret_cast<f32x4*>(p) = v;
+  *reinterpret_cast<f32x2*>(p) = f32x2{v[0], v[1]};
+  *reinterpret_cast<f32x2*>(p + 2) = f32x2{v[2], v[3]};
 }
 template <typename E>
 __device__ __forceinline__ f32x4 load4(const E* p);
@@ -150,7 +130,8 @@ __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 }
 template <>
 __device__ __forceinline__ f32x4 load4<float>(const float* p) {
-  return *reinterpret_cast<const f32x4*>(p);
+  const f32x2 a = *reinterpret_cast<const f32x2*>(p), b = *reinterpret_cast<const f32x2*>(p + 2);
+  return f32x4{a[0], a[1], b[0], b[1]};
 }
 
 
@@ -167,36 +148,93 @@ struct Pair<float> {
 __device__ __forceinline__ f32x2 unpack2(bf16x2 x) { return f32x2{(float)x[0], (float)x[1]}; }
 __device__ __forceinline__ f32x2 unpack2(f32x2 x) { return x; }
 
-// Store N consecutive values (a contiguous run) with the widest aligned stores.
+// Store N consecutive values (a contiguous run) with 8-byte stores (LDS rows
+// are 8-byte aligned: their pitches are skewed by 8 bytes against bank conflicts).
 template <typename E, int N>
 __device__ __forceinline__ void store_run(E* p, const float (&x)[N]) {
   if constexpr (sizeof(E) == 2) {
-    if constexpr (N % 8 == 0) {
-#pragma unroll
-      for (int i = 0; i < N; i += 8) {
-        bf16x8 v;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (bf16)x[i + j];
-        *reinterpret_cast<bf16x8*>(p + i) = v;
-      }
-    } else if constexpr (N % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < N; i += 4)
-        *reinterpret_cast<bf16x4*>(p + i) = bf16x4{(bf16)x[i], (bf16)x[i + 1], (bf16)x[i + 2], (bf16)x[i + 3]};
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; i += 2) *reinterpret_cast<bf16x2*>(p + i) = bf16x2{(bf16)x[i], (bf16)x[i + 1]};
-    }
-  } else {
     if constexpr (N % 4 == 0) {
 #pragma unroll
       for (int i = 0; i < N; i += 4)
-        *reinterpret_cast<f32x4*>(p + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+        *reinterpret_cast<bf16x4*>(p + i) = bf16x4{(bf16)x[i], (bf16)x[i + 1], (bf16)x[i + 2], (bf16)x[i + 3]};
+    } else if constexpr (N % 2 == 0) {
+#pragma unroll
+      for (int i = 0; i < N; i += 2) *reinterpret_cast<bf16x2*>(p + i) = bf16x2{(bf16)x[i], (bf16)x[i + 1]};
     } else {
 #pragma unroll
+      for (int i = 0; i < N; ++i) p[i] = (bf16)x[i];
+    }
+  } else {
+    if constexpr (N % 2 == 0) {
+#pragma unroll
       for (int i = 0; i < N; i += 2) *reinterpret_cast<f32x2*>(p + i) = f32x2{x[i], x[i + 1]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) p[i] = x[i];
     }
   }
+}
+
+// Store NP element pairs as one contiguous run of 2*NP elements.
+template <typename E, int NP>
+__device__ __forceinline__ void store_pairs(E* p, const typename Pair<E>::type (&x)[NP]) {
+  if constexpr (sizeof(E) == 2 && NP % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < NP; i += 2)
+      *reinterpret_cast<bf16x4*>(p + 2 * i) = __builtin_shufflevector(x[i], x[i + 1], 0, 1, 2, 3);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) *reinterpret_cast<typename Pair<E>::type*>(p + 2 * i) = x[i];
+  }
+}
+
+// Raw buffer access: a per-chunk descriptor bounds every access, so loads of
+// rows past the end of a sequence return zero (the inert zero padding of a
+// partial chunk) and stores past the end are dropped -- no clamping, masking
+// or branches.  Offsets are 32-bit byte offsets within the chunk.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename P>
+__device__ __forceinline__ P bload(rsrc_t r, int off) {
+  if constexpr (sizeof(P) == 2)
+    return __builtin_bit_cast(P, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+  else if constexpr (sizeof(P) == 4)
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+// Eight consecutive elements, loaded with 16-byte accesses.
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  typedef bf16x8 type;
+  __device__ __forceinline__ static type load(rsrc_t r, int off) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+};
+template <>
+struct Vec8<float> {
+  typedef f32x8 type;
+  __device__ __forceinline__ static type load(rsrc_t r, int off) {
+    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+template <typename V>
+__device__ __forceinline__ float elem(const V& v, int i) {
+  return (float)v[i];
+}
+
+__device__ __forceinline__ void bstore(bf16 x, rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore(float x, rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), r, off, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -208,66 +246,190 @@ struct PrefillCfg {
   typedef T_ E;  // MFMA operand type (bf16 path: bf16; f32 path: float)
   static constexpr int DK = DK_, DV = DV_, VS = VS_, GG = GG_;
   static constexpr int C = 64;                   // chunk length
-  static constexpr int NT = 256;                 // threads per workgroup
-  static constexpr int PADE = 16 / sizeof(E);    // 16-byte row skew
+  static constexpr int NA = 256;                 // producer threads (4 wavefronts)
+  static constexpr int RT = VS / 16;             // value-column tiles per slice
+  static constexpr int TPW = RT >= 2 ? 2 : 1;    // value tiles per state wavefront
+  static constexpr int NBW = RT / TPW;           // state wavefronts
+  static constexpr int NT = NA + 64 * NBW;       // threads per workgroup
+  static constexpr int PADE = 8 / sizeof(E);     // 8-byte row skew: pitch = 2 (mod 32) dwords
   static constexpr int KP = DK + PADE;           // pitch of [*][DK] operand tiles
   static constexpr int CP = C + PADE;            // pitch of [*][C] operand tiles
   static constexpr int AP = C + 4;               // pitch of the fp32 A tile
   static constexpr int XP = 16 + PADE;           // pitch of 16x16 solve tiles
-  static constexpr int PAIRS = DK / 2;           // gating: channel pairs
-  static constexpr int NRB = NT / PAIRS;         // gating: row blocks
+  static constexpr int CGN = DK / 8;             // gating: groups of 8 key channels
+  static constexpr int NRB = NA / CGN;           // gating: row blocks
   static constexpr int RPB = C / NRB;            // gating: rows per block
-  static constexpr int RT = VS / 16;             // value-column tiles per slice
-  static constexpr int SMT = DK / 64;            // state row tiles per wave
+  static constexpr int RBW = 64 / CGN;           // gating: row blocks per wavefront
+  static constexpr int VCG = VS / 8;             // V: groups of 8 value columns
+  static constexpr int VRPT = VS >= 32 ? VS / 32 : 1;  // V: rows per loading thread
+  static constexpr int VTH = 64 * VCG / VRPT;    // V: loading threads
+  static constexpr int KT = DK / 16;             // key-channel tiles
   static constexpr int NS = DV / VS;             // slices per head
   static_assert(DK == 64 || DK == 128, "DK");
-  static_assert(VS % 16 == 0 && DV % VS == 0, "VS");
-  static_assert(NRB * PAIRS == NT && RPB * NRB == C, "gating map");
+  static_assert(VS % 16 == 0 && DV % VS == 0 && RT % TPW == 0, "VS");
+  static_assert(NRB * CGN == NA && RPB * NRB == C && RPB % 2 == 0 && RBW * CGN == 64, "gating map");
+  static_assert(VTH <= NA && VTH * VRPT == 64 * VCG, "V map");
 };
 
 template <class Cfg>
 struct Smem {
   typedef typename Cfg::E E;
-  E q[Cfg::C][Cfg::KP];    // Qt
-  E k[Cfg::C][Cfg::KP];    // Kt
-  union {
-    E kh[Cfg::C][Cfg::KP];  // Kh (live until A and P are formed)
-    struct {
-      E xt[Cfg::C][Cfg::CP];        // X^T, X = (I + A)^-1   (solve)
-      E xd[4][16][Cfg::XP];         // diagonal blocks of X, row-major
-      E m[4][16][Cfg::XP];          // per-wave 16x16 scratch (transposed)
-    } sv;
-  } u1;
-  E kbt[Cfg::DK][Cfg::CP];  // Kb^T (key channel major)
-  float a[Cfg::C][Cfg::AP];  // A (fp32)
-  E t[Cfg::C][Cfg::CP];     // Tm row-major
-  E p[Cfg::C][Cfg::CP];     // P row-major
-  E vr[Cfg::VS][Cfg::CP];   // V^T, overwritten by R^T
-  E uu[Cfg::VS][Cfg::CP];   // U^T
-  E s[Cfg::VS][Cfg::KP];    // S^T (operand copy of the state)
+  E q[Cfg::C][Cfg::KP];     // Qt = Q e^G          (token-major)
+  E k[Cfg::C][Cfg::KP];     // Kt = K e^G          (token-major)
+  E kh[Cfg::C][Cfg::KP];    // Kh = K e^-G         (token-major)
+  E kht[Cfg::DK][Cfg::CP];  // Kh^T                (key-channel-major)
+  E vt[Cfg::VS][Cfg::CP];   // V^T of the slice    (value-column-major)
+  E t[Cfg::C][Cfg::CP];     // Tm = (I + A)^-1 Diag(b), row-major
+  E p[Cfg::C][Cfg::CP];     // P, row-major
+  alignas(16) float a[Cfg::C][Cfg::AP];  // A (fp32), rows 16-byte aligned
+  alignas(16) float xd[4][16][20];  // diagonal blocks of X = (I + A)^-1, row-major (fp32)
   float beta[Cfg::C];
-  float gam[Cfg::DK];       // e^{G_C}
-  float gsum[Cfg::NRB][Cfg::DK];
+  alignas(16) float gam[Cfg::DK];  // e^{G_C}
+  alignas(16) float gsum[4][Cfg::DK];  // per-wavefront log2-decay totals
 };
 
-// Lower-triangular 16x16 tiles (I, J), J <= I, in the order used for A and P.
-__constant__ const int kTriI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ const int kTriJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// MFMA fragments with a k order that matches the accumulator layout, so that
+// accumulators (S, R, U) feed the next product as B operands straight from
+// registers.  bf16 (16x16x32): slab s covers k = 32s .. 32s+31 and lane group
+// kg holds k = 32s + 4kg + {0..3} and 32s + 16 + 4kg + {0..3}, i.e. rows
+// 4kg..4kg+3 of accumulator tiles 2s and 2s+1.  fp32 (16x16x4): slab s
+// covers k = 16(s/4) + 4kg + (s%4), i.e. element s%4 of accumulator tile s/4.
+template <typename E>
+struct Frag;
 
+template <>
+struct Frag<bf16> {
+  typedef bf16x8 V;
+  static constexpr int SLAB = 32;
+  // From a row-major LDS row (the lane's row of an A or Bt tile).
+  __device__ __forceinline__ static V ld(const bf16* row, int s, int kg) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * s + 4 * kg);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * s + 16 + 4 * kg);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // From accumulator tiles x (tile 2s) and y (tile 2s + 1).
+  __device__ __forceinline__ static V acc2(const f32x4& x, const f32x4& y) {
+    return V{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3], (bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+  }
+  __device__ __forceinline__ static f32x4 mma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
 
+template <>
+struct Frag<float> {
+  typedef float V;
+  static constexpr int SLAB = 4;
+  __device__ __forceinline__ static V ld(const float* row, int s, int kg) {
+    return row[16 * (s >> 2) + 4 * kg + (s & 3)];
+  }
+  __device__ __forceinline__ static f32x4 mma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// 16x16 products with both operands in accumulator form: prod(At, B) = A * B,
+// where At holds A^T and B holds B in the accumulator layout (lane l: rows
+// 4(l/16) + i of column l % 16).  The accumulator form of a matrix is its
+// B-operand layout and the accumulator form of its transpose is its
+// A-operand layout, so chains of products never leave registers.  bf16: each
+// operand is split into bf16 hi + lo parts (three MFMAs), which keeps the
+// product accurate to about 2^-16 relative; fp32: four 16x16x4 steps.
+template <typename E>
+struct Reg16;
+template <>
+struct Reg16<bf16> {
+  __device__ __forceinline__ static void split(const f32x4& x, s16x4& hi, s16x4& lo) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = (bf16)x[i];
+      l[i] = (bf16)(x[i] - (float)h[i]);
+    }
+    hi = __builtin_bit_cast(s16x4, h);
+    lo = __builtin_bit_cast(s16x4, l);
+  }
+  __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) {
+    s16x4 ah, al, bh, bl;
+    split(At, ah, al);
+    split(B, bh, bl);
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+    return c;
+  }
+};
+template <>
+struct Reg16<float> {
+  __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(At[i], B[i], c, 0, 0, 0);
+    return c;
+  }
+};
+
+// (I + N)^-1 for a strictly lower 16x16 N (nilpotent, N^16 = 0), as the
+// product (I + N^8)(I + N^4)(I + N^2)(I - N) = sum_{k<16} (-N)^k.
+// N and Nt are N and N^T in accumulator form; returns X in accumulator form.
+template <typename E>
+__device__ __forceinline__ f32x4 unit_lower_inverse16(const f32x4& N, const f32x4& Nt, int lane) {
+  typedef Reg16<E> R;
+  f32x4 I4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) I4[i] = (4 * (lane >> 4) + i == (lane & 15)) ? 1.f : 0.f;
+  const f32x4 N2 = R::prod(Nt, N), N2t = R::prod(N, Nt);
+  const f32x4 N4 = R::prod(N2t, N2), N4t = R::prod(N2, N2t);
+  const f32x4 N8t = R::prod(N4, N4t);
+  const f32x4 Z1 = R::prod(I4 + N2t, I4 - N);
+  const f32x4 Z2 = R::prod(I4 + N4t, Z1);
+  return R::prod(I4 + N8t, Z2);
+}
+
+// B-operand fragment of slab s from accumulator tiles acc[0..n) along k.
+template <int N>
+__device__ __forceinline__ bf16x8 acc_frag(const f32x4 (&acc)[N], int s, bf16) {
+  return Frag<bf16>::acc2(acc[2 * s], acc[2 * s + 1]);
+}
+template <int N>
+__device__ __forceinline__ float acc_frag(const f32x4 (&acc)[N], int s, float) {
+  return acc[s >> 2][s & 3];
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.  Wavefronts 0-3 (producer) prepare chunk c+1 -- gating, the
+// k-k and q-k blocks and the UT transform -- while wavefronts 4.. (state)
+// run the state pass of chunk c.  One iteration, between LDS barriers:
+//
+//   X0 | producer: decay block sums, V^T, beta  | state: U = Tm R, O += P U, o
+//  MID | producer: gated Qt, Kt, Kh             | state: S <- e^{G_C} (S + Kh^T U)
+//   X1 | producer: A, P, diagonal solve blocks  | state: R = V - Kt S
+//   X2 | producer: off-diagonal solve, Kh^T, e^G| state: O = Qt S
+//
+// Each state wavefront owns TPW 16-column tiles of the slice and keeps S,
+// R/U and O in registers; from LDS it reads only producer outputs.
+// ---------------------------------------------------------------------------
 template <class Cfg>
-__global__ __launch_bounds__(256) void chunk_fwd_kernel(PrefillArgs args) {
+__global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
   typedef typename Cfg::T T;
   typedef typename Cfg::E E;
-  constexpr int DK = Cfg::DK, DV = Cfg::DV, VS = Cfg::VS, GG = Cfg::GG, C = Cfg::C;
-  constexpr int RT = Cfg::RT, SMT = Cfg::SMT, NS = Cfg::NS;
+  typedef Frag<E> F;
   typedef Mma<E> M;
+  constexpr int DK = Cfg::DK, DV = Cfg::DV, VS = Cfg::VS, GG = Cfg::GG, C = Cfg::C;
+  constexpr int NS = Cfg::NS, TPW = Cfg::TPW, KT = Cfg::KT, RPB = Cfg::RPB;
+  constexpr int VP = VS / 2, VRG = Cfg::NA / VP, VRPT = C / VRG;
+  constexpr int SLAB = F::SLAB;
+  constexpr int SK = DK / SLAB;  // slabs over key channels
+  constexpr int SC = C / SLAB;   // slabs over the chunk's tokens
 
   __shared__ Smem<Cfg> sm;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int l16 = lane & 15, kg = lane >> 4;
+  const bool producer = wave < 4;
 
   // ---- workgroup -> (unit, slice); the NS slices of a unit share an XCD ----
   const int grp = blockIdx.x / (8 * NS);
@@ -291,6 +453,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(PrefillArgs args) {
     len = args.T;
   }
   const int col0 = slice * VS;  // first value column of this slice
+  const int nchunks = (len + C - 1) / C;
 
   const T* __restrict__ gq = static_cast<const T*>(args.q);
   const T* __restrict__ gk = static_cast<const T*>(args.k);
@@ -300,7 +463,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(PrefillArgs args) {
   T* __restrict__ go = static_cast<T*>(args.o);
   const size_t state_off = ((size_t)seq * H + h) * DK * DV;
 
-  // ---- zero the upper tiles of Tm and P once (never written afterwards) ----
+  // ---- upper 16x16 tiles of Tm and P are zero and never written again ----
   for (int idx = tid; idx < C * C; idx += Cfg::NT) {
     const int r = idx / C, c = idx % C;
     if ((c >> 4) > (r >> 4)) {
@@ -309,252 +472,398 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(PrefillArgs args) {
     }
   }
 
-  // ---- initial state slice -> accumulators and operand copy ----
-  // wave w owns key-channel rows [DK/4 * w, DK/4 * (w+1)), all VS columns.
-  f32x4 S[SMT][RT];
-#pragma unroll
-  for (int mt = 0; mt < SMT; ++mt) {
-#pragma unroll
-    for (int nt = 0; nt < RT; ++nt) {
-      const int row0 = (DK / 4) * wave + 16 * mt + 4 * kg;
-      const int col = 16 * nt + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[mt][nt][i] = args.h0 ? args.h0[state_off + (size_t)(row0 + i) * DV + col0 + col] : 0.f;
-      store4<E>(&sm.s[col][row0], S[mt][nt]);
-    }
-  }
-
-  // ---- raw inputs of one chunk, held in registers (prefetched) ----
-  // Gating map: thread = (channel pair, block of RPB consecutive tokens).
-  // V map: thread = (value-column pair, block of VRPT consecutive tokens).
-  constexpr int RPB = Cfg::RPB;
-  constexpr int VP = VS / 2, VRG = Cfg::NT / VP, VRPT = C / VRG;
-  typedef typename Pair<T>::type P2;
-  const int pr = tid % Cfg::PAIRS, rb = tid / Cfg::PAIRS;
-  const int ch = 2 * pr;
-  const int vcp = tid % VP, vrg = tid / VP;
-  P2 rq[RPB], rk[RPB], rg[GG == 1 ? RPB : 1], rv[VRPT];
-  T rgs[GG == 1 ? 1 : RPB], rbeta;
-  // Loads are clamped to the last valid token so that they are branch-free
-  // and can all be in flight together; out-of-range rows are zeroed at use.
-  auto load_raw = [&](int ck) {
-    const int cbase = ck * C;
-#pragma unroll
-    for (int j = 0; j < RPB; ++j) {
-      const int pos = min(cbase + rb * RPB + j, len - 1);
-      const size_t tk = (size_t)(tok0 + pos) * H + h;
-      rq[j] = *reinterpret_cast<const P2*>(gq + tk * DK + ch);
-      rk[j] = *reinterpret_cast<const P2*>(gk + tk * DK + ch);
-      if constexpr (GG == 1)
-        rg[j] = *reinterpret_cast<const P2*>(gg + tk * DK + ch);
-      else
-        rgs[j] = gg[tk * (DK / GG) + ch / GG];
-    }
-#pragma unroll
-    for (int j = 0; j < VRPT; ++j) {
-      const int pos = min(cbase + vrg * VRPT + j, len - 1);
-      rv[j] = *reinterpret_cast<const P2*>(gv + ((size_t)(tok0 + pos) * H + h) * DV + col0 + 2 * vcp);
-    }
-    if (tid < C) rbeta = gb[(size_t)(tok0 + min(cbase + tid, len - 1)) * H + h];
-  };
-
-  const int nchunks = (len + C - 1) / C;
-  if (nchunks > 0) load_raw(0);
-  for (int ck = 0; ck < nchunks; ++ck) {
-    const int cbase = ck * C;  // token offset of the chunk within the sequence
-    __syncthreads();           // previous chunk's readers are done
-
-    // ================= phase 1: cumulative decay, gated operands ============
-    {
-      f32x2 qv[RPB], kv[RPB], G[RPB];
-      float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < RPB; ++j) {
-        const bool ok = cbase + rb * RPB + j < len;
-        f32x2 gx;
-        if constexpr (GG == 1) {
-          gx = unpack2(rg[j]);
-        } else {
-          const float gs = to_f32(rgs[j]);
-          gx = f32x2{gs, gs};
-        }
-        const f32x2 z = {0.f, 0.f};
-        qv[j] = ok ? unpack2(rq[j]) : z;
-        kv[j] = ok ? unpack2(rk[j]) : z;
-        gx = ok ? gx : z;
-        acc0 += gx[0] * kLog2e;
-        acc1 += gx[1] * kLog2e;
-        G[j] = f32x2{acc0, acc1};
-      }
-      sm.gsum[rb][ch] = acc0;
-      sm.gsum[rb][ch + 1] = acc1;
-      // V slice, transposed: vr[col][token], one contiguous run per column
-      {
-        float v0[VRPT], v1[VRPT];
-#pragma unroll
-        for (int j = 0; j < VRPT; ++j) {
-          const bool ok = cbase + vrg * VRPT + j < len;
-          const f32x2 x = unpack2(rv[j]);
-          v0[j] = ok ? x[0] : 0.f;
-          v1[j] = ok ? x[1] : 0.f;
-        }
-        store_run<E, VRPT>(&sm.vr[2 * vcp][vrg * VRPT], v0);
-        store_run<E, VRPT>(&sm.vr[2 * vcp + 1][vrg * VRPT], v1);
-      }
-      if (tid < C) sm.beta[tid] = cbase + tid < len ? to_f32(rbeta) : 0.f;
-      __syncthreads();
-      // the next chunk's raw loads fly while this chunk is computed
-      if (ck + 1 < nchunks) load_raw(ck + 1);
-      float off0 = 0.f, off1 = 0.f, tot0 = 0.f, tot1 = 0.f;
-#pragma unroll
-      for (int b = 0; b < Cfg::NRB; ++b) {
-        const float x0 = sm.gsum[b][ch], x1 = sm.gsum[b][ch + 1];
-        if (b < rb) {
-          off0 += x0;
-          off1 += x1;
-        }
-        tot0 += x0;
-        tot1 += x1;
-      }
-      const float eT0 = fast_exp2(tot0), eT1 = fast_exp2(tot1);
-      if (rb == 0) {
-        sm.gam[ch] = eT0;
-        sm.gam[ch + 1] = eT1;
-      }
-      float kb0[RPB], kb1[RPB];
+  if (producer) {
+    // ================= producer wavefronts ===================================
+    // Gating map: thread = (8 key channels, block of RPB consecutive tokens);
+    // the row blocks of one wavefront cover 16 consecutive tokens.
+    // V map: thread = (8 value columns, VRPT consecutive tokens).
+    typedef typename Vec8<T>::type V8;
+    typedef typename Pair<E>::type EP2;
+    constexpr int CGN = Cfg::CGN, RBW = Cfg::RBW;
+    constexpr int VCG = Cfg::VCG, VRPT = Cfg::VRPT, VTH = Cfg::VTH;
+    const int cg = tid % CGN, rb = tid / CGN;
+    const int ch = 8 * cg;                 // first key channel of this thread
+    const int rbw = lane / CGN;            // row block within the wavefront
+    const int vcg = tid % VCG, vrb = tid / VCG;
+    V8 rq[RPB], rk[RPB], rg[GG == 1 ? RPB : 1], rv[VRPT];
+    T rgs[GG == 1 ? 1 : RPB], rbeta;
+    // All loads of a chunk are in flight together; rows past the end of the
+    // sequence read as zero through the per-chunk buffer bounds.
+    const int rsk = H * DK * (int)sizeof(T);           // token stride of q, k (bytes)
+    const int rsg = H * (DK / GG) * (int)sizeof(T);    // token stride of g
+    const int rsv = H * DV * (int)sizeof(T);           // token stride of v
+    const int rsb = H * (int)sizeof(T);                // token stride of beta
+    auto load_raw = [&](int ck) {
+      const int cb = ck * C;
+      const int nv = min(C, len - cb);  // valid rows of this chunk (>= 1)
+      const size_t row0 = (size_t)(tok0 + cb) * H + h;
+      const rsrc_t bq = make_rsrc(gq + row0 * DK, (nv - 1) * rsk + DK * (int)sizeof(T));
+      const rsrc_t bk = make_rsrc(gk + row0 * DK, (nv - 1) * rsk + DK * (int)sizeof(T));
+      const rsrc_t bg = make_rsrc(gg + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * (int)sizeof(T));
+      const rsrc_t bv = make_rsrc(gv + row0 * DV + col0, (nv - 1) * rsv + VS * (int)sizeof(T));
+      const rsrc_t bb = make_rsrc(gb + row0, (nv - 1) * rsb + (int)sizeof(T));
 #pragma unroll
       for (int j = 0; j < RPB; ++j) {
         const int r = rb * RPB + j;
-        const float G0 = off0 + G[j][0], G1 = off1 + G[j][1];
-        const float e0 = fast_exp2(G0), e1 = fast_exp2(G1);
-        const float n0 = fast_exp2(-G0), n1 = fast_exp2(-G1);
-        store2(&sm.q[r][ch], qv[j][0] * e0, qv[j][1] * e1);
-        store2(&sm.k[r][ch], kv[j][0] * e0, kv[j][1] * e1);
-        const float h0v = kv[j][0] * n0, h1v = kv[j][1] * n1;
-        store2(&sm.u1.kh[r][ch], h0v, h1v);
-        kb0[j] = h0v * eT0;
-        kb1[j] = h1v * eT1;
+        rq[j] = Vec8<T>::load(bq, r * rsk + ch * (int)sizeof(T));
+        rk[j] = Vec8<T>::load(bk, r * rsk + ch * (int)sizeof(T));
+        if constexpr (GG == 1)
+          rg[j] = Vec8<T>::load(bg, r * rsg + ch * (int)sizeof(T));
+        else
+          rgs[j] = bload<T>(bg, r * rsg + (ch / GG) * (int)sizeof(T));
       }
-      store_run<E, RPB>(&sm.kbt[ch][rb * RPB], kb0);
-      store_run<E, RPB>(&sm.kbt[ch + 1][rb * RPB], kb1);
-    }
-    __syncthreads();
-
-    // ================= phase 2: A = strict_lower(Diag(b) Kt Kh^T), P ========
-    for (int task = wave; task < 20; task += 4) {
-      const int tri = task % 10;
-      const int I = kTriI[tri], J = kTriJ[tri];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const E* Aop = task < 10 ? &sm.k[16 * I][0] : &sm.q[16 * I][0];
-      M::template run<DK>(acc, Aop, Cfg::KP, &sm.u1.kh[16 * J][0], Cfg::KP, lane);
-      const int col = 16 * J + l16;
+      if (tid < VTH) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * I + 4 * kg + i;
-        if (task < 10) {
-          float val = acc[i] * sm.beta[row];
-          if (col >= row) val = 0.f;
-          sm.a[row][col] = val;
-        } else {
-          sm.p[row][col] = from_f32<E>(col > row ? 0.f : acc[i]);
+        for (int j = 0; j < VRPT; ++j) rv[j] = Vec8<T>::load(bv, (vrb * VRPT + j) * rsv + 8 * vcg * (int)sizeof(T));
+      }
+      if (tid < C) rbeta = bload<T>(bb, tid * rsb);
+    };
+    float G[RPB][8];        // cumulative log2-decay of this thread's rows (block-local)
+    float off[8];           // log2-decay of the chunk before this thread's block
+    float eT[8];            // e^{G_C} of this thread's channels
+    EP2 khp[8][RPB / 2];    // Kh of this thread's rows per channel (token pairs), for Kh^T
+    f32x4 Xdiag;            // X_ww = (I + A_ww)^-1 of this wave's block, accumulator form
+    if (nchunks > 0) load_raw(0);
+
+    for (int it = 0; it <= nchunks; ++it) {
+      const int cbase = it * C;  // chunk it
+      lds_barrier();  // -------------------------------------------------- X0
+      if (it < nchunks) {
+        // block-local cumulative decay; prefix over this wavefront's blocks
+        float acc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll
+        for (int j = 0; j < RPB; ++j) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float gx = GG == 1 ? elem(rg[j], c) : to_f32(rgs[j]);
+            acc[c] += gx * kLog2e;
+            G[j][c] = acc[c];
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) off[c] = acc[c];  // inclusive prefix over blocks
+#pragma unroll
+        for (int d = 1; d < RBW; d <<= 1) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float y = __shfl_up(off[c], d * CGN);
+            if (rbw >= d) off[c] += y;
+          }
+        }
+        if (rbw == RBW - 1) {
+          *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch]) = f32x4{off[0], off[1], off[2], off[3]};
+          *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch + 4]) = f32x4{off[4], off[5], off[6], off[7]};
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) off[c] -= acc[c];  // exclusive within the wavefront
+        // V^T of the slice: one contiguous run of VRPT tokens per column
+        if (tid < VTH) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            float vr[VRPT];
+#pragma unroll
+            for (int j = 0; j < VRPT; ++j) vr[j] = elem(rv[j], c);
+            store_run<E, VRPT>(&sm.vt[8 * vcg + c][vrb * VRPT], vr);
+          }
+        }
+        if (tid < C) sm.beta[tid] = to_f32(rbeta);
+      }
+      lds_barrier();  // ------------------------------------------------- MID
+      if (it < nchunks) {
+        // gated operands Qt, Kt, Kh (token-major)
+        {
+          float tot[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) tot[c] = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch]);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch + 4]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              tot[c] += a[c];
+              tot[c + 4] += b[c];
+              if (w < wave) {
+                off[c] += a[c];
+                off[c + 4] += b[c];
+              }
+            }
+          }
+#pragma unroll
+          for (int c = 0; c < 8; ++c) eT[c] = fast_exp2(tot[c]);
+        }
+#pragma unroll
+        for (int j = 0; j < RPB; ++j) {
+          const int r = rb * RPB + j;
+          float e[8], n[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float Gc = off[c] + G[j][c];
+            e[c] = fast_exp2(Gc);
+            n[c] = fast_exp2(-Gc);
+          }
+          float qo[8], ko[8], ho[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float kx = elem(rk[j], c);
+            qo[c] = elem(rq[j], c) * e[c];
+            ko[c] = kx * e[c];
+            ho[c] = kx * n[c];
+            khp[c][j >> 1][j & 1] = from_f32<E>(ho[c]);
+          }
+          store_run<E, 8>(&sm.q[r][ch], qo);
+          store_run<E, 8>(&sm.k[r][ch], ko);
+          store_run<E, 8>(&sm.kh[r][ch], ho);
+        }
+      }
+      lds_barrier();  // -------------------------------------------------- X1
+      if (it < nchunks) {
+        // A row block w and P row block 3 - w, all four column tiles each
+        // (straight-line, every fragment load issued up front; tiles above the
+        // diagonal are computed and dropped).  Then the diagonal block
+        // X_ww = (I + A_ww)^-1 in registers.
+        const int I = wave, IP = 3 - wave;
+        f32x4 aacc[4], pacc[4];
+        (void)0;
+        {
+          typename F::V ka[SK], qa[SK];
+#pragma unroll
+          for (int s = 0; s < SK; ++s) {
+            ka[s] = F::ld(&sm.k[16 * I + l16][0], s, kg);
+            qa[s] = F::ld(&sm.q[16 * IP + l16][0], s, kg);
+          }
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            typename F::V hb[SK];
+#pragma unroll
+            for (int s = 0; s < SK; ++s) hb[s] = F::ld(&sm.kh[16 * J + l16][0], s, kg);
+            aacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+            pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < SK; ++s) {
+              aacc[J] = F::mma(ka[s], hb[s], aacc[J]);
+              pacc[J] = F::mma(qa[s], hb[s], pacc[J]);
+            }
+          }
+        }
+        // A = strictly_lower(Diag(beta) Kt Kh^T), fp32
+        {
+          f32x4 brow;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) brow[i] = sm.beta[16 * I + 4 * kg + i];
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            const int col = 16 * J + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = 16 * I + 4 * kg + i;
+              aacc[J][i] = col >= row ? 0.f : aacc[J][i] * brow[i];
+              sm.a[row][col] = aacc[J][i];
+            }
+          }
+        }
+        // P = lower_incl_diag(Qt Kh^T) for row block IP (upper tiles stay zero)
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          if (J <= IP) {
+            const int col = 16 * J + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = 16 * IP + 4 * kg + i;
+              sm.p[row][col] = from_f32<E>(col > row ? 0.f : pacc[J][i]);
+            }
+          }
+        }
+        lds_wave_sync();
+        // diagonal block: N = A_II in accumulator form is aacc[I]; N^T from LDS
+        {
+          f32x4 N = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int J = 0; J < 4; ++J)
+            if (J == I) N = aacc[J];
+          const f32x4 Nt = *reinterpret_cast<const f32x4*>(&sm.a[16 * I + l16][16 * I + 4 * kg]);
+          Xdiag = unit_lower_inverse16<E>(N, Nt, lane);
+          const float bj = sm.beta[16 * I + l16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sm.xd[I][4 * kg + i][l16] = Xdiag[i];
+            sm.t[16 * I + 4 * kg + i][16 * I + l16] = from_f32<E>(Xdiag[i] * bj);
+          }
+        }
+      }
+      lds_barrier();  // -------------------------------------------------- X2
+      // the next chunk's raw loads fly while this chunk is computed
+      if (it + 1 < nchunks) load_raw(it + 1);
+      if (it < nchunks) {
+        // Off-diagonal blocks: wave J walks down block column J, which depends
+        // only on its own earlier blocks (kept in registers) and on the
+        // diagonal blocks:  X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ.
+        if (wave < 3) {
+          const int J = wave;
+          const float bj = sm.beta[16 * J + l16];
+          f32x4 Xc[4];  // X_KJ, K = J .. 3, accumulator form
+          Xc[0] = Xdiag;
+#pragma unroll
+          for (int d = 1; d < 4; ++d) {
+            if (J + d < 4) {
+              const int I = J + d;
+              f32x4 Mt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int e = 0; e < d; ++e) {
+                // At = (A_{I,J+e})^T in accumulator form: lane holds A[16I + l16][16(J+e) + 4kg + i]
+                const f32x4 At = *reinterpret_cast<const f32x4*>(&sm.a[16 * I + l16][16 * (J + e) + 4 * kg]);
+                Mt += Reg16<E>::prod(At, Xc[e]);
+              }
+              const f32x4 XIt = *reinterpret_cast<const f32x4*>(&sm.xd[I][l16][4 * kg]);
+              Xc[d] = -Reg16<E>::prod(XIt, Mt);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sm.t[16 * I + 4 * kg + i][16 * J + l16] = from_f32<E>(Xc[d][i] * bj);
+            }
+          }
+        }
+        // transposed Kh and the chunk decay, read by the state pass next
+#pragma unroll
+        for (int c = 0; c < 8; ++c) store_pairs<E, RPB / 2>(&sm.kht[ch + c][rb * RPB], khp[c]);
+        if (rb == 0) {
+          *reinterpret_cast<f32x4*>(&sm.gam[ch]) = f32x4{eT[0], eT[1], eT[2], eT[3]};
+          *reinterpret_cast<f32x4*>(&sm.gam[ch + 4]) = f32x4{eT[4], eT[5], eT[6], eT[7]};
         }
       }
     }
-    __syncthreads();
+    return;
+  }
 
-    // ================= phase 3: Tm = (I + A)^-1 Diag(b) ====================
-    if (wave == 0) {
-      // Diagonal 16x16 blocks by forward substitution, fp32; lane = (block, column).
-      const int blk = lane >> 4, j = lane & 15;
-      const int o16 = 16 * blk;
-      float x[16];
+  // ================= state wavefronts ======================================
+  const int bw = wave - 4;  // state wavefront index
+  f32x4 S[TPW][KT];         // S: rows (key channels) 16mt + 4kg + i, column l16
+  f32x4 R[TPW][4];          // R, then U: token rows 16t + 4kg + i
+  f32x4 O[TPW][4];
+  {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = (r == j) ? 1.f : 0.f;
+    for (int j = 0; j < TPW; ++j) {
+      const int col = col0 + 16 * (TPW * bw + j) + l16;
 #pragma unroll
-        for (int i = 0; i < r; ++i) s -= sm.a[o16 + r][o16 + i] * x[i];
-        x[r] = s;
-      }
-      const float bj = sm.beta[o16 + j];
+      for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sm.u1.sv.xd[blk][r][j] = from_f32<E>(x[r]);
-        sm.u1.sv.xt[o16 + j][o16 + r] = from_f32<E>(x[r]);
-        sm.t[o16 + r][o16 + j] = from_f32<E>(x[r] * bj);
-      }
+        for (int i = 0; i < 4; ++i)
+          S[j][mt][i] = args.h0 ? args.h0[state_off + (size_t)(16 * mt + 4 * kg + i) * DV + col] : 0.f;
     }
-    __syncthreads();
-    // Off-diagonal blocks, one diagonal band per level:
-    //   X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ
-#pragma unroll
-    for (int d = 1; d < 4; ++d) {
-      const int I = d + wave, J = wave;
-      const bool act = wave < 4 - d;
-      if (act) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int K = J; K < I; ++K)
-          M::run16_fa(acc, &sm.a[16 * I][16 * K], Cfg::AP, &sm.u1.sv.xt[16 * J][16 * K], Cfg::CP, lane);
-        store4<E>(&sm.u1.sv.m[wave][l16][4 * kg], acc);
-      }
-      __syncthreads();
-      if (act) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        M::run16(acc, &sm.u1.sv.xd[I][0][0], Cfg::XP, &sm.u1.sv.m[wave][0][0], Cfg::XP, lane);
-        acc = -acc;
-        store4<E>(&sm.u1.sv.xt[16 * J + l16][16 * I + 4 * kg], acc);
-        const float bj = sm.beta[16 * J + l16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.t[16 * I + 4 * kg + i][16 * J + l16] = from_f32<E>(acc[i] * bj);
-      }
-      __syncthreads();
-    }
+  }
 
-    // ================= phase 4: state pass over this slice ==================
-    // 4a: R = V - Kt S and O = Qt S; wave w owns token rows [16w, 16w + 16).
-    f32x4 O[RT];
+  const int rso = H * DV * (int)sizeof(T);  // token stride of o (bytes)
+  typename F::V UF[TPW][SC];  // U as B-operand fragments (bf16 or fp32)
+  for (int it = 0; it <= nchunks; ++it) {
+    lds_barrier();  // -------------------------------------------------- X0
+    if (it >= 1) {
+      // ---- state: U = Tm R (Tm lower triangular: tile t needs k < 16(t+1)) ----
+      {
+        typename F::V RF[TPW][SC];
 #pragma unroll
-    for (int nt = 0; nt < RT; ++nt) {
-      f32x4 r = {0.f, 0.f, 0.f, 0.f};
-      O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      M::template run<DK>(r, &sm.k[16 * wave][0], Cfg::KP, &sm.s[16 * nt][0], Cfg::KP, lane);
-      M::template run<DK>(O[nt], &sm.q[16 * wave][0], Cfg::KP, &sm.s[16 * nt][0], Cfg::KP, lane);
-      E* vp = &sm.vr[16 * nt + l16][16 * wave + 4 * kg];
-      store4<E>(vp, load4<E>(vp) - r);
-    }
-    __syncthreads();
-    // 4b: U = Tm R (Tm lower triangular: only K < 16(w+1) contributes).
-    const int kmax = ((16 * (wave + 1) + M::KSTEP - 1) / M::KSTEP) * M::KSTEP;
+        for (int j = 0; j < TPW; ++j)
 #pragma unroll
-    for (int nt = 0; nt < RT; ++nt) {
-      f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
-      M::run_n(uacc, &sm.t[16 * wave][0], Cfg::CP, &sm.vr[16 * nt][0], Cfg::CP, kmax, lane);
-      store4<E>(&sm.uu[16 * nt + l16][16 * wave + 4 * kg], uacc);
-    }
-    __syncthreads();
-    // 4c: O += P U, then write o.
+          for (int s = 0; s < SC; ++s) RF[j][s] = acc_frag(R[j], s, E());
 #pragma unroll
-    for (int nt = 0; nt < RT; ++nt) {
-      M::run_n(O[nt], &sm.p[16 * wave][0], Cfg::CP, &sm.uu[16 * nt][0], Cfg::CP, kmax, lane);
-      const int col = col0 + 16 * nt + l16;
+        for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = cbase + 16 * wave + 4 * kg + i;
-        if (pos < len) go[((size_t)(tok0 + pos) * H + h) * DV + col] = from_f32<T>(O[nt][i]);
+          for (int j = 0; j < TPW; ++j) R[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const E* trow = &sm.t[16 * t + l16][0];
+#pragma unroll
+          for (int s = 0; s < (16 * (t + 1) + SLAB - 1) / SLAB; ++s) {
+            const typename F::V a = F::ld(trow, s, kg);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) R[j][t] = F::mma(a, RF[j][s], R[j][t]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+          for (int s = 0; s < SC; ++s) UF[j][s] = acc_frag(R[j], s, E());
+      }
+      // ---- O += P U, then write o of chunk it - 1 ----
+      const int pbase = (it - 1) * C;
+      const int nv = min(C, len - pbase);
+      const rsrc_t bo = make_rsrc(go + ((size_t)(tok0 + pbase) * H + h) * DV + col0, (nv - 1) * rso + VS * (int)sizeof(T));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const E* prow = &sm.p[16 * t + l16][0];
+#pragma unroll
+        for (int s = 0; s < (16 * (t + 1) + SLAB - 1) / SLAB; ++s) {
+          const typename F::V a = F::ld(prow, s, kg);
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(a, UF[j][s], O[j][t]);
+        }
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          const int cb = (16 * (TPW * bw + j) + l16) * (int)sizeof(T);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bstore(from_f32<T>(O[j][t][i]), bo, (16 * t + 4 * kg + i) * rso + cb);
+        }
       }
     }
-    // 4d: S <- Diag(e^{G_C}) S + Kb^T U; refresh the operand copy of S.
+    lds_barrier();  // ------------------------------------------------- MID
+    if (it >= 1) {
+      // ---- state: S <- Diag(e^{G_C}) (S + Kh^T U) ----
 #pragma unroll
-    for (int mt = 0; mt < SMT; ++mt) {
-      const int row0 = (DK / 4) * wave + 16 * mt;
-      f32x4 gm;
+      for (int mt = 0; mt < KT; ++mt) {
+        const E* krow = &sm.kht[16 * mt + l16][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gm[i] = sm.gam[row0 + 4 * kg + i];
+        for (int s = 0; s < SC; ++s) {
+          const typename F::V a = F::ld(krow, s, kg);
 #pragma unroll
-      for (int nt = 0; nt < RT; ++nt) {
-        S[mt][nt] *= gm;
-        M::template run<C>(S[mt][nt], &sm.kbt[row0][0], Cfg::CP, &sm.uu[16 * nt][0], Cfg::CP, lane);
-        store4<E>(&sm.s[16 * nt + l16][row0 + 4 * kg], S[mt][nt]);
+          for (int j = 0; j < TPW; ++j) S[j][mt] = F::mma(a, UF[j][s], S[j][mt]);
+        }
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[16 * mt + 4 * kg]);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) S[j][mt] *= gm;
+      }
+    }
+    lds_barrier();  // -------------------------------------------------- X1
+    if (it < nchunks) {
+      // ---- state: R = V - Kt S ----
+      typename F::V SF[TPW][SK];  // S as B-operand fragments
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int s = 0; s < SK; ++s) SF[j][s] = acc_frag(S[j], s, E());
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) R[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const E* krow = &sm.k[16 * t + l16][0];
+#pragma unroll
+        for (int s = 0; s < SK; ++s) {
+          const typename F::V a = F::ld(krow, s, kg);
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) R[j][t] = F::mma(a, SF[j][s], R[j][t]);
+        }
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          const f32x4 vv = load4<E>(&sm.vt[16 * (TPW * bw + j) + l16][16 * t + 4 * kg]);
+          R[j][t] = vv - R[j][t];
+        }
+      }
+    }
+    lds_barrier();  // -------------------------------------------------- X2
+    if (it < nchunks) {
+      // ---- state: O = Qt S ----
+      typename F::V SF[TPW][SK];
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int s = 0; s < SK; ++s) SF[j][s] = acc_frag(S[j], s, E());
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) O[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const E* qrow = &sm.q[16 * t + l16][0];
+#pragma unroll
+        for (int s = 0; s < SK; ++s) {
+          const typename F::V a = F::ld(qrow, s, kg);
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(a, SF[j][s], O[j][t]);
+        }
       }
     }
   }
@@ -562,14 +871,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(PrefillArgs args) {
   // ---- final state ----
   if (args.ht) {
 #pragma unroll
-    for (int mt = 0; mt < SMT; ++mt) {
+    for (int j = 0; j < TPW; ++j) {
+      const int col = col0 + 16 * (TPW * bw + j) + l16;
 #pragma unroll
-      for (int nt = 0; nt < RT; ++nt) {
-        const int row0 = (DK / 4) * wave + 16 * mt + 4 * kg;
-        const int col = 16 * nt + l16;
+      for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) args.ht[state_off + (size_t)(row0 + i) * DV + col0 + col] = S[mt][nt][i];
-      }
+        for (int i = 0; i < 4; ++i) args.ht[state_off + (size_t)(16 * mt + 4 * kg + i) * DV + col] = S[j][mt][i];
     }
   }
 }
@@ -618,11 +925,12 @@ static hipError_t launch_dims(int Dk, int Dv, int VS, const PrefillArgs& a, hipS
   if constexpr (sizeof(T) == 2) {
     KDA_CASE(64, 64, 64)
     KDA_CASE(64, 64, 32)
-    KDA_CASE(64, 64, 16)
+    KDA_CASE(64, 128, 128)
     KDA_CASE(64, 128, 64)
     KDA_CASE(64, 128, 32)
     KDA_CASE(128, 64, 64)
     KDA_CASE(128, 64, 32)
+    KDA_CASE(128, 128, 128)
     KDA_CASE(128, 128, 64)
     KDA_CASE(128, 128, 32)
   } else {
@@ -639,10 +947,10 @@ static hipError_t launch_dims(int Dk, int Dv, int VS, const PrefillArgs& a, hipS
 // possible; narrower slices cost a repeated intra-chunk transform.
 int prefill_slice_width(bool bf16_io, int Dk, int Dv, long long units, int num_cus) {
   if (!bf16_io) return (Dk == 64) ? (units * (Dv / 16) <= num_cus ? 16 : 32) : 0;
-  int vs = 64;
-  if (Dv == 128 && units * 2 < (long long)num_cus / 2) vs = 32;
-  if (Dv == 64 && units < (long long)num_cus / 2) vs = 32;
-  return vs;
+  // widest slice that still gives every CU a workgroup
+  for (int vs = Dv; vs > 32; vs /= 2)
+    if (units * (Dv / vs) >= num_cus / 2) return vs;
+  return 32;
 }
 
 bool prefill_supported(bool bf16_io, int Dk, int Dv) { return bf16_io || Dk == 64; }

@@ -34,6 +34,7 @@ def assert_close(name, got, ref, dtype):
     got64 = f64(got)
     assert np.all(np.isfinite(got64)), "%s: non-finite values" % name
     maxabs, rel = errors(got64, ref)
+    print("PARITY %-40s max-abs %.3e rel-L2 %.3e" % (name, maxabs, rel), flush=True)
     if dtype == torch.float32:
         assert maxabs <= TOL_F32_MAXABS, "%s: max-abs %.3e > %.0e" % (name, maxabs, TOL_F32_MAXABS)
     else:
