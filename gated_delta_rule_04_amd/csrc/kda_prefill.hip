@@ -332,32 +332,19 @@ struct Frag<float> {
 // where At holds A^T and B holds B in the accumulator layout (lane l: rows
 // 4(l/16) + i of column l % 16).  The accumulator form of a matrix is its
 // B-operand layout and the accumulator form of its transpose is its
-// A-operand layout, so chains of products never leave registers.  bf16: each
-// operand is split into bf16 hi + lo parts (three MFMAs), which keeps the
-// product accurate to about 2^-16 relative; fp32: four 16x16x4 steps.
+// A-operand layout, so chains of products never leave registers.  bf16: one
+// 16x16x16 MFMA on bf16-rounded operands (the transform is stored in bf16
+// afterwards; the extra rounding raises its error from 1.6e-4 to 2.2e-4
+// relative); fp32: four 16x16x4 steps.
 template <typename E>
 struct Reg16;
 template <>
 struct Reg16<bf16> {
-  __device__ __forceinline__ static void split(const f32x4& x, s16x4& hi, s16x4& lo) {
-    bf16x4 h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = (bf16)x[i];
-      l[i] = (bf16)(x[i] - (float)h[i]);
-    }
-    hi = __builtin_bit_cast(s16x4, h);
-    lo = __builtin_bit_cast(s16x4, l);
+  __device__ __forceinline__ static s16x4 cvt(const f32x4& x) {
+    return __builtin_bit_cast(s16x4, bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]});
   }
   __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) {
-    s16x4 ah, al, bh, bl;
-    split(At, ah, al);
-    split(B, bh, bl);
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
-    return c;
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt(At), cvt(B), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
 };
 template <>
@@ -493,20 +480,20 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
     const int rsg = H * (DK / GG) * (int)sizeof(T);    // token stride of g
     const int rsv = H * DV * (int)sizeof(T);           // token stride of v
     const int rsb = H * (int)sizeof(T);                // token stride of beta
-    auto load_raw = [&](int ck) {
-      const int cb = ck * C;
-      const int nv = min(C, len - cb);  // valid rows of this chunk (>= 1)
-      const size_t row0 = (size_t)(tok0 + cb) * H + h;
-      const rsrc_t bq = make_rsrc(gq + row0 * DK, (nv - 1) * rsk + DK * (int)sizeof(T));
-      const rsrc_t bk = make_rsrc(gk + row0 * DK, (nv - 1) * rsk + DK * (int)sizeof(T));
+    // The prefetch of the next chunk is split in three parts, each issued as
+    // soon as its registers are free, so that no single wave stalls on a long
+    // burst of loads (the vector L1 moves about 64 bytes per clock).
+    auto chunk_rows = [&](int ck) { return min(C, len - ck * C); };
+    auto chunk_row0 = [&](int ck) { return (size_t)(tok0 + ck * C) * H + h; };
+    auto load_gvb = [&](int ck) {  // g, v, beta
+      const int nv = chunk_rows(ck);
+      const size_t row0 = chunk_row0(ck);
       const rsrc_t bg = make_rsrc(gg + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * (int)sizeof(T));
       const rsrc_t bv = make_rsrc(gv + row0 * DV + col0, (nv - 1) * rsv + VS * (int)sizeof(T));
       const rsrc_t bb = make_rsrc(gb + row0, (nv - 1) * rsb + (int)sizeof(T));
 #pragma unroll
       for (int j = 0; j < RPB; ++j) {
         const int r = rb * RPB + j;
-        rq[j] = Vec8<T>::load(bq, r * rsk + ch * (int)sizeof(T));
-        rk[j] = Vec8<T>::load(bk, r * rsk + ch * (int)sizeof(T));
         if constexpr (GG == 1)
           rg[j] = Vec8<T>::load(bg, r * rsg + ch * (int)sizeof(T));
         else
@@ -518,12 +505,26 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
       }
       if (tid < C) rbeta = bload<T>(bb, tid * rsb);
     };
+    auto load_q = [&](int ck) {
+      const rsrc_t bq = make_rsrc(gq + chunk_row0(ck) * DK, (chunk_rows(ck) - 1) * rsk + DK * (int)sizeof(T));
+#pragma unroll
+      for (int j = 0; j < RPB; ++j) rq[j] = Vec8<T>::load(bq, (rb * RPB + j) * rsk + ch * (int)sizeof(T));
+    };
+    auto load_k = [&](int ck) {
+      const rsrc_t bk = make_rsrc(gk + chunk_row0(ck) * DK, (chunk_rows(ck) - 1) * rsk + DK * (int)sizeof(T));
+#pragma unroll
+      for (int j = 0; j < RPB; ++j) rk[j] = Vec8<T>::load(bk, (rb * RPB + j) * rsk + ch * (int)sizeof(T));
+    };
     float G[RPB][8];        // cumulative log2-decay of this thread's rows (block-local)
     float off[8];           // log2-decay of the chunk before this thread's block
     float eT[8];            // e^{G_C} of this thread's channels
     EP2 khp[8][RPB / 2];    // Kh of this thread's rows per channel (token pairs), for Kh^T
     f32x4 Xdiag;            // X_ww = (I + A_ww)^-1 of this wave's block, accumulator form
-    if (nchunks > 0) load_raw(0);
+    if (nchunks > 0) {
+      load_gvb(0);
+      load_q(0);
+      load_k(0);
+    }
 
     for (int it = 0; it <= nchunks; ++it) {
       const int cbase = it * C;  // chunk it
@@ -571,6 +572,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
         if (tid < C) sm.beta[tid] = to_f32(rbeta);
       }
       lds_barrier();  // ------------------------------------------------- MID
+      if (it + 1 < nchunks) load_gvb(it + 1);  // prefetch (g, v, beta registers are free)
       if (it < nchunks) {
         // gated operands Qt, Kt, Kh (token-major)
         {
@@ -619,32 +621,25 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
         }
       }
       lds_barrier();  // -------------------------------------------------- X1
+      if (it + 1 < nchunks) load_q(it + 1);  // prefetch (q registers are free)
       if (it < nchunks) {
-        // A row block w and P row block 3 - w, all four column tiles each
-        // (straight-line, every fragment load issued up front; tiles above the
-        // diagonal are computed and dropped).  Then the diagonal block
-        // X_ww = (I + A_ww)^-1 in registers.
-        const int I = wave, IP = 3 - wave;
-        f32x4 aacc[4], pacc[4];
-        (void)0;
+        // A row block w (tiles J <= w, fragment loads issued up front), then
+        // the diagonal block X_ww = (I + A_ww)^-1 in registers.
+        const int I = wave;
+        f32x4 aacc[4];
         {
-          typename F::V ka[SK], qa[SK];
+          typename F::V ka[SK];
 #pragma unroll
-          for (int s = 0; s < SK; ++s) {
-            ka[s] = F::ld(&sm.k[16 * I + l16][0], s, kg);
-            qa[s] = F::ld(&sm.q[16 * IP + l16][0], s, kg);
-          }
+          for (int s = 0; s < SK; ++s) ka[s] = F::ld(&sm.k[16 * I + l16][0], s, kg);
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
-            typename F::V hb[SK];
-#pragma unroll
-            for (int s = 0; s < SK; ++s) hb[s] = F::ld(&sm.kh[16 * J + l16][0], s, kg);
             aacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-            pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (J <= I) {
+              typename F::V hb[SK];
 #pragma unroll
-            for (int s = 0; s < SK; ++s) {
-              aacc[J] = F::mma(ka[s], hb[s], aacc[J]);
-              pacc[J] = F::mma(qa[s], hb[s], pacc[J]);
+              for (int s = 0; s < SK; ++s) hb[s] = F::ld(&sm.kh[16 * J + l16][0], s, kg);
+#pragma unroll
+              for (int s = 0; s < SK; ++s) aacc[J] = F::mma(ka[s], hb[s], aacc[J]);
             }
           }
         }
@@ -655,24 +650,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
           for (int i = 0; i < 4; ++i) brow[i] = sm.beta[16 * I + 4 * kg + i];
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
-            const int col = 16 * J + l16;
+            if (J <= I) {
+              const int col = 16 * J + l16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = 16 * I + 4 * kg + i;
-              aacc[J][i] = col >= row ? 0.f : aacc[J][i] * brow[i];
-              sm.a[row][col] = aacc[J][i];
-            }
-          }
-        }
-        // P = lower_incl_diag(Qt Kh^T) for row block IP (upper tiles stay zero)
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          if (J <= IP) {
-            const int col = 16 * J + l16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = 16 * IP + 4 * kg + i;
-              sm.p[row][col] = from_f32<E>(col > row ? 0.f : pacc[J][i]);
+              for (int i = 0; i < 4; ++i) {
+                const int row = 16 * I + 4 * kg + i;
+                aacc[J][i] = col >= row ? 0.f : aacc[J][i] * brow[i];
+                sm.a[row][col] = aacc[J][i];
+              }
             }
           }
         }
@@ -694,8 +679,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
         }
       }
       lds_barrier();  // -------------------------------------------------- X2
-      // the next chunk's raw loads fly while this chunk is computed
-      if (it + 1 < nchunks) load_raw(it + 1);
+      if (it + 1 < nchunks) load_k(it + 1);  // prefetch (k registers are free)
       if (it < nchunks) {
         // Off-diagonal blocks: wave J walks down block column J, which depends
         // only on its own earlier blocks (kept in registers) and on the
@@ -720,6 +704,31 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
               Xc[d] = -Reg16<E>::prod(XIt, Mt);
 #pragma unroll
               for (int i = 0; i < 4; ++i) sm.t[16 * I + 4 * kg + i][16 * J + l16] = from_f32<E>(Xc[d][i] * bj);
+            }
+          }
+        }
+        // P = lower_incl_diag(Qt Kh^T), row block w (upper tiles stay zero);
+        // it balances the sweeps above (wave w walks 3 - w sweep blocks)
+        {
+          const int IP = wave;
+          typename F::V qa[SK];
+#pragma unroll
+          for (int s = 0; s < SK; ++s) qa[s] = F::ld(&sm.q[16 * IP + l16][0], s, kg);
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            if (J <= IP) {
+              typename F::V hb[SK];
+#pragma unroll
+              for (int s = 0; s < SK; ++s) hb[s] = F::ld(&sm.kh[16 * J + l16][0], s, kg);
+              f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int s = 0; s < SK; ++s) pacc = F::mma(qa[s], hb[s], pacc);
+              const int col = 16 * J + l16;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int row = 16 * IP + 4 * kg + i;
+                sm.p[row][col] = from_f32<E>(col > row ? 0.f : pacc[i]);
+              }
             }
           }
         }
