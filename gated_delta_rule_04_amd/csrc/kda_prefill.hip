@@ -246,9 +246,10 @@ struct PrefillCfg {
   typedef T_ E;  // MFMA operand type (bf16 path: bf16; f32 path: float)
   static constexpr int DK = DK_, DV = DV_, VS = VS_, GG = GG_;
   static constexpr int C = 64;                   // chunk length
-  static constexpr int NA = 256;                 // producer threads (4 wavefronts)
+  static constexpr int NPW = DK / 16;            // producer wavefronts (8 or 4)
+  static constexpr int NA = 64 * NPW;            // producer threads
   static constexpr int RT = VS / 16;             // value-column tiles per slice
-  static constexpr int TPW = RT >= 2 ? 2 : 1;    // value tiles per state wavefront
+  static constexpr int TPW = RT > 4 ? RT / 4 : 1;  // value tiles per state wavefront
   static constexpr int NBW = RT / TPW;           // state wavefronts
   static constexpr int NT = NA + 64 * NBW;       // threads per workgroup
   static constexpr int PADE = 8 / sizeof(E);     // 8-byte row skew: pitch = 2 (mod 32) dwords
@@ -261,13 +262,14 @@ struct PrefillCfg {
   static constexpr int RPB = C / NRB;            // gating: rows per block
   static constexpr int RBW = 64 / CGN;           // gating: row blocks per wavefront
   static constexpr int VCG = VS / 8;             // V: groups of 8 value columns
-  static constexpr int VRPT = VS >= 32 ? VS / 32 : 1;  // V: rows per loading thread
+  static constexpr int VRPT = 64 * VCG > NA ? 64 * VCG / NA : 1;  // V: rows per loading thread
   static constexpr int VTH = 64 * VCG / VRPT;    // V: loading threads
   static constexpr int KT = DK / 16;             // key-channel tiles
   static constexpr int NS = DV / VS;             // slices per head
   static_assert(DK == 64 || DK == 128, "DK");
   static_assert(VS % 16 == 0 && DV % VS == 0 && RT % TPW == 0, "VS");
   static_assert(NRB * CGN == NA && RPB * NRB == C && RPB % 2 == 0 && RBW * CGN == 64, "gating map");
+  static_assert(NPW == 4 || NPW == 8, "producer wavefronts");
   static_assert(VTH <= NA && VTH * VRPT == 64 * VCG, "V map");
 };
 
@@ -285,7 +287,7 @@ struct Smem {
   alignas(16) float xd[4][16][20];  // diagonal blocks of X = (I + A)^-1, row-major (fp32)
   float beta[Cfg::C];
   alignas(16) float gam[Cfg::DK];  // e^{G_C}
-  alignas(16) float gsum[4][Cfg::DK];  // per-wavefront log2-decay totals
+  alignas(16) float gsum[Cfg::NPW][Cfg::DK];  // per-wavefront log2-decay totals
 };
 
 // MFMA fragments with a k order that matches the accumulator layout, so that
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int l16 = lane & 15, kg = lane >> 4;
-  const bool producer = wave < 4;
+  const bool producer = wave < Cfg::NPW;
 
   // ---- workgroup -> (unit, slice); the NS slices of a unit share an XCD ----
   const int grp = blockIdx.x / (8 * NS);
@@ -520,6 +522,31 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
     float eT[8];            // e^{G_C} of this thread's channels
     EP2 khp[8][RPB / 2];    // Kh of this thread's rows per channel (token pairs), for Kh^T
     f32x4 Xdiag;            // X_ww = (I + A_ww)^-1 of this wave's block, accumulator form
+    // P = lower_incl_diag(Qt Kh^T) for row block IP (upper tiles stay zero)
+    auto p_tiles = [&](int IP) {
+      typename F::V qa[SK];
+#pragma unroll
+      for (int s = 0; s < SK; ++s) qa[s] = F::ld(&sm.q[16 * IP + l16][0], s, kg);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        if (J <= IP) {
+          typename F::V hb[SK];
+#pragma unroll
+          for (int s = 0; s < SK; ++s) hb[s] = F::ld(&sm.kh[16 * J + l16][0], s, kg);
+          f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < SK; ++s) pacc = F::mma(qa[s], hb[s], pacc);
+          const int col = 16 * J + l16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * IP + 4 * kg + i;
+            float pv = pacc[i];
+            if (J == IP) pv = col > row ? 0.f : pv;  // lower including the diagonal
+            sm.p[row][col] = from_f32<E>(pv);
+          }
+        }
+      }
+    };
     if (nchunks > 0) {
       load_gvb(0);
       load_q(0);
@@ -575,26 +602,20 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
       if (it + 1 < nchunks) load_gvb(it + 1);  // prefetch (g, v, beta registers are free)
       if (it < nchunks) {
         // gated operands Qt, Kt, Kh (token-major)
-        {
-          float tot[8];
+        // decay before this thread's block: earlier wavefronts' totals
+        for (int w = 0; w < wave; ++w) {  // uniform trip count
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch]);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch + 4]);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) tot[c] = 0.f;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch]);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch + 4]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              tot[c] += a[c];
-              tot[c + 4] += b[c];
-              if (w < wave) {
-                off[c] += a[c];
-                off[c + 4] += b[c];
-              }
-            }
+          for (int c = 0; c < 4; ++c) {
+            off[c] += a[c];
+            off[c + 4] += b[c];
           }
+        }
+        // the chunk's total decay: the last row block's inclusive prefix
+        if (rb == Cfg::NRB - 1) {
 #pragma unroll
-          for (int c = 0; c < 8; ++c) eT[c] = fast_exp2(tot[c]);
+          for (int c = 0; c < 8; ++c) eT[c] = fast_exp2(off[c] + G[RPB - 1][c]);
         }
 #pragma unroll
         for (int j = 0; j < RPB; ++j) {
@@ -622,7 +643,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
       }
       lds_barrier();  // -------------------------------------------------- X1
       if (it + 1 < nchunks) load_q(it + 1);  // prefetch (q registers are free)
-      if (it < nchunks) {
+      if (it < nchunks && Cfg::NPW == 8 && wave >= 4) p_tiles(wave - 4);
+      if (it < nchunks && wave < 4) {
         // A row block w (tiles J <= w, fragment loads issued up front), then
         // the diagonal block X_ww = (I + A_ww)^-1 in registers.
         const int I = wave;
@@ -655,7 +677,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int row = 16 * I + 4 * kg + i;
-                aacc[J][i] = col >= row ? 0.f : aacc[J][i] * brow[i];
+                aacc[J][i] *= brow[i];
+                if (J == I) aacc[J][i] = col >= row ? 0.f : aacc[J][i];  // strictly lower
                 sm.a[row][col] = aacc[J][i];
               }
             }
@@ -707,35 +730,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
             }
           }
         }
-        // P = lower_incl_diag(Qt Kh^T), row block w (upper tiles stay zero);
-        // it balances the sweeps above (wave w walks 3 - w sweep blocks)
-        {
-          const int IP = wave;
-          typename F::V qa[SK];
-#pragma unroll
-          for (int s = 0; s < SK; ++s) qa[s] = F::ld(&sm.q[16 * IP + l16][0], s, kg);
-#pragma unroll
-          for (int J = 0; J < 4; ++J) {
-            if (J <= IP) {
-              typename F::V hb[SK];
-#pragma unroll
-              for (int s = 0; s < SK; ++s) hb[s] = F::ld(&sm.kh[16 * J + l16][0], s, kg);
-              f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int s = 0; s < SK; ++s) pacc = F::mma(qa[s], hb[s], pacc);
-              const int col = 16 * J + l16;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int row = 16 * IP + 4 * kg + i;
-                sm.p[row][col] = from_f32<E>(col > row ? 0.f : pacc[i]);
-              }
-            }
-          }
-        }
+        if constexpr (Cfg::NPW == 4) p_tiles(wave);  // balances the sweeps above
         // transposed Kh and the chunk decay, read by the state pass next
 #pragma unroll
         for (int c = 0; c < 8; ++c) store_pairs<E, RPB / 2>(&sm.kht[ch + c][rb * RPB], khp[c]);
-        if (rb == 0) {
+        if (rb == Cfg::NRB - 1) {
           *reinterpret_cast<f32x4*>(&sm.gam[ch]) = f32x4{eT[0], eT[1], eT[2], eT[3]};
           *reinterpret_cast<f32x4*>(&sm.gam[ch + 4]) = f32x4{eT[4], eT[5], eT[6], eT[7]};
         }
@@ -745,7 +744,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
   }
 
   // ================= state wavefronts ======================================
-  const int bw = wave - 4;  // state wavefront index
+  const int bw = wave - Cfg::NPW;  // state wavefront index
   f32x4 S[TPW][KT];         // S: rows (key channels) 16mt + 4kg + i, column l16
   f32x4 R[TPW][4];          // R, then U: token rows 16t + 4kg + i
   f32x4 O[TPW][4];
@@ -939,7 +938,6 @@ static hipError_t launch_dims(int Dk, int Dv, int VS, const PrefillArgs& a, hipS
     KDA_CASE(64, 128, 32)
     KDA_CASE(128, 64, 64)
     KDA_CASE(128, 64, 32)
-    KDA_CASE(128, 128, 128)
     KDA_CASE(128, 128, 64)
     KDA_CASE(128, 128, 32)
   } else {
@@ -956,8 +954,9 @@ static hipError_t launch_dims(int Dk, int Dv, int VS, const PrefillArgs& a, hipS
 // possible; narrower slices cost a repeated intra-chunk transform.
 int prefill_slice_width(bool bf16_io, int Dk, int Dv, long long units, int num_cus) {
   if (!bf16_io) return (Dk == 64) ? (units * (Dv / 16) <= num_cus ? 16 : 32) : 0;
-  // widest slice that still gives every CU a workgroup
-  for (int vs = Dv; vs > 32; vs /= 2)
+  // widest slice that still gives every CU a workgroup (64 at most with 128
+  // key channels: wider state slices do not fit the register budget)
+  for (int vs = (Dk == 128 ? 64 : Dv); vs > 32; vs /= 2)
     if (units * (Dv / vs) >= num_cus / 2) return vs;
   return 32;
 }
