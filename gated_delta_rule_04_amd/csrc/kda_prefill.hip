@@ -8,25 +8,27 @@
 // tokens, with S the state entering the chunk and G_r = sum_{j<=r} g_j the
 // chunk-local cumulative log-decay (per key channel):
 //
-//   gated operands   Qt = Q*e^G, Kt = K*e^G, Kh = K*e^-G, Kb = K*e^(G_C - G)
+//   gated operands   Qt = Q*e^G, Kt = K*e^G, Kh = K*e^-G
 //   k-k block        A  = strictly_lower(Diag(b) Kt Kh^T)              (MFMA)
 //   q-k block        P  = lower_incl_diag(Qt Kh^T)                      (MFMA)
-//   UT transform     Tm = (I + A)^-1 Diag(b): 16x16 diagonal blocks by
-//                    forward substitution, off-diagonal blocks by MFMA
+//   UT transform     Tm = (I + A)^-1 Diag(b): 16x16 diagonal blocks by a
+//                    product of Neumann factors, the blocks below them by
+//                    block forward substitution                         (MFMA)
 //   state pass       R = V - Kt S;  U = Tm R;  O = Qt S + P U;
-//                    S <- Diag(e^G_C) S + Kb^T U                        (MFMA)
+//                    S <- Diag(e^G_C) (S + Kh^T U)                      (MFMA)
 //
-// Design for MI355X.  HBM bytes bind this path (about 100 flop per byte at
-// d = 128, against a ridge near 300), so q, k, v, g, beta are read from HBM
-// exactly once and o written once: the intra-chunk transform and the
-// sequential state pass run in the same workgroup and hand over through LDS,
-// never through HBM.  One workgroup (4 wavefronts) owns one (sequence, head,
-// d_v slice) and walks that sequence's chunks in order with its fp32 state
-// slice resident in MFMA accumulators.  Columns of S evolve independently, so
-// splitting d_v over workgroups adds parallelism for few-head shapes; the
-// slices of one head are placed on the same XCD so their shared q/k/g reads
-// hit that XCD's L2.  bf16 inputs use v_mfma_f32_16x16x32_bf16 (fp32
-// accumulate); float32 inputs use v_mfma_f32_16x16x4_f32 throughout.
+// Design for MI355X.  The whole chain for one chunk runs in one workgroup and
+// hands over through LDS, never through HBM: q, k, v, g, beta are read once
+// and o written once.  A workgroup owns one (sequence, head, d_v slice) and
+// walks that sequence's chunks in order.  Its wavefronts are specialised:
+// producer wavefronts (one per 16 key channels) prepare chunk c -- gating,
+// the k-k and q-k blocks, the UT transform -- while state wavefronts (one per
+// 16 value columns of the slice, at most four) keep their columns of the fp32
+// state in MFMA accumulators and run the state pass, which trails the
+// producer by half a chunk.  The slices of one head are placed on the same
+// XCD so that their shared q/k/g reads hit that XCD's L2.  bf16 inputs use
+// v_mfma_f32_16x16x32_bf16 (fp32 accumulate); float32 inputs use
+// v_mfma_f32_16x16x4_f32 throughout.
 //
 // Numerics: S, A, the diagonal solve, all accumulators and e^G are fp32; MFMA
 // operands (gated q/k, Tm, P, R, U and a copy of S) are rounded to the input
@@ -38,78 +40,42 @@
 
 namespace kda {
 
-// ---------------------------------------------------------------------------
-// MFMA helpers.  All 16x16 tiles: lane l holds D[4*(l/16) + i][l % 16].
-// A is read row-major [m][k]; B is read transposed, Bt[n][k] (k contiguous).
-// ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-template <typename E>
-struct Mma;
-
-template <>
-struct Mma<bf16> {
-  // acc += A[16 x 16] * B[16 x 16], A given in float32 (converted), B transposed.
-  __device__ __forceinline__ static void run16_fa(f32x4& acc, const float* A, int lda, const bf16* Bt, int ldb,
-                                                  int lane) {
-    const int r = lane & 15, kg = lane >> 4;
-    const f32x4 af = *reinterpret_cast<const f32x4*>(A + r * lda + 4 * kg);
-    bf16x4 a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = (bf16)af[i];
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(Bt + r * ldb + 4 * kg);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), acc,
-                                                     0, 0, 0);
-  }
-  // acc += A[16 x 16] * B[16 x 16], both in bf16 (A row-major, B transposed).
-  __device__ __forceinline__ static void run16(f32x4& acc, const bf16* A, int lda, const bf16* Bt, int ldb,
-                                               int lane) {
-    const int r = lane & 15, kg = lane >> 4;
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + r * lda + 4 * kg);
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(Bt + r * ldb + 4 * kg);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), acc,
-                                                     0, 0, 0);
-  }
-};
-
-template <>
-struct Mma<float> {
-  // acc += A[16 x 16] * B[16 x 16] (B transposed), four 16x16x4 steps.
-  template <typename TA>
-  __device__ __forceinline__ static void run16_any(f32x4& acc, const TA* A, int lda, const float* Bt, int ldb,
-                                                   int lane) {
-    const int r = lane & 15, kg = lane >> 4;
-#pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + kg], Bt[r * ldb + k0 + kg], acc, 0, 0, 0);
-  }
-  __device__ __forceinline__ static void run16_fa(f32x4& acc, const float* A, int lda, const float* Bt, int ldb,
-                                                  int lane) {
-    run16_any(acc, A, lda, Bt, ldb, lane);
-  }
-  __device__ __forceinline__ static void run16(f32x4& acc, const float* A, int lda, const float* Bt, int ldb,
-                                               int lane) {
-    run16_any(acc, A, lda, Bt, ldb, lane);
-  }
-};
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // traffic, not for its global loads/stores, so prefetched global loads stay
 // in flight across it (the compiler waits for them at their first use).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Completes this wave's own LDS writes before it reads them back.
-__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Two adjacent elements, loaded as one 4- or 8-byte access.
-__device__ __forceinline__ f32x2 load2(const bf16* p) {
-  const bf16x2 x = *reinterpret_cast<const bf16x2*>(p);
-  return f32x2{(float)x[0], (float)x[1]};
+// Compile-time wavefront roles: fn(IC<w>{}) for the uniform index w < N, so
+// each wavefront's share of a stage is specialised (scalar branches only).
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+template <int N, class Fn>
+__device__ __forceinline__ void static_switch(int w, Fn&& fn) {
+  if constexpr (N > 0) {
+    if (w == N - 1)
+      fn(IC<N - 1>{});
+    else
+      static_switch<N - 1>(w, fn);
+  }
 }
-__device__ __forceinline__ f32x2 load2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
-__device__ __forceinline__ void store2(bf16* p, float a, float b) {
-  *reinterpret_cast<bf16x2*>(p) = bf16x2{(bf16)a, (bf16)b};
+
+// A lane offset the compiler must recompute where it is used: keeps the LDS
+// addresses of the per-wavefront jobs (compile-time block offsets on top)
+// from being hoisted out of the chunk loop, where the variants' hoisted
+// addresses together would exhaust the registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
-__device__ __forceinline__ void store2(float* p, float a, float b) { *reinterpret_cast<f32x2*>(p) = f32x2{a, b}; }
+
+// Four consecutive values to LDS: one 8-byte write (bf16) or two (fp32; fp32
+// operand rows are 8-byte aligned: their pitches are skewed by 8 bytes).
 template <typename E>
 __device__ __forceinline__ void store4(E* p, const f32x4& v);
 template <>
@@ -121,19 +87,6 @@ __device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
   *reinterpret_cast<f32x2*>(p) = f32x2{v[0], v[1]};
   *reinterpret_cast<f32x2*>(p + 2) = f32x2{v[2], v[3]};
 }
-template <typename E>
-__device__ __forceinline__ f32x4 load4(const E* p);
-template <>
-__device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
-  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
-template <>
-__device__ __forceinline__ f32x4 load4<float>(const float* p) {
-  const f32x2 a = *reinterpret_cast<const f32x2*>(p), b = *reinterpret_cast<const f32x2*>(p + 2);
-  return f32x4{a[0], a[1], b[0], b[1]};
-}
-
 
 template <typename T>
 struct Pair;
@@ -145,35 +98,6 @@ template <>
 struct Pair<float> {
   typedef f32x2 type;
 };
-__device__ __forceinline__ f32x2 unpack2(bf16x2 x) { return f32x2{(float)x[0], (float)x[1]}; }
-__device__ __forceinline__ f32x2 unpack2(f32x2 x) { return x; }
-
-// Store N consecutive values (a contiguous run) with 8-byte stores (LDS rows
-// are 8-byte aligned: their pitches are skewed by 8 bytes against bank conflicts).
-template <typename E, int N>
-__device__ __forceinline__ void store_run(E* p, const float (&x)[N]) {
-  if constexpr (sizeof(E) == 2) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < N; i += 4)
-        *reinterpret_cast<bf16x4*>(p + i) = bf16x4{(bf16)x[i], (bf16)x[i + 1], (bf16)x[i + 2], (bf16)x[i + 3]};
-    } else if constexpr (N % 2 == 0) {
-#pragma unroll
-      for (int i = 0; i < N; i += 2) *reinterpret_cast<bf16x2*>(p + i) = bf16x2{(bf16)x[i], (bf16)x[i + 1]};
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; ++i) p[i] = (bf16)x[i];
-    }
-  } else {
-    if constexpr (N % 2 == 0) {
-#pragma unroll
-      for (int i = 0; i < N; i += 2) *reinterpret_cast<f32x2*>(p + i) = f32x2{x[i], x[i + 1]};
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; ++i) p[i] = x[i];
-    }
-  }
-}
 
 // Store NP element pairs as one contiguous run of 2*NP elements.
 template <typename E, int NP>
@@ -202,8 +126,10 @@ __device__ __forceinline__ P bload(rsrc_t r, int off) {
     return __builtin_bit_cast(P, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
   else if constexpr (sizeof(P) == 4)
     return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-  else
+  else if constexpr (sizeof(P) == 8)
     return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 // Eight consecutive elements, loaded with 16-byte accesses.
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -212,16 +138,13 @@ struct Vec8;
 template <>
 struct Vec8<bf16> {
   typedef bf16x8 type;
-  __device__ __forceinline__ static type load(rsrc_t r, int off) {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  }
+  __device__ __forceinline__ static type load(rsrc_t r, int off) { return bload<bf16x8>(r, off); }
 };
 template <>
 struct Vec8<float> {
   typedef f32x8 type;
   __device__ __forceinline__ static type load(rsrc_t r, int off) {
-    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    const f32x4 a = bload<f32x4>(r, off), b = bload<f32x4>(r, off + 16);
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
@@ -229,12 +152,23 @@ template <typename V>
 __device__ __forceinline__ float elem(const V& v, int i) {
   return (float)v[i];
 }
-
-__device__ __forceinline__ void bstore(bf16 x, rsrc_t r, int off) {
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
+// Four consecutive elements of a row (one 8- or 16-byte access).
+template <typename T>
+struct Row4;
+template <>
+struct Row4<bf16> {
+  typedef bf16x4 type;
+};
+template <>
+struct Row4<float> {
+  typedef f32x4 type;
+};
+__device__ __forceinline__ void bstore4(const f32x4& v, rsrc_t r, int off, bf16) {
+  const bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), r, off, 0, 0);
 }
-__device__ __forceinline__ void bstore(float x, rsrc_t r, int off) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), r, off, 0, 0);
+__device__ __forceinline__ void bstore4(const f32x4& v, rsrc_t r, int off, float) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -256,22 +190,23 @@ struct PrefillCfg {
   static constexpr int KP = DK + PADE;           // pitch of [*][DK] operand tiles
   static constexpr int CP = C + PADE;            // pitch of [*][C] operand tiles
   static constexpr int AP = C + 4;               // pitch of the fp32 A tile
-  static constexpr int XP = 16 + PADE;           // pitch of 16x16 solve tiles
   static constexpr int CGN = DK / 8;             // gating: groups of 8 key channels
   static constexpr int NRB = NA / CGN;           // gating: row blocks
   static constexpr int RPB = C / NRB;            // gating: rows per block
   static constexpr int RBW = 64 / CGN;           // gating: row blocks per wavefront
-  static constexpr int VCG = VS / 8;             // V: groups of 8 value columns
-  static constexpr int VRPT = 64 * VCG > NA ? 64 * VCG / NA : 1;  // V: rows per loading thread
-  static constexpr int VTH = 64 * VCG / VRPT;    // V: loading threads
   static constexpr int KT = DK / 16;             // key-channel tiles
   static constexpr int NS = DV / VS;             // slices per head
   static_assert(DK == 64 || DK == 128, "DK");
   static_assert(VS % 16 == 0 && DV % VS == 0 && RT % TPW == 0, "VS");
-  static_assert(NRB * CGN == NA && RPB * NRB == C && RPB % 2 == 0 && RBW * CGN == 64, "gating map");
+  static_assert(NRB * CGN == NA && RPB * NRB == C && RBW * CGN == 64, "gating map");
+  static_assert(RPB == 2 || RPB == 4, "a thread's Kh^T run stays inside one 4-token group");
   static_assert(NPW == 4 || NPW == 8, "producer wavefronts");
-  static_assert(VTH <= NA && VTH * VRPT == 64 * VCG, "V map");
 };
+
+// Kh^T is stored with its 4-token groups XOR-permuted per 16 key channels,
+// which spreads the producer's column writes over all banks while the state
+// wavefronts' row reads (one 16-row block per instruction) stay conflict-free.
+__device__ __forceinline__ int kht_swizzle(int row) { return (5 * (row >> 4)) & 15; }
 
 template <class Cfg>
 struct Smem {
@@ -279,23 +214,27 @@ struct Smem {
   E q[Cfg::C][Cfg::KP];     // Qt = Q e^G          (token-major)
   E k[Cfg::C][Cfg::KP];     // Kt = K e^G          (token-major)
   E kh[Cfg::C][Cfg::KP];    // Kh = K e^-G         (token-major)
-  E kht[Cfg::DK][Cfg::CP];  // Kh^T                (key-channel-major)
-  E vt[Cfg::VS][Cfg::CP];   // V^T of the slice    (value-column-major)
+  E kht[Cfg::DK][Cfg::CP];  // Kh^T                (key-channel-major, swizzled)
   E t[Cfg::C][Cfg::CP];     // Tm = (I + A)^-1 Diag(b), row-major
   E p[Cfg::C][Cfg::CP];     // P, row-major
   alignas(16) float a[Cfg::C][Cfg::AP];  // A (fp32), rows 16-byte aligned
   alignas(16) float xd[4][16][20];  // diagonal blocks of X = (I + A)^-1, row-major (fp32)
-  float beta[Cfg::C];
-  alignas(16) float gam[Cfg::DK];  // e^{G_C}
+  alignas(16) float beta[Cfg::C];
+  alignas(16) float gam[2][Cfg::DK];  // e^{G_C}, by chunk parity
   alignas(16) float gsum[Cfg::NPW][Cfg::DK];  // per-wavefront log2-decay totals
 };
 
 // MFMA fragments with a k order that matches the accumulator layout, so that
-// accumulators (S, R, U) feed the next product as B operands straight from
-// registers.  bf16 (16x16x32): slab s covers k = 32s .. 32s+31 and lane group
-// kg holds k = 32s + 4kg + {0..3} and 32s + 16 + 4kg + {0..3}, i.e. rows
-// 4kg..4kg+3 of accumulator tiles 2s and 2s+1.  fp32 (16x16x4): slab s
-// covers k = 16(s/4) + 4kg + (s%4), i.e. element s%4 of accumulator tile s/4.
+// accumulators (S, R, U) feed the next product straight from registers.
+// bf16 (16x16x32): slab s covers k = 32s .. 32s+31 and lane group kg holds
+// k = 32s + 4kg + {0..3} and 32s + 16 + 4kg + {0..3}, i.e. rows 4kg..4kg+3 of
+// accumulator tiles 2s and 2s+1.  fp32 (16x16x4): slab s covers
+// k = 16(s/4) + 4kg + (s%4), i.e. element s%4 of accumulator tile s/4.
+// A and B operands share this layout: lane l16 supplies row l16 of A, or
+// column l16 of B, over the slab's k.  So the accumulator form of a matrix
+// M (lane l: M[4(l/16) + i][l % 16]) is both M's B operand and M^T's A
+// operand, and a tile loaded from row-major rows serves as an A operand of
+// itself or a B operand of its transpose.
 template <typename E>
 struct Frag;
 
@@ -303,10 +242,16 @@ template <>
 struct Frag<bf16> {
   typedef bf16x8 V;
   static constexpr int SLAB = 32;
-  // From a row-major LDS row (the lane's row of an A or Bt tile).
+  // From a row-major LDS row (the lane's row).
   __device__ __forceinline__ static V ld(const bf16* row, int s, int kg) {
     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * s + 4 * kg);
     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * s + 16 + 4 * kg);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // Same, from a row whose 4-element groups are XOR-permuted by sw.
+  __device__ __forceinline__ static V ld_sw(const bf16* row, int s, int kg, int sw) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 4 * ((8 * s + kg) ^ sw));
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 4 * ((8 * s + 4 + kg) ^ sw));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   // From accumulator tiles x (tile 2s) and y (tile 2s + 1).
@@ -325,16 +270,17 @@ struct Frag<float> {
   __device__ __forceinline__ static V ld(const float* row, int s, int kg) {
     return row[16 * (s >> 2) + 4 * kg + (s & 3)];
   }
+  __device__ __forceinline__ static V ld_sw(const float* row, int s, int kg, int sw) {
+    return row[4 * ((4 * (s >> 2) + kg) ^ sw) + (s & 3)];
+  }
   __device__ __forceinline__ static f32x4 mma(V a, V b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
 };
 
 // 16x16 products with both operands in accumulator form: prod(At, B) = A * B,
-// where At holds A^T and B holds B in the accumulator layout (lane l: rows
-// 4(l/16) + i of column l % 16).  The accumulator form of a matrix is its
-// B-operand layout and the accumulator form of its transpose is its
-// A-operand layout, so chains of products never leave registers.  bf16: one
+// where At holds A^T and B holds B.  prod(M, I) = M^T moves a tile to its
+// transpose exactly (for bf16, exactly after the operand rounding).  bf16: one
 // 16x16x16 MFMA on bf16-rounded operands (the transform is stored in bf16
 // afterwards; the extra rounding raises its error from 1.6e-4 to 2.2e-4
 // relative); fp32: four 16x16x4 steps.
@@ -348,6 +294,17 @@ struct Reg16<bf16> {
   __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt(At), cvt(B), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
+  // c + the 16x16 tile given as rows (lane l16: elements 4kg..4kg+3 of row
+  // l16), exact: a product with the identity, in the 16x16x32 shape of the
+  // chains it joins (the rows fill k = 0..15, the upper half of k is zero).
+  // An accumulator produced by one MFMA shape is never fed to another shape
+  // as its C operand.
+  __device__ __forceinline__ static f32x4 rows(const bf16x4& r, const f32x4& ident, const f32x4& c) {
+    const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    const bf16x4 i4 = {(bf16)ident[0], (bf16)ident[1], (bf16)ident[2], (bf16)ident[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(r, z, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                   __builtin_shufflevector(i4, z, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
+  }
 };
 template <>
 struct Reg16<float> {
@@ -357,17 +314,20 @@ struct Reg16<float> {
     for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(At[i], B[i], c, 0, 0, 0);
     return c;
   }
+  __device__ __forceinline__ static f32x4 rows(const f32x4& r, const f32x4& ident, const f32x4& c) {
+    f32x4 d = c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_mfma_f32_16x16x4f32(r[i], ident[i], d, 0, 0, 0);
+    return d;
+  }
 };
 
 // (I + N)^-1 for a strictly lower 16x16 N (nilpotent, N^16 = 0), as the
 // product (I + N^8)(I + N^4)(I + N^2)(I - N) = sum_{k<16} (-N)^k.
 // N and Nt are N and N^T in accumulator form; returns X in accumulator form.
 template <typename E>
-__device__ __forceinline__ f32x4 unit_lower_inverse16(const f32x4& N, const f32x4& Nt, int lane) {
+__device__ __forceinline__ f32x4 unit_lower_inverse16(const f32x4& N, const f32x4& Nt, const f32x4& I4) {
   typedef Reg16<E> R;
-  f32x4 I4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) I4[i] = (4 * (lane >> 4) + i == (lane & 15)) ? 1.f : 0.f;
   const f32x4 N2 = R::prod(Nt, N), N2t = R::prod(N, Nt);
   const f32x4 N4 = R::prod(N2t, N2), N4t = R::prod(N2, N2t);
   const f32x4 N8t = R::prod(N4, N4t);
@@ -376,7 +336,8 @@ __device__ __forceinline__ f32x4 unit_lower_inverse16(const f32x4& N, const f32x
   return R::prod(I4 + N8t, Z2);
 }
 
-// B-operand fragment of slab s from accumulator tiles acc[0..n) along k.
+// Operand fragment of slab s from accumulator tiles acc[0..n) along k (and
+// the same for the negated tiles).
 template <int N>
 __device__ __forceinline__ bf16x8 acc_frag(const f32x4 (&acc)[N], int s, bf16) {
   return Frag<bf16>::acc2(acc[2 * s], acc[2 * s + 1]);
@@ -385,29 +346,38 @@ template <int N>
 __device__ __forceinline__ float acc_frag(const f32x4 (&acc)[N], int s, float) {
   return acc[s >> 2][s & 3];
 }
+template <int N>
+__device__ __forceinline__ bf16x8 acc_frag_neg(const f32x4 (&acc)[N], int s, bf16) {
+  return Frag<bf16>::acc2(-acc[2 * s], -acc[2 * s + 1]);
+}
+template <int N>
+__device__ __forceinline__ float acc_frag_neg(const f32x4 (&acc)[N], int s, float) {
+  return -acc[s >> 2][s & 3];
+}
 
 // ---------------------------------------------------------------------------
-// The kernel.  Wavefronts 0-3 (producer) prepare chunk c+1 -- gating, the
-// k-k and q-k blocks and the UT transform -- while wavefronts 4.. (state)
-// run the state pass of chunk c.  One iteration, between LDS barriers:
+// The kernel.  Producer wavefronts prepare chunk c while state wavefronts run
+// the state pass; one iteration, between LDS barriers:
 //
-//   X0 | producer: decay block sums, V^T, beta  | state: U = Tm R, O += P U, o
-//  MID | producer: gated Qt, Kt, Kh             | state: S <- e^{G_C} (S + Kh^T U)
-//   X1 | producer: A, P, diagonal solve blocks  | state: R = V - Kt S
-//   X2 | producer: off-diagonal solve, Kh^T, e^G| state: O = Qt S
+//   X0 | producer: decay block sums, beta        | state: U = Tm R, O += P U, o
+//  MID | producer: gated Qt, Kt, Kh, e^{G_C}     | state: S <- e^{G_C} (S + Kh^T U)
+//   X1 | producer: A, P, diagonal solve blocks   | state: R = V - Kt S
+//   X2 | producer: blocks below the diagonal, Kh^T | state: O = Qt S
 //
-// Each state wavefront owns TPW 16-column tiles of the slice and keeps S,
-// R/U and O in registers; from LDS it reads only producer outputs.
+// Each state wavefront owns TPW 16-column tiles of the slice and keeps S, R/U
+// and O^T in registers; it reads V from HBM itself and producer outputs from
+// LDS.  Products whose result leaves the registers are taken transposed
+// (operands swapped), so that a lane holds four consecutive columns of a
+// row: 8- or 16-byte writes to LDS and HBM.
 // ---------------------------------------------------------------------------
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
   typedef typename Cfg::T T;
   typedef typename Cfg::E E;
   typedef Frag<E> F;
-  typedef Mma<E> M;
-  constexpr int DK = Cfg::DK, DV = Cfg::DV, VS = Cfg::VS, GG = Cfg::GG, C = Cfg::C;
-  constexpr int NS = Cfg::NS, TPW = Cfg::TPW, KT = Cfg::KT, RPB = Cfg::RPB;
-  constexpr int VP = VS / 2, VRG = Cfg::NA / VP, VRPT = C / VRG;
+  typedef typename F::V FV;
+  constexpr int DK = Cfg::DK, DV = Cfg::DV, VS = Cfg::VS, GG = Cfg::GG, C = Cfg::C, KP = Cfg::KP;
+  constexpr int NS = Cfg::NS, TPW = Cfg::TPW, KT = Cfg::KT, RPB = Cfg::RPB, NPW = Cfg::NPW;
   constexpr int SLAB = F::SLAB;
   constexpr int SK = DK / SLAB;  // slabs over key channels
   constexpr int SC = C / SLAB;   // slabs over the chunk's tokens
@@ -418,7 +388,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int l16 = lane & 15, kg = lane >> 4;
-  const bool producer = wave < Cfg::NPW;
+  const bool producer = wave < NPW;
 
   // ---- workgroup -> (unit, slice); the NS slices of a unit share an XCD ----
   const int grp = blockIdx.x / (8 * NS);
@@ -452,6 +422,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
   T* __restrict__ go = static_cast<T*>(args.o);
   const size_t state_off = ((size_t)seq * H + h) * DK * DV;
 
+  f32x4 ident;  // 16x16 identity, accumulator form
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
+
   // ---- upper 16x16 tiles of Tm and P are zero and never written again ----
   for (int idx = tid; idx < C * C; idx += Cfg::NT) {
     const int r = idx / C, c = idx % C;
@@ -461,37 +435,45 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
     }
   }
 
+  // Fragments of the 16-row block blk of a token-major operand tile.
+  auto ld_rows = [&](FV (&fr)[SK], const E (*tile)[KP], int blk) {
+    const E* row = &tile[0][0] + opaque(l16 * KP) + 16 * blk * KP;
+#pragma unroll
+    for (int s = 0; s < SK; ++s) fr[s] = F::ld(row, s, kg);
+  };
+  auto mma_rows = [&](const FV (&a)[SK], const FV (&b)[SK]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SK; ++s) acc = F::mma(a[s], b[s], acc);
+    return acc;
+  };
+
   if (producer) {
     // ================= producer wavefronts ===================================
     // Gating map: thread = (8 key channels, block of RPB consecutive tokens);
-    // the row blocks of one wavefront cover 16 consecutive tokens.
-    // V map: thread = (8 value columns, VRPT consecutive tokens).
+    // the row blocks of one wavefront cover 64 / (DK / 8) * RPB consecutive tokens.
     typedef typename Vec8<T>::type V8;
     typedef typename Pair<E>::type EP2;
     constexpr int CGN = Cfg::CGN, RBW = Cfg::RBW;
-    constexpr int VCG = Cfg::VCG, VRPT = Cfg::VRPT, VTH = Cfg::VTH;
     const int cg = tid % CGN, rb = tid / CGN;
     const int ch = 8 * cg;                 // first key channel of this thread
     const int rbw = lane / CGN;            // row block within the wavefront
-    const int vcg = tid % VCG, vrb = tid / VCG;
-    V8 rq[RPB], rk[RPB], rg[GG == 1 ? RPB : 1], rv[VRPT];
+    V8 rq[RPB], rk[RPB], rg[GG == 1 ? RPB : 1];
     T rgs[GG == 1 ? 1 : RPB], rbeta;
     // All loads of a chunk are in flight together; rows past the end of the
     // sequence read as zero through the per-chunk buffer bounds.
-    const int rsk = H * DK * (int)sizeof(T);           // token stride of q, k (bytes)
-    const int rsg = H * (DK / GG) * (int)sizeof(T);    // token stride of g
-    const int rsv = H * DV * (int)sizeof(T);           // token stride of v
-    const int rsb = H * (int)sizeof(T);                // token stride of beta
+    const int rsk = H * DK * (int)sizeof(T);         // token stride of q, k (bytes)
+    const int rsg = H * (DK / GG) * (int)sizeof(T);  // token stride of g
+    const int rsb = H * (int)sizeof(T);              // token stride of beta
     // The prefetch of the next chunk is split in three parts, each issued as
     // soon as its registers are free, so that no single wave stalls on a long
     // burst of loads (the vector L1 moves about 64 bytes per clock).
     auto chunk_rows = [&](int ck) { return min(C, len - ck * C); };
     auto chunk_row0 = [&](int ck) { return (size_t)(tok0 + ck * C) * H + h; };
-    auto load_gvb = [&](int ck) {  // g, v, beta
+    auto load_gb = [&](int ck) {  // g, beta
       const int nv = chunk_rows(ck);
       const size_t row0 = chunk_row0(ck);
       const rsrc_t bg = make_rsrc(gg + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * (int)sizeof(T));
-      const rsrc_t bv = make_rsrc(gv + row0 * DV + col0, (nv - 1) * rsv + VS * (int)sizeof(T));
       const rsrc_t bb = make_rsrc(gb + row0, (nv - 1) * rsb + (int)sizeof(T));
 #pragma unroll
       for (int j = 0; j < RPB; ++j) {
@@ -500,10 +482,6 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
           rg[j] = Vec8<T>::load(bg, r * rsg + ch * (int)sizeof(T));
         else
           rgs[j] = bload<T>(bg, r * rsg + (ch / GG) * (int)sizeof(T));
-      }
-      if (tid < VTH) {
-#pragma unroll
-        for (int j = 0; j < VRPT; ++j) rv[j] = Vec8<T>::load(bv, (vrb * VRPT + j) * rsv + 8 * vcg * (int)sizeof(T));
       }
       if (tid < C) rbeta = bload<T>(bb, tid * rsb);
     };
@@ -519,42 +497,84 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
     };
     float G[RPB][8];        // cumulative log2-decay of this thread's rows (block-local)
     float off[8];           // log2-decay of the chunk before this thread's block
-    float eT[8];            // e^{G_C} of this thread's channels
     EP2 khp[8][RPB / 2];    // Kh of this thread's rows per channel (token pairs), for Kh^T
     f32x4 Xdiag;            // X_ww = (I + A_ww)^-1 of this wave's block, accumulator form
-    // P = lower_incl_diag(Qt Kh^T) for row block IP (upper tiles stay zero)
-    auto p_tiles = [&](int IP) {
-      typename F::V qa[SK];
+    // Kh^T run of this thread: channels ch..ch+7 share one swizzle
+    const int kht_col = ((((rb * RPB) >> 2) ^ kht_swizzle(ch)) << 2) | ((rb * RPB) & 3);
+
+    // ---- tile jobs.  Operands are ordered for the transposed product, so a
+    // lane ends with four consecutive columns of one row of the block. ----
+    // A_IJ below the diagonal (I > J), fp32 row-major; khJ = fragments of Kh block J
+    auto a_tile = [&](int I, int J, const FV (&khJ)[SK]) {
+      FV kt[SK];
+      ld_rows(kt, sm.k, I);
+      const f32x4 d = mma_rows(khJ, kt) * sm.beta[opaque(l16) + 16 * I];
+      *reinterpret_cast<f32x4*>(&sm.a[0][0] + opaque(l16 * Cfg::AP + 4 * kg) + 16 * I * Cfg::AP + 16 * J) = d;
+    };
+    // P_IJ below the diagonal (I > J)
+    auto p_tile = [&](int I, int J, const FV (&khJ)[SK]) {
+      FV qt[SK];
+      ld_rows(qt, sm.q, I);
+      store4<E>(&sm.p[0][0] + opaque(l16 * Cfg::CP + 4 * kg) + 16 * I * Cfg::CP + 16 * J, mma_rows(khJ, qt));
+    };
+    // Diagonal block I: N = A_II and N^T (registers only), P_II, and the
+    // inverse X_II = (I + N)^-1 kept in registers for the forward substitution;
+    // X_II (row-major, fp32) and Tm_II = X_II Diag(b_I) go to LDS.
+    auto diag_job = [&](int I) {
+      FV kt[SK], kh[SK], qt[SK];
+      ld_rows(kt, sm.k, I);
+      ld_rows(kh, sm.kh, I);
+      ld_rows(qt, sm.q, I);
+      f32x4 N = mma_rows(kt, kh), Nt = mma_rows(kh, kt);
+      f32x4 Pt = mma_rows(kh, qt);
+      const float bl = sm.beta[opaque(l16) + 16 * I];
+      const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[opaque(4 * kg) + 16 * I]);
 #pragma unroll
-      for (int s = 0; s < SK; ++s) qa[s] = F::ld(&sm.q[16 * IP + l16][0], s, kg);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * kg + i;
+        N[i] = l16 < r ? N[i] * br[i] : 0.f;  // strictly lower, rows scaled
+        Nt[i] = r < l16 ? Nt[i] * bl : 0.f;
+        Pt[i] = r <= l16 ? Pt[i] : 0.f;                     // lower including the diagonal
+      }
+      const int pt = opaque(l16 * Cfg::CP + 4 * kg) + 16 * I * Cfg::CP + 16 * I;
+      store4<E>(&sm.p[0][0] + pt, Pt);
+      Xdiag = unit_lower_inverse16<E>(N, Nt, ident);
+      *reinterpret_cast<f32x4*>(&sm.xd[I][0][0] + opaque(20 * l16 + 4 * kg)) = Reg16<E>::prod(Xdiag, ident);
+      store4<E>(&sm.t[0][0] + pt, Reg16<E>::prod(Xdiag * bl, ident));
+    };
+    // Blocks below the diagonal in block column J, top to bottom; each needs
+    // only this column's blocks above it (registers) and the diagonal blocks:
+    // X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ.
+    auto solve_column = [&](auto Jc) {
+      constexpr int J = decltype(Jc)::value;
+      const float bj = sm.beta[opaque(l16) + 16 * J];
+      const int ao = opaque(l16 * Cfg::AP + 4 * kg), xo = opaque(20 * l16 + 4 * kg);
+      const int to = opaque(l16 * Cfg::CP + 4 * kg);
+      f32x4 Xc[4 - J];  // X_KJ, K = J .. 3, accumulator form
+      Xc[0] = Xdiag;
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        if (J <= IP) {
-          typename F::V hb[SK];
+      for (int d = 1; d < 4 - J; ++d) {
+        const int I = J + d;
+        f32x4 M = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < SK; ++s) hb[s] = F::ld(&sm.kh[16 * J + l16][0], s, kg);
-          f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < SK; ++s) pacc = F::mma(qa[s], hb[s], pacc);
-          const int col = 16 * J + l16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * IP + 4 * kg + i;
-            float pv = pacc[i];
-            if (J == IP) pv = col > row ? 0.f : pv;  // lower including the diagonal
-            sm.p[row][col] = from_f32<E>(pv);
-          }
+        for (int e = 0; e < d; ++e) {
+          // (A_{I,J+e})^T in accumulator form: lane holds A[16I + l16][16(J+e) + 4kg + i]
+          const f32x4 At = *reinterpret_cast<const f32x4*>(&sm.a[0][0] + ao + 16 * I * Cfg::AP + 16 * (J + e));
+          M += Reg16<E>::prod(At, Xc[e]);
         }
+        const f32x4 XIt = *reinterpret_cast<const f32x4*>(&sm.xd[I][0][0] + xo);
+        Xc[d] = -Reg16<E>::prod(XIt, M);
+        store4<E>(&sm.t[0][0] + to + 16 * I * Cfg::CP + 16 * J, Reg16<E>::prod(Xc[d] * bj, ident));
       }
     };
+
     if (nchunks > 0) {
-      load_gvb(0);
+      load_gb(0);
       load_q(0);
       load_k(0);
     }
 
     for (int it = 0; it <= nchunks; ++it) {
-      const int cbase = it * C;  // chunk it
       lds_barrier();  // -------------------------------------------------- X0
       if (it < nchunks) {
         // block-local cumulative decay; prefix over this wavefront's blocks
@@ -586,22 +606,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) off[c] -= acc[c];  // exclusive within the wavefront
-        // V^T of the slice: one contiguous run of VRPT tokens per column
-        if (tid < VTH) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            float vr[VRPT];
-#pragma unroll
-            for (int j = 0; j < VRPT; ++j) vr[j] = elem(rv[j], c);
-            store_run<E, VRPT>(&sm.vt[8 * vcg + c][vrb * VRPT], vr);
-          }
-        }
         if (tid < C) sm.beta[tid] = to_f32(rbeta);
       }
       lds_barrier();  // ------------------------------------------------- MID
-      if (it + 1 < nchunks) load_gvb(it + 1);  // prefetch (g, v, beta registers are free)
+      if (it + 1 < nchunks) load_gb(it + 1);  // prefetch (g, beta registers are free)
       if (it < nchunks) {
-        // gated operands Qt, Kt, Kh (token-major)
         // decay before this thread's block: earlier wavefronts' totals
         for (int w = 0; w < wave; ++w) {  // uniform trip count
           const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch]);
@@ -612,11 +621,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
             off[c + 4] += b[c];
           }
         }
-        // the chunk's total decay: the last row block's inclusive prefix
-        if (rb == Cfg::NRB - 1) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) eT[c] = fast_exp2(off[c] + G[RPB - 1][c]);
-        }
+        // gated operands Qt, Kt, Kh (token-major)
+        float eL[8];  // e^G of this thread's last row
 #pragma unroll
         for (int j = 0; j < RPB; ++j) {
           const int r = rb * RPB + j;
@@ -626,6 +632,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
             const float Gc = off[c] + G[j][c];
             e[c] = fast_exp2(Gc);
             n[c] = fast_exp2(-Gc);
+            if (j == RPB - 1) eL[c] = e[c];
           }
           float qo[8], ko[8], ho[8];
 #pragma unroll
@@ -636,118 +643,102 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
             ho[c] = kx * n[c];
             khp[c][j >> 1][j & 1] = from_f32<E>(ho[c]);
           }
-          store_run<E, 8>(&sm.q[r][ch], qo);
-          store_run<E, 8>(&sm.k[r][ch], ko);
-          store_run<E, 8>(&sm.kh[r][ch], ho);
+#pragma unroll
+          for (int c = 0; c < 8; c += 4) {
+            store4<E>(&sm.q[r][ch + c], f32x4{qo[c], qo[c + 1], qo[c + 2], qo[c + 3]});
+            store4<E>(&sm.k[r][ch + c], f32x4{ko[c], ko[c + 1], ko[c + 2], ko[c + 3]});
+            store4<E>(&sm.kh[r][ch + c], f32x4{ho[c], ho[c + 1], ho[c + 2], ho[c + 3]});
+          }
+        }
+        // the chunk's decay e^{G_C}: the last row of the chunk (its buffer
+        // alternates with the chunk parity; the state pass reads the other)
+        if (rb == Cfg::NRB - 1) {
+          *reinterpret_cast<f32x4*>(&sm.gam[it & 1][ch]) = f32x4{eL[0], eL[1], eL[2], eL[3]};
+          *reinterpret_cast<f32x4*>(&sm.gam[it & 1][ch + 4]) = f32x4{eL[4], eL[5], eL[6], eL[7]};
         }
       }
       lds_barrier();  // -------------------------------------------------- X1
       if (it + 1 < nchunks) load_q(it + 1);  // prefetch (q registers are free)
-      if (it < nchunks && Cfg::NPW == 8 && wave >= 4) p_tiles(wave - 4);
-      if (it < nchunks && wave < 4) {
-        // A row block w (tiles J <= w, fragment loads issued up front), then
-        // the diagonal block X_ww = (I + A_ww)^-1 in registers.
-        const int I = wave;
-        f32x4 aacc[4];
-        {
-          typename F::V ka[SK];
-#pragma unroll
-          for (int s = 0; s < SK; ++s) ka[s] = F::ld(&sm.k[16 * I + l16][0], s, kg);
-#pragma unroll
-          for (int J = 0; J < 4; ++J) {
-            aacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (J <= I) {
-              typename F::V hb[SK];
-#pragma unroll
-              for (int s = 0; s < SK; ++s) hb[s] = F::ld(&sm.kh[16 * J + l16][0], s, kg);
-#pragma unroll
-              for (int s = 0; s < SK; ++s) aacc[J] = F::mma(ka[s], hb[s], aacc[J]);
+      if (it < nchunks) {
+        // A and P: 10 + 10 tiles and four diagonal inverses over the producers
+        static_switch<NPW>(wave, [&](auto Wc) {
+          constexpr int W = decltype(Wc)::value;
+          if constexpr (W < 4) diag_job(W);
+          FV kh0[SK];
+          if constexpr (NPW == 8) {
+            if constexpr (W == 4) {
+              ld_rows(kh0, sm.kh, 0);
+              a_tile(1, 0, kh0);
+              p_tile(1, 0, kh0);
+              a_tile(3, 0, kh0);
+            } else if constexpr (W == 5) {
+              ld_rows(kh0, sm.kh, 0);
+              p_tile(3, 0, kh0);
+              a_tile(2, 0, kh0);
+              p_tile(2, 0, kh0);
+            } else if constexpr (W == 6) {
+              ld_rows(kh0, sm.kh, 1);
+              a_tile(2, 1, kh0);
+              p_tile(2, 1, kh0);
+              a_tile(3, 1, kh0);
+            } else if constexpr (W == 7) {
+              ld_rows(kh0, sm.kh, 1);
+              p_tile(3, 1, kh0);
+              ld_rows(kh0, sm.kh, 2);
+              a_tile(3, 2, kh0);
+              p_tile(3, 2, kh0);
+            }
+          } else {  // four producers: the A blocks now, the P blocks with the solve
+            if constexpr (W == 0) {
+              ld_rows(kh0, sm.kh, 0);
+              a_tile(1, 0, kh0);
+              a_tile(2, 0, kh0);
+            } else if constexpr (W == 1) {
+              ld_rows(kh0, sm.kh, 1);
+              a_tile(2, 1, kh0);
+              ld_rows(kh0, sm.kh, 0);
+              a_tile(3, 0, kh0);
+            } else if constexpr (W == 2) {
+              ld_rows(kh0, sm.kh, 1);
+              a_tile(3, 1, kh0);
+            } else if constexpr (W == 3) {
+              ld_rows(kh0, sm.kh, 2);
+              a_tile(3, 2, kh0);
             }
           }
-        }
-        // A = strictly_lower(Diag(beta) Kt Kh^T), fp32
-        {
-          f32x4 brow;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) brow[i] = sm.beta[16 * I + 4 * kg + i];
-#pragma unroll
-          for (int J = 0; J < 4; ++J) {
-            if (J <= I) {
-              const int col = 16 * J + l16;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int row = 16 * I + 4 * kg + i;
-                aacc[J][i] *= brow[i];
-                if (J == I) aacc[J][i] = col >= row ? 0.f : aacc[J][i];  // strictly lower
-                sm.a[row][col] = aacc[J][i];
-              }
-            }
-          }
-        }
-        lds_wave_sync();
-        // diagonal block: N = A_II in accumulator form is aacc[I]; N^T from LDS
-        {
-          f32x4 N = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int J = 0; J < 4; ++J)
-            if (J == I) N = aacc[J];
-          const f32x4 Nt = *reinterpret_cast<const f32x4*>(&sm.a[16 * I + l16][16 * I + 4 * kg]);
-          Xdiag = unit_lower_inverse16<E>(N, Nt, lane);
-          const float bj = sm.beta[16 * I + l16];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sm.xd[I][4 * kg + i][l16] = Xdiag[i];
-            sm.t[16 * I + 4 * kg + i][16 * I + l16] = from_f32<E>(Xdiag[i] * bj);
-          }
-        }
+        });
       }
       lds_barrier();  // -------------------------------------------------- X2
       if (it + 1 < nchunks) load_k(it + 1);  // prefetch (k registers are free)
       if (it < nchunks) {
-        // Off-diagonal blocks: wave J walks down block column J, which depends
-        // only on its own earlier blocks (kept in registers) and on the
-        // diagonal blocks:  X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ.
-        if (wave < 3) {
-          const int J = wave;
-          const float bj = sm.beta[16 * J + l16];
-          f32x4 Xc[4];  // X_KJ, K = J .. 3, accumulator form
-          Xc[0] = Xdiag;
+        static_switch<NPW>(wave, [&](auto Wc) {
+          constexpr int W = decltype(Wc)::value;
+          if constexpr (W < 3) solve_column(IC<W>{});
+          if constexpr (NPW == 4 && W > 0) {  // P blocks below the diagonal, against the solve's load
+            FV khj[SK];
 #pragma unroll
-          for (int d = 1; d < 4; ++d) {
-            if (J + d < 4) {
-              const int I = J + d;
-              f32x4 Mt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int e = 0; e < d; ++e) {
-                // At = (A_{I,J+e})^T in accumulator form: lane holds A[16I + l16][16(J+e) + 4kg + i]
-                const f32x4 At = *reinterpret_cast<const f32x4*>(&sm.a[16 * I + l16][16 * (J + e) + 4 * kg]);
-                Mt += Reg16<E>::prod(At, Xc[e]);
-              }
-              const f32x4 XIt = *reinterpret_cast<const f32x4*>(&sm.xd[I][l16][4 * kg]);
-              Xc[d] = -Reg16<E>::prod(XIt, Mt);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sm.t[16 * I + 4 * kg + i][16 * J + l16] = from_f32<E>(Xc[d][i] * bj);
+            for (int J = 0; J < W; ++J) {
+              ld_rows(khj, sm.kh, J);
+              p_tile(W, J, khj);
             }
           }
-        }
-        if constexpr (Cfg::NPW == 4) p_tiles(wave);  // balances the sweeps above
-        // transposed Kh and the chunk decay, read by the state pass next
+        });
+        // transposed Kh, read by the state pass next
 #pragma unroll
-        for (int c = 0; c < 8; ++c) store_pairs<E, RPB / 2>(&sm.kht[ch + c][rb * RPB], khp[c]);
-        if (rb == Cfg::NRB - 1) {
-          *reinterpret_cast<f32x4*>(&sm.gam[ch]) = f32x4{eT[0], eT[1], eT[2], eT[3]};
-          *reinterpret_cast<f32x4*>(&sm.gam[ch + 4]) = f32x4{eT[4], eT[5], eT[6], eT[7]};
-        }
+        for (int c = 0; c < 8; ++c) store_pairs<E, RPB / 2>(&sm.kht[ch + c][kht_col], khp[c]);
       }
     }
     return;
   }
 
   // ================= state wavefronts ======================================
-  const int bw = wave - Cfg::NPW;  // state wavefront index
+  const int bw = wave - NPW;  // state wavefront index
+  // The state pass carries the recurrence; its short VALU/LDS/MFMA bursts are
+  // issued ahead of the producers' long VALU streams on the same SIMD.
+  __builtin_amdgcn_s_setprio(2);
   f32x4 S[TPW][KT];         // S: rows (key channels) 16mt + 4kg + i, column l16
-  f32x4 R[TPW][4];          // R, then U: token rows 16t + 4kg + i
-  f32x4 O[TPW][4];
+  f32x4 R[TPW][4];          // R, then U: token rows 16t + 4kg + i, column l16
+  f32x4 O[TPW][4];          // O^T: lane holds token 16t + l16, columns 4kg + i
   {
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -760,14 +751,27 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
     }
   }
 
-  const int rso = H * DV * (int)sizeof(T);  // token stride of o (bytes)
-  typename F::V UF[TPW][SC];  // U as B-operand fragments (bf16 or fp32)
+  const int rsv = H * DV * (int)sizeof(T);  // token stride of v and o (bytes)
+  // V rows of the next chunk: lane holds 4 columns of token 16t + l16
+  typename Row4<T>::type vr[TPW][4];
+  auto load_v = [&](int ck) {
+    const int nv = min(C, len - ck * C);
+    const rsrc_t bv = make_rsrc(gv + ((size_t)(tok0 + ck * C) * H + h) * DV + col0, (nv - 1) * rsv + VS * (int)sizeof(T));
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        vr[j][t] = bload<typename Row4<T>::type>(bv, (16 * t + l16) * rsv + (16 * (TPW * bw + j) + 4 * kg) * (int)sizeof(T));
+  };
+  if (nchunks > 0) load_v(0);
+
+  FV UF[TPW][SC];  // U as operand fragments (bf16 or fp32)
   for (int it = 0; it <= nchunks; ++it) {
     lds_barrier();  // -------------------------------------------------- X0
     if (it >= 1) {
       // ---- state: U = Tm R (Tm lower triangular: tile t needs k < 16(t+1)) ----
       {
-        typename F::V RF[TPW][SC];
+        FV RF[TPW][SC];
 #pragma unroll
         for (int j = 0; j < TPW; ++j)
 #pragma unroll
@@ -779,7 +783,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
           const E* trow = &sm.t[16 * t + l16][0];
 #pragma unroll
           for (int s = 0; s < (16 * (t + 1) + SLAB - 1) / SLAB; ++s) {
-            const typename F::V a = F::ld(trow, s, kg);
+            const FV a = F::ld(trow, s, kg);
 #pragma unroll
             for (int j = 0; j < TPW; ++j) R[j][t] = F::mma(a, RF[j][s], R[j][t]);
           }
@@ -789,25 +793,22 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
 #pragma unroll
           for (int s = 0; s < SC; ++s) UF[j][s] = acc_frag(R[j], s, E());
       }
-      // ---- O += P U, then write o of chunk it - 1 ----
+      // ---- O^T += U^T P^T, then write o of chunk it - 1 (rows of 4 columns) ----
       const int pbase = (it - 1) * C;
       const int nv = min(C, len - pbase);
-      const rsrc_t bo = make_rsrc(go + ((size_t)(tok0 + pbase) * H + h) * DV + col0, (nv - 1) * rso + VS * (int)sizeof(T));
+      const rsrc_t bo = make_rsrc(go + ((size_t)(tok0 + pbase) * H + h) * DV + col0, (nv - 1) * rsv + VS * (int)sizeof(T));
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const E* prow = &sm.p[16 * t + l16][0];
 #pragma unroll
         for (int s = 0; s < (16 * (t + 1) + SLAB - 1) / SLAB; ++s) {
-          const typename F::V a = F::ld(prow, s, kg);
+          const FV b = F::ld(prow, s, kg);
 #pragma unroll
-          for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(a, UF[j][s], O[j][t]);
+          for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(UF[j][s], b, O[j][t]);
         }
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-          const int cb = (16 * (TPW * bw + j) + l16) * (int)sizeof(T);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) bstore(from_f32<T>(O[j][t][i]), bo, (16 * t + 4 * kg + i) * rso + cb);
-        }
+        for (int j = 0; j < TPW; ++j)
+          bstore4(O[j][t], bo, (16 * t + l16) * rsv + (16 * (TPW * bw + j) + 4 * kg) * (int)sizeof(T), T());
       }
     }
     lds_barrier();  // ------------------------------------------------- MID
@@ -816,25 +817,26 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
 #pragma unroll
       for (int mt = 0; mt < KT; ++mt) {
         const E* krow = &sm.kht[16 * mt + l16][0];
+        const int sw = kht_swizzle(16 * mt);
 #pragma unroll
         for (int s = 0; s < SC; ++s) {
-          const typename F::V a = F::ld(krow, s, kg);
+          const FV a = F::ld_sw(krow, s, kg, sw);
 #pragma unroll
           for (int j = 0; j < TPW; ++j) S[j][mt] = F::mma(a, UF[j][s], S[j][mt]);
         }
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[16 * mt + 4 * kg]);
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[(it - 1) & 1][16 * mt + 4 * kg]);
 #pragma unroll
         for (int j = 0; j < TPW; ++j) S[j][mt] *= gm;
       }
     }
     lds_barrier();  // -------------------------------------------------- X1
     if (it < nchunks) {
-      // ---- state: R = V - Kt S ----
-      typename F::V SF[TPW][SK];  // S as B-operand fragments
+      // ---- state: R = V - Kt S (V enters through an exact identity product) ----
+      FV SF[TPW][SK];  // -S as B-operand fragments
 #pragma unroll
       for (int j = 0; j < TPW; ++j)
 #pragma unroll
-        for (int s = 0; s < SK; ++s) SF[j][s] = acc_frag(S[j], s, E());
+        for (int s = 0; s < SK; ++s) SF[j][s] = acc_frag_neg(S[j], s, E());
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -842,21 +844,19 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
         const E* krow = &sm.k[16 * t + l16][0];
 #pragma unroll
         for (int s = 0; s < SK; ++s) {
-          const typename F::V a = F::ld(krow, s, kg);
+          const FV a = F::ld(krow, s, kg);
 #pragma unroll
           for (int j = 0; j < TPW; ++j) R[j][t] = F::mma(a, SF[j][s], R[j][t]);
         }
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-          const f32x4 vv = load4<E>(&sm.vt[16 * (TPW * bw + j) + l16][16 * t + 4 * kg]);
-          R[j][t] = vv - R[j][t];
-        }
+        for (int j = 0; j < TPW; ++j) R[j][t] = Reg16<E>::rows(vr[j][t], ident, R[j][t]);
       }
+      if (it + 1 < nchunks) load_v(it + 1);  // prefetch (V registers are free)
     }
     lds_barrier();  // -------------------------------------------------- X2
     if (it < nchunks) {
-      // ---- state: O = Qt S ----
-      typename F::V SF[TPW][SK];
+      // ---- state: O^T = S^T Qt^T ----
+      FV SF[TPW][SK];
 #pragma unroll
       for (int j = 0; j < TPW; ++j)
 #pragma unroll
@@ -868,9 +868,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
         const E* qrow = &sm.q[16 * t + l16][0];
 #pragma unroll
         for (int s = 0; s < SK; ++s) {
-          const typename F::V a = F::ld(qrow, s, kg);
+          const FV b = F::ld(qrow, s, kg);
 #pragma unroll
-          for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(a, SF[j][s], O[j][t]);
+          for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(SF[j][s], b, O[j][t]);
         }
       }
     }
@@ -984,3 +984,4 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
 }
 
 }  // namespace kda
+
