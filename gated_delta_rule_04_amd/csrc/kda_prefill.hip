@@ -188,6 +188,11 @@ struct PrefillCfg {
   static constexpr int NT = NA + 64 * NBW;       // threads per workgroup
   static constexpr int PADE = 8 / sizeof(E);     // 8-byte row skew: pitch = 2 (mod 32) dwords
   static constexpr int KP = DK + PADE;           // pitch of [*][DK] operand tiles
+  // bf16: Kh^T fragments come from the token-major Kh tile through transposing
+  // LDS reads (gfx950 ds_read_b64_tr_b16); Kh rows are then 16 elements longer
+  // and XOR-permuted, and no separate Kh^T tile exists.  fp32 keeps Kh^T.
+  static constexpr bool TR = sizeof(E) == 2;
+  static constexpr int KHP = TR ? DK + 16 : KP;  // pitch of the Kh tile
   static constexpr int CP = C + PADE;            // pitch of [*][C] operand tiles
   static constexpr int AP = C + 4;               // pitch of the fp32 A tile
   static constexpr int CGN = DK / 8;             // gating: groups of 8 key channels
@@ -207,14 +212,18 @@ struct PrefillCfg {
 // which spreads the producer's column writes over all banks while the state
 // wavefronts' row reads (one 16-row block per instruction) stay conflict-free.
 __device__ __forceinline__ int kht_swizzle(int row) { return (5 * (row >> 4)) & 15; }
+// bf16 Kh rows: 4-element unit u of token row r is stored at unit u ^ ((r / 4) % 4).
+// Row reads (16 consecutive rows), transposing reads (4 rows x 4 units per
+// 16 lanes) and the producer's row writes then spread over all banks.
+__device__ __forceinline__ int kh_swizzle(int row) { return (row >> 2) & 3; }
 
 template <class Cfg>
 struct Smem {
   typedef typename Cfg::E E;
   E q[Cfg::C][Cfg::KP];     // Qt = Q e^G          (token-major)
   E k[Cfg::C][Cfg::KP];     // Kt = K e^G          (token-major)
-  E kh[Cfg::C][Cfg::KP];    // Kh = K e^-G         (token-major)
-  E kht[Cfg::DK][Cfg::CP];  // Kh^T                (key-channel-major, swizzled)
+  E kh[Cfg::C][Cfg::KHP];   // Kh = K e^-G         (token-major; bf16: swizzled)
+  E kht[Cfg::TR ? 1 : Cfg::DK][Cfg::CP];  // Kh^T  (fp32 only; key-channel-major, swizzled)
   E t[Cfg::C][Cfg::CP];     // Tm = (I + A)^-1 Diag(b), row-major
   E p[Cfg::C][Cfg::CP];     // P, row-major
   alignas(16) float a[Cfg::C][Cfg::AP];  // A (fp32), rows 16-byte aligned
@@ -253,6 +262,21 @@ struct Frag<bf16> {
     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 4 * ((8 * s + kg) ^ sw));
     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 4 * ((8 * s + 4 + kg) ^ sw));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // Fragment of M^T from a token-major tile M (swizzled by kh_swizzle): the
+  // lane's row of M^T is column m0 + l16 of M over slab s.  In each 16-lane
+  // group a transposing read hands lane l16 element l16 % 4 of the 4-element
+  // pieces addressed by lanes l16 / 4 + {0, 4, 8, 12}; so lane 4e + q of group
+  // kg addresses row 32s + h + 4kg + e, elements m0 + 4q .. m0 + 4q + 3.
+  template <int P>
+  __device__ __forceinline__ static V ld_tr(const bf16* tile, int m0, int s, int l16, int kg) {
+    const int e = l16 >> 2, q = l16 & 3;
+    const bf16* lo = tile + (32 * s + 4 * kg + e) * P + 4 * ((m0 >> 2) + (q ^ kg));
+    const bf16* hi = lo + 16 * P;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lo));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(hi));
+    return __builtin_bit_cast(V, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   }
   // From accumulator tiles x (tile 2s) and y (tile 2s + 1).
   __device__ __forceinline__ static V acc2(const f32x4& x, const f32x4& y) {
@@ -441,6 +465,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
 #pragma unroll
     for (int s = 0; s < SK; ++s) fr[s] = F::ld(row, s, kg);
   };
+  // Same for the Kh tile (bf16: its units are XOR-permuted by row / 4).
+  auto ld_kh_rows = [&](FV (&fr)[SK], int blk) {
+    const E* row = &sm.kh[0][0] + opaque(l16 * Cfg::KHP) + 16 * blk * Cfg::KHP;
+    const int kgx = Cfg::TR ? kg ^ kh_swizzle(l16) : kg;
+#pragma unroll
+    for (int s = 0; s < SK; ++s) fr[s] = F::ld(row, s, kgx);
+  };
   auto mma_rows = [&](const FV (&a)[SK], const FV (&b)[SK]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -497,7 +528,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
     };
     float G[RPB][8];        // cumulative log2-decay of this thread's rows (block-local)
     float off[8];           // log2-decay of the chunk before this thread's block
-    EP2 khp[8][RPB / 2];    // Kh of this thread's rows per channel (token pairs), for Kh^T
+    EP2 khp[Cfg::TR ? 1 : 8][RPB / 2];  // fp32: Kh of this thread's rows per channel (token pairs), for Kh^T
     f32x4 Xdiag;            // X_ww = (I + A_ww)^-1 of this wave's block, accumulator form
     // Kh^T run of this thread: channels ch..ch+7 share one swizzle
     const int kht_col = ((((rb * RPB) >> 2) ^ kht_swizzle(ch)) << 2) | ((rb * RPB) & 3);
@@ -523,7 +554,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
     auto diag_job = [&](int I) {
       FV kt[SK], kh[SK], qt[SK];
       ld_rows(kt, sm.k, I);
-      ld_rows(kh, sm.kh, I);
+      ld_kh_rows(kh, I);
       ld_rows(qt, sm.q, I);
       f32x4 N = mma_rows(kt, kh), Nt = mma_rows(kh, kt);
       f32x4 Pt = mma_rows(kh, qt);
@@ -641,13 +672,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
             qo[c] = elem(rq[j], c) * e[c];
             ko[c] = kx * e[c];
             ho[c] = kx * n[c];
-            khp[c][j >> 1][j & 1] = from_f32<E>(ho[c]);
+            if constexpr (!Cfg::TR) khp[c][j >> 1][j & 1] = from_f32<E>(ho[c]);
           }
 #pragma unroll
           for (int c = 0; c < 8; c += 4) {
             store4<E>(&sm.q[r][ch + c], f32x4{qo[c], qo[c + 1], qo[c + 2], qo[c + 3]});
             store4<E>(&sm.k[r][ch + c], f32x4{ko[c], ko[c + 1], ko[c + 2], ko[c + 3]});
-            store4<E>(&sm.kh[r][ch + c], f32x4{ho[c], ho[c + 1], ho[c + 2], ho[c + 3]});
+            const int khc = Cfg::TR ? 4 * (((ch + c) >> 2) ^ kh_swizzle(r)) : ch + c;
+            store4<E>(&sm.kh[r][khc], f32x4{ho[c], ho[c + 1], ho[c + 2], ho[c + 3]});
           }
         }
         // the chunk's decay e^{G_C}: the last row of the chunk (its buffer
@@ -667,42 +699,42 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
           FV kh0[SK];
           if constexpr (NPW == 8) {
             if constexpr (W == 4) {
-              ld_rows(kh0, sm.kh, 0);
+              ld_kh_rows(kh0, 0);
               a_tile(1, 0, kh0);
               p_tile(1, 0, kh0);
               a_tile(3, 0, kh0);
             } else if constexpr (W == 5) {
-              ld_rows(kh0, sm.kh, 0);
+              ld_kh_rows(kh0, 0);
               p_tile(3, 0, kh0);
               a_tile(2, 0, kh0);
               p_tile(2, 0, kh0);
             } else if constexpr (W == 6) {
-              ld_rows(kh0, sm.kh, 1);
+              ld_kh_rows(kh0, 1);
               a_tile(2, 1, kh0);
               p_tile(2, 1, kh0);
               a_tile(3, 1, kh0);
             } else if constexpr (W == 7) {
-              ld_rows(kh0, sm.kh, 1);
+              ld_kh_rows(kh0, 1);
               p_tile(3, 1, kh0);
-              ld_rows(kh0, sm.kh, 2);
+              ld_kh_rows(kh0, 2);
               a_tile(3, 2, kh0);
               p_tile(3, 2, kh0);
             }
           } else {  // four producers: the A blocks now, the P blocks with the solve
             if constexpr (W == 0) {
-              ld_rows(kh0, sm.kh, 0);
+              ld_kh_rows(kh0, 0);
               a_tile(1, 0, kh0);
               a_tile(2, 0, kh0);
             } else if constexpr (W == 1) {
-              ld_rows(kh0, sm.kh, 1);
+              ld_kh_rows(kh0, 1);
               a_tile(2, 1, kh0);
-              ld_rows(kh0, sm.kh, 0);
+              ld_kh_rows(kh0, 0);
               a_tile(3, 0, kh0);
             } else if constexpr (W == 2) {
-              ld_rows(kh0, sm.kh, 1);
+              ld_kh_rows(kh0, 1);
               a_tile(3, 1, kh0);
             } else if constexpr (W == 3) {
-              ld_rows(kh0, sm.kh, 2);
+              ld_kh_rows(kh0, 2);
               a_tile(3, 2, kh0);
             }
           }
@@ -718,14 +750,16 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
             FV khj[SK];
 #pragma unroll
             for (int J = 0; J < W; ++J) {
-              ld_rows(khj, sm.kh, J);
+              ld_kh_rows(khj, J);
               p_tile(W, J, khj);
             }
           }
         });
-        // transposed Kh, read by the state pass next
+        // fp32: transposed Kh, read by the state pass next
+        if constexpr (!Cfg::TR) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) store_pairs<E, RPB / 2>(&sm.kht[ch + c][kht_col], khp[c]);
+          for (int c = 0; c < 8; ++c) store_pairs<E, RPB / 2>(&sm.kht[ch + c][kht_col], khp[c]);
+        }
       }
     }
     return;
@@ -816,11 +850,15 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_kernel(PrefillArgs args) {
       // ---- state: S <- Diag(e^{G_C}) (S + Kh^T U) ----
 #pragma unroll
       for (int mt = 0; mt < KT; ++mt) {
-        const E* krow = &sm.kht[16 * mt + l16][0];
+        const E* krow = &sm.kht[Cfg::TR ? 0 : 16 * mt + l16][0];
         const int sw = kht_swizzle(16 * mt);
 #pragma unroll
         for (int s = 0; s < SC; ++s) {
-          const FV a = F::ld_sw(krow, s, kg, sw);
+          FV a;
+          if constexpr (Cfg::TR)
+            a = F::template ld_tr<Cfg::KHP>(&sm.kh[0][0], 16 * mt, s, l16, kg);
+          else
+            a = F::ld_sw(krow, s, kg, sw);
 #pragma unroll
           for (int j = 0; j < TPW; ++j) S[j][mt] = F::mma(a, UF[j][s], S[j][mt]);
         }
