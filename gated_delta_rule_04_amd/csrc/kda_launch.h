@@ -26,6 +26,7 @@ hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* 
                          const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream);
 hipError_t launch_prefill(bool bf16_io, int Dk, int Dv, int g_group, int VS, const PrefillArgs& a,
                           hipStream_t stream);
+hipError_t launch_prefill_pipe(int Dk, int Dv, int g_group, int VS, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_varlen_order(const int* cu, int N, int T, int* order, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 int prefill_slice_width(bool bf16_io, int Dk, int Dv, long long units, int num_cus);

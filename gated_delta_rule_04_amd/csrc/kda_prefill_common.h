@@ -1,0 +1,335 @@
+// Device helpers shared by the KDA prefill kernels (gfx950 / CDNA4, wave64):
+// MFMA operand fragments in the accumulator-matching k order, buffer-resource
+// loads and stores, compile-time wavefront dispatch and the launch geometry.
+#pragma once
+
+#include "kda_common.h"
+
+namespace kda {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// traffic, not for its global loads/stores, so prefetched global loads stay
+// in flight across it (the compiler waits for them at their first use).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Compile-time wavefront roles: fn(IC<w>{}) for the uniform index w < N, so
+// each wavefront's share of a stage is specialised (scalar branches only).
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+template <int N, class Fn>
+__device__ __forceinline__ void static_switch(int w, Fn&& fn) {
+  if constexpr (N > 0) {
+    if (w == N - 1)
+      fn(IC<N - 1>{});
+    else
+      static_switch<N - 1>(w, fn);
+  }
+}
+
+// A lane offset the compiler must recompute where it is used: keeps the LDS
+// addresses of the per-wavefront jobs (compile-time block offsets on top)
+// from being hoisted out of the chunk loop, where the variants' hoisted
+// addresses together would exhaust the registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Four consecutive values to LDS: one 8-byte write (bf16) or two (fp32; fp32
+// operand rows are 8-byte aligned: their pitches are skewed by 8 bytes).
+template <typename E>
+__device__ __forceinline__ void store4(E* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, const f32x4& v) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x2*>(p) = f32x2{v[0], v[1]};
+  *reinterpret_cast<f32x2*>(p + 2) = f32x2{v[2], v[3]};
+}
+
+template <typename T>
+struct Pair;
+template <>
+struct Pair<bf16> {
+  typedef bf16x2 type;
+};
+template <>
+struct Pair<float> {
+  typedef f32x2 type;
+};
+
+// Store NP element pairs as one contiguous run of 2*NP elements.
+template <typename E, int NP>
+__device__ __forceinline__ void store_pairs(E* p, const typename Pair<E>::type (&x)[NP]) {
+  if constexpr (sizeof(E) == 2 && NP % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < NP; i += 2)
+      *reinterpret_cast<bf16x4*>(p + 2 * i) = __builtin_shufflevector(x[i], x[i + 1], 0, 1, 2, 3);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) *reinterpret_cast<typename Pair<E>::type*>(p + 2 * i) = x[i];
+  }
+}
+
+// Raw buffer access: a per-chunk descriptor bounds every access, so loads of
+// rows past the end of a sequence return zero (the inert zero padding of a
+// partial chunk) and stores past the end are dropped -- no clamping, masking
+// or branches.  Offsets are 32-bit byte offsets within the chunk.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename P>
+__device__ __forceinline__ P bload(rsrc_t r, int off) {
+  if constexpr (sizeof(P) == 2)
+    return __builtin_bit_cast(P, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+  else if constexpr (sizeof(P) == 4)
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  else if constexpr (sizeof(P) == 8)
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// Eight consecutive elements, loaded with 16-byte accesses.
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  typedef bf16x8 type;
+  __device__ __forceinline__ static type load(rsrc_t r, int off) { return bload<bf16x8>(r, off); }
+};
+template <>
+struct Vec8<float> {
+  typedef f32x8 type;
+  __device__ __forceinline__ static type load(rsrc_t r, int off) {
+    const f32x4 a = bload<f32x4>(r, off), b = bload<f32x4>(r, off + 16);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+template <typename V>
+__device__ __forceinline__ float elem(const V& v, int i) {
+  return (float)v[i];
+}
+// Four consecutive elements of a row (one 8- or 16-byte access).
+template <typename T>
+struct Row4;
+template <>
+struct Row4<bf16> {
+  typedef bf16x4 type;
+};
+template <>
+struct Row4<float> {
+  typedef f32x4 type;
+};
+__device__ __forceinline__ void bstore4(const f32x4& v, rsrc_t r, int off, bf16) {
+  const bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(const f32x4& v, rsrc_t r, int off, float) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Launch geometry and LDS layout.
+// ---------------------------------------------------------------------------
+template <int DK_, int DV_, int VS_, typename T_, int GG_>
+struct PrefillCfg {
+  typedef T_ T;  // input/output element type
+  typedef T_ E;  // MFMA operand type (bf16 path: bf16; f32 path: float)
+  static constexpr int DK = DK_, DV = DV_, VS = VS_, GG = GG_;
+  static constexpr int C = 64;                   // chunk length
+  static constexpr int NPW = DK / 16;            // producer wavefronts (8 or 4)
+  static constexpr int NA = 64 * NPW;            // producer threads
+  static constexpr int RT = VS / 16;             // value-column tiles per slice
+  static constexpr int TPW = RT > 4 ? RT / 4 : 1;  // value tiles per state wavefront
+  static constexpr int NBW = RT / TPW;           // state wavefronts
+  static constexpr int NT = NA + 64 * NBW;       // threads per workgroup
+  static constexpr int PADE = 8 / sizeof(E);     // 8-byte row skew: pitch = 2 (mod 32) dwords
+  static constexpr int KP = DK + PADE;           // pitch of [*][DK] operand tiles
+  // bf16: Kh^T fragments come from the token-major Kh tile through transposing
+  // LDS reads (gfx950 ds_read_b64_tr_b16); Kh rows are then 16 elements longer
+  // and XOR-permuted, and no separate Kh^T tile exists.  fp32 keeps Kh^T.
+  static constexpr bool TR = sizeof(E) == 2;
+  static constexpr int KHP = TR ? DK + 16 : KP;  // pitch of the Kh tile
+  static constexpr int CP = C + PADE;            // pitch of [*][C] operand tiles
+  static constexpr int AP = C + 4;               // pitch of the fp32 A tile
+  static constexpr int CGN = DK / 8;             // gating: groups of 8 key channels
+  static constexpr int NRB = NA / CGN;           // gating: row blocks
+  static constexpr int RPB = C / NRB;            // gating: rows per block
+  static constexpr int RBW = 64 / CGN;           // gating: row blocks per wavefront
+  static constexpr int KT = DK / 16;             // key-channel tiles
+  static constexpr int NS = DV / VS;             // slices per head
+  static_assert(DK == 64 || DK == 128, "DK");
+  static_assert(VS % 16 == 0 && DV % VS == 0 && RT % TPW == 0, "VS");
+  static_assert(NRB * CGN == NA && RPB * NRB == C && RBW * CGN == 64, "gating map");
+  static_assert(RPB == 2 || RPB == 4, "a thread's Kh^T run stays inside one 4-token group");
+  static_assert(NPW == 4 || NPW == 8, "producer wavefronts");
+};
+
+// Kh^T is stored with its 4-token groups XOR-permuted per 16 key channels,
+// which spreads the producer's column writes over all banks while the state
+// wavefronts' row reads (one 16-row block per instruction) stay conflict-free.
+__device__ __forceinline__ int kht_swizzle(int row) { return (5 * (row >> 4)) & 15; }
+// bf16 Kh rows: 4-element unit u of token row r is stored at unit u ^ ((r / 4) % 4).
+// Row reads (16 consecutive rows), transposing reads (4 rows x 4 units per
+// 16 lanes) and the producer's row writes then spread over all banks.
+__device__ __forceinline__ int kh_swizzle(int row) { return (row >> 2) & 3; }
+
+
+// MFMA fragments with a k order that matches the accumulator layout, so that
+// accumulators (S, R, U) feed the next product straight from registers.
+// bf16 (16x16x32): slab s covers k = 32s .. 32s+31 and lane group kg holds
+// k = 32s + 4kg + {0..3} and 32s + 16 + 4kg + {0..3}, i.e. rows 4kg..4kg+3 of
+// accumulator tiles 2s and 2s+1.  fp32 (16x16x4): slab s covers
+// k = 16(s/4) + 4kg + (s%4), i.e. element s%4 of accumulator tile s/4.
+// A and B operands share this layout: lane l16 supplies row l16 of A, or
+// column l16 of B, over the slab's k.  So the accumulator form of a matrix
+// M (lane l: M[4(l/16) + i][l % 16]) is both M's B operand and M^T's A
+// operand, and a tile loaded from row-major rows serves as an A operand of
+// itself or a B operand of its transpose.
+template <typename E>
+struct Frag;
+
+template <>
+struct Frag<bf16> {
+  typedef bf16x8 V;
+  static constexpr int SLAB = 32;
+  // From a row-major LDS row (the lane's row).
+  __device__ __forceinline__ static V ld(const bf16* row, int s, int kg) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * s + 4 * kg);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * s + 16 + 4 * kg);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // Same, from a row whose 4-element groups are XOR-permuted by sw.
+  __device__ __forceinline__ static V ld_sw(const bf16* row, int s, int kg, int sw) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 4 * ((8 * s + kg) ^ sw));
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 4 * ((8 * s + 4 + kg) ^ sw));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // Fragment of M^T from a token-major tile M (swizzled by kh_swizzle): the
+  // lane's row of M^T is column m0 + l16 of M over slab s.  In each 16-lane
+  // group a transposing read hands lane l16 element l16 % 4 of the 4-element
+  // pieces addressed by lanes l16 / 4 + {0, 4, 8, 12}; so lane 4e + q of group
+  // kg addresses row 32s + h + 4kg + e, elements m0 + 4q .. m0 + 4q + 3.
+  template <int P>
+  __device__ __forceinline__ static V ld_tr(const bf16* tile, int m0, int s, int l16, int kg) {
+    const int e = l16 >> 2, q = l16 & 3;
+    const bf16* lo = tile + (32 * s + 4 * kg + e) * P + 4 * ((m0 >> 2) + (q ^ kg));
+    const bf16* hi = lo + 16 * P;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lo));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(hi));
+    return __builtin_bit_cast(V, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  // From accumulator tiles x (tile 2s) and y (tile 2s + 1).
+  __device__ __forceinline__ static V acc2(const f32x4& x, const f32x4& y) {
+    return V{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3], (bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+  }
+  __device__ __forceinline__ static f32x4 mma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Frag<float> {
+  typedef float V;
+  static constexpr int SLAB = 4;
+  __device__ __forceinline__ static V ld(const float* row, int s, int kg) {
+    return row[16 * (s >> 2) + 4 * kg + (s & 3)];
+  }
+  __device__ __forceinline__ static V ld_sw(const float* row, int s, int kg, int sw) {
+    return row[4 * ((4 * (s >> 2) + kg) ^ sw) + (s & 3)];
+  }
+  __device__ __forceinline__ static f32x4 mma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// 16x16 products with both operands in accumulator form: prod(At, B) = A * B,
+// where At holds A^T and B holds B.  prod(M, I) = M^T moves a tile to its
+// transpose exactly (for bf16, exactly after the operand rounding).  bf16: one
+// 16x16x16 MFMA on bf16-rounded operands (the transform is stored in bf16
+// afterwards; the extra rounding raises its error from 1.6e-4 to 2.2e-4
+// relative); fp32: four 16x16x4 steps.
+template <typename E>
+struct Reg16;
+template <>
+struct Reg16<bf16> {
+  __device__ __forceinline__ static s16x4 cvt(const f32x4& x) {
+    return __builtin_bit_cast(s16x4, bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]});
+  }
+  __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt(At), cvt(B), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+  // c + the 16x16 tile given as rows (lane l16: elements 4kg..4kg+3 of row
+  // l16), exact: a product with the identity, in the 16x16x32 shape of the
+  // chains it joins (the rows fill k = 0..15, the upper half of k is zero).
+  // An accumulator produced by one MFMA shape is never fed to another shape
+  // as its C operand.
+  __device__ __forceinline__ static f32x4 rows(const bf16x4& r, const f32x4& ident, const f32x4& c) {
+    const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    const bf16x4 i4 = {(bf16)ident[0], (bf16)ident[1], (bf16)ident[2], (bf16)ident[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(r, z, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                   __builtin_shufflevector(i4, z, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
+  }
+};
+template <>
+struct Reg16<float> {
+  __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(At[i], B[i], c, 0, 0, 0);
+    return c;
+  }
+  __device__ __forceinline__ static f32x4 rows(const f32x4& r, const f32x4& ident, const f32x4& c) {
+    f32x4 d = c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_mfma_f32_16x16x4f32(r[i], ident[i], d, 0, 0, 0);
+    return d;
+  }
+};
+
+// (I + N)^-1 for a strictly lower 16x16 N (nilpotent, N^16 = 0), as the
+// product (I + N^8)(I + N^4)(I + N^2)(I - N) = sum_{k<16} (-N)^k.
+// N and Nt are N and N^T in accumulator form; returns X in accumulator form.
+template <typename E>
+__device__ __forceinline__ f32x4 unit_lower_inverse16(const f32x4& N, const f32x4& Nt, const f32x4& I4) {
+  typedef Reg16<E> R;
+  const f32x4 N2 = R::prod(Nt, N), N2t = R::prod(N, Nt);
+  const f32x4 N4 = R::prod(N2t, N2), N4t = R::prod(N2, N2t);
+  const f32x4 N8t = R::prod(N4, N4t);
+  const f32x4 Z1 = R::prod(I4 + N2t, I4 - N);
+  const f32x4 Z2 = R::prod(I4 + N4t, Z1);
+  return R::prod(I4 + N8t, Z2);
+}
+
+// Operand fragment of slab s from accumulator tiles acc[0..n) along k (and
+// the same for the negated tiles).
+template <int N>
+__device__ __forceinline__ bf16x8 acc_frag(const f32x4 (&acc)[N], int s, bf16) {
+  return Frag<bf16>::acc2(acc[2 * s], acc[2 * s + 1]);
+}
+template <int N>
+__device__ __forceinline__ float acc_frag(const f32x4 (&acc)[N], int s, float) {
+  return acc[s >> 2][s & 3];
+}
+template <int N>
+__device__ __forceinline__ bf16x8 acc_frag_neg(const f32x4 (&acc)[N], int s, bf16) {
+  return Frag<bf16>::acc2(-acc[2 * s], -acc[2 * s + 1]);
+}
+template <int N>
+__device__ __forceinline__ float acc_frag_neg(const f32x4 (&acc)[N], int s, float) {
+  return -acc[s >> 2][s & 3];
+}
+
+
+}  // namespace kda
