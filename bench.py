@@ -27,8 +27,10 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA chunked-prefill tokens/s + decode tokens/s; % MFMA peak, % HBM GB/s"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc", "kda_prefill.hip")
-DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc", "kda_decode.hip")
+CSRC = os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc")
+# Sources of each measured kernel (the bf16 prefill kernel is the pipelined one).
+PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("kda_prefill_common.h", "kda_prefill.hip", "kda_prefill_pipe.hip")]
+DECODE_SRCS = [os.path.join(CSRC, "kda_decode.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 
 
@@ -52,9 +54,13 @@ def alg_decode(N, H, dk, dv, g_group, elem=2):
     return N * H * per
 
 
-def sha256_file(p):
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sha256_files(paths):
+    """sha256 of the concatenated contents of paths (in order)."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic(kernel):
@@ -62,8 +68,7 @@ def read_traffic(kernel):
     valid only while the kernel source is unchanged since the counters."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    src = PREFILL_SRC if kernel == "prefill" else DECODE_SRC
-    want = sha256_file(src)
+    want = sha256_files(PREFILL_SRCS if kernel == "prefill" else DECODE_SRCS)
     rec = {}
     with open(TRAFFIC_FILE) as f:
         for line in f:
@@ -234,7 +239,7 @@ def main():
             "io_dtype": "bf16", "state_dtype": "fp32", "accumulate": "fp32",
         },
         "roofline": {
-            "kernel": "chunk_fwd_kernel (prefill)",
+            "kernel": "chunk_fwd_pipe_kernel (prefill, bf16)",
             "bound": "hbm",
             "achieved": pre_gbs,
             "peak": PEAK_HBM_GBS,
