@@ -54,6 +54,13 @@ def alg_decode(N, H, dk, dv, g_group, elem=2):
     return N * H * per
 
 
+def alg_decode_pool(N, H, dk, dv, g_group, state_elem=2, elem=2):
+    """Bytes of one serving-pool decode step with a state of state_elem bytes
+    per value (bf16: 2), read and written, plus the inputs and o."""
+    per = 2 * state_elem * dk * dv + elem * (2 * dk + dv + dk // g_group + 1 + dv)
+    return N * H * per
+
+
 def sha256_files(paths):
     """sha256 of the concatenated contents of paths (in order)."""
     h = hashlib.sha256()
@@ -276,6 +283,34 @@ def main():
         },
         "event_ms_per_step": mean(step_ms),
         "input_gen_s": t_gen,
+    }
+    # Serving form (outside the timed step above): the same decode inputs over a
+    # bf16 state pool, sequences in shuffled slots of a larger pool.
+    ns = N + N // 4
+    slots = torch.randperm(ns, generator=torch.Generator().manual_seed(17))[:N].to(torch.int32).to(dev)
+    pool = torch.zeros((ns, H, dk, dv), dtype=torch.bfloat16, device=dev)
+    pool[slots.long()] = state.to(torch.bfloat16)
+    for i in range(args.warmup):
+        s = D[i % len(D)]
+        kda.recurrent_step_pool(s["q"], s["k"], s["v"], s["g"], s["beta"], pool, slots, out=od)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        s = D[i % len(D)]
+        pev[i][0].record()
+        kda.recurrent_step_pool(s["q"], s["k"], s["v"], s["g"], s["beta"], pool, slots, out=od)
+        pev[i][1].record()
+    torch.cuda.synchronize()
+    pool_ms = [e[0].elapsed_time(e[1]) for e in pev]
+    pool_avg = mean(pool_ms)
+    pool_bytes = alg_decode_pool(N, H, dk, dv, g_group)
+    line["decode_pool_bf16"] = {
+        "kernel": "decode_step_kernel (bf16 state pool, slot indirection)",
+        "config": {"N": N, "H": H, "dk": dk, "dv": dv, "num_slots": ns, "state": "bf16"},
+        "tokens_per_s": N / (pool_avg * 1e-3),
+        "ms_per_step": pool_avg,
+        "ms_min": min(pool_ms),
+        "alg_bytes_per_launch": pool_bytes,
+        "hbm_frac_alg": pool_bytes / (pool_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, dec)

@@ -22,16 +22,39 @@
 // through cross-lane shuffles and an LDS exchange between the 8 wavefronts.
 // An in-place read-modify-write stream of this shape runs at about 67% of the
 // 8 TB/s peak on MI355X (measured: read-only about 74%, write-only about 70%).
+//
+// Serving form: the states live in a pool and sequence n uses slot slots[n]
+// (the state pool that bounds concurrency in the K3-Tiny-L13 card's serving
+// notes, with the state dtype as a knob).  A slot outside the pool marks an
+// inactive sequence: its output row is zero and no state is touched.  A bf16
+// pool is widened to fp32 for the step and rounded to nearest even after it.
 
 #include "kda_common.h"
 #include "kda_launch.h"
 
 namespace kda {
 
-template <int DK, int DV, typename T, int GG>
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+
+// Four consecutive state values (fp32: one 16-byte access; bf16: one 8-byte
+// access), streamed with non-temporal loads.
+__device__ __forceinline__ f32x4 load_state4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ f32x4 load_state4(const bf16* p) {
+  const bf16x4 b = __builtin_bit_cast(bf16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p)));
+  return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+__device__ __forceinline__ void store_state4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ __forceinline__ void store_state4(bf16* p, const f32x4& x) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};  // RNE
+}
+
+template <int DK, int DV, typename T, int GG, typename SE>
 __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                           const T* __restrict__ v, const T* __restrict__ g,
-                                                          const T* __restrict__ beta, float* __restrict__ state,
+                                                          const T* __restrict__ beta, SE* __restrict__ state,
+                                                          const int* __restrict__ slots, int num_slots, int H,
                                                           T* __restrict__ o) {
   constexpr int NT = 512;
   constexpr int CG = DV / 4;         // column groups of 4 floats
@@ -52,13 +75,24 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
   const int lane = tid % kWave;
   const int wave = tid / kWave;
 
+  // The state of this (sequence, head): pool slot slots[n], or n itself.
+  size_t su = u;
+  if (slots) {
+    const int n = (int)(u / H), h = (int)(u % H);
+    const int slot = slots[n];
+    if (slot < 0 || slot >= num_slots) {  // inactive sequence: zero output, no state access
+      if (tid < DV) o[u * DV + tid] = from_f32<T>(0.f);
+      return;
+    }
+    su = (size_t)slot * H + h;
+  }
   // Issue the state loads first: they are the whole cost of the step.
-  float* S = state + u * (size_t)DK * DV;
+  SE* S = state + su * (size_t)DK * DV;
   f32x4 s[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + RG * m;
-    s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)r * DV + 4 * cg));
+    s[m] = load_state4(S + (size_t)r * DV + 4 * cg);
   }
 
   // Stage q, k and alpha = exp(g) for the key channels.
@@ -127,35 +161,60 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + RG * m;
-    *reinterpret_cast<f32x4*>(S + (size_t)r * DV + 4 * cg) = s[m] + s_k[r] * uu;
+    store_state4(S + (size_t)r * DV + 4 * cg, s[m] + s_k[r] * uu);
   }
 }
 
-template <int DK, int DV, typename T, int GG>
+template <int DK, int DV, typename T, int GG, typename SE>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                                  float* state, void* o, int NH, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, GG>), dim3(NH), dim3(512), 0, stream, (const T*)q, (const T*)k,
-                     (const T*)v, (const T*)g, (const T*)beta, state, (T*)o);
+                                  void* state, const int* slots, int num_slots, int H, void* o, int NH,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, GG, SE>), dim3(NH), dim3(512), 0, stream, (const T*)q,
+                     (const T*)k, (const T*)v, (const T*)g, (const T*)beta, (SE*)state, slots, num_slots, H, (T*)o);
   return hipGetLastError();
 }
 
-template <typename T, int GG>
+template <typename T, int GG, typename SE>
 static hipError_t launch_decode_g(int Dk, int Dv, const void* q, const void* k, const void* v, const void* g,
-                                  const void* beta, float* state, void* o, int NH, hipStream_t stream) {
-  if (Dk == 64 && Dv == 64) return launch_decode_t<64, 64, T, GG>(q, k, v, g, beta, state, o, NH, stream);
-  if (Dk == 64 && Dv == 128) return launch_decode_t<64, 128, T, GG>(q, k, v, g, beta, state, o, NH, stream);
-  if (Dk == 128 && Dv == 64) return launch_decode_t<128, 64, T, GG>(q, k, v, g, beta, state, o, NH, stream);
-  return launch_decode_t<128, 128, T, GG>(q, k, v, g, beta, state, o, NH, stream);
+                                  const void* beta, void* state, const int* slots, int num_slots, int H, void* o,
+                                  int NH, hipStream_t stream) {
+#define KDA_DEC(DK_, DV_)      \
+  if (Dk == DK_ && Dv == DV_) \
+    return launch_decode_t<DK_, DV_, T, GG, SE>(q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream);
+  KDA_DEC(64, 64)
+  KDA_DEC(64, 128)
+  KDA_DEC(128, 64)
+  KDA_DEC(128, 128)
+#undef KDA_DEC
+  return hipErrorInvalidValue;
+}
+
+template <typename SE>
+static hipError_t launch_decode_s(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k,
+                                  const void* v, const void* g, const void* beta, void* state, const int* slots,
+                                  int num_slots, int H, void* o, int NH, hipStream_t stream) {
+  if (bf16_io)
+    return g_group == 1
+               ? launch_decode_g<bf16, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream)
+               : launch_decode_g<bf16, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream);
+  return g_group == 1
+             ? launch_decode_g<float, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream)
+             : launch_decode_g<float, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream);
 }
 
 hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream) {
-  if (bf16_io) {
-    return g_group == 1 ? launch_decode_g<bf16, 1>(Dk, Dv, q, k, v, g, beta, state, o, NH, stream)
-                        : launch_decode_g<bf16, 64>(Dk, Dv, q, k, v, g, beta, state, o, NH, stream);
-  }
-  return g_group == 1 ? launch_decode_g<float, 1>(Dk, Dv, q, k, v, g, beta, state, o, NH, stream)
-                      : launch_decode_g<float, 64>(Dk, Dv, q, k, v, g, beta, state, o, NH, stream);
+  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, state, nullptr, 0, 1, o, NH, stream);
+}
+
+hipError_t launch_decode_pool(bool bf16_io, bool bf16_state, int Dk, int Dv, int g_group, const void* q,
+                              const void* k, const void* v, const void* g, const void* beta, void* pool,
+                              const int* slots, int num_slots, int H, void* o, int NH, hipStream_t stream) {
+  if (bf16_state)
+    return launch_decode_s<bf16>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, NH,
+                                 stream);
+  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, NH,
+                                stream);
 }
 
 }  // namespace kda

@@ -24,6 +24,9 @@ struct PrefillArgs {
 
 hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream);
+hipError_t launch_decode_pool(bool bf16_io, bool bf16_state, int Dk, int Dv, int g_group, const void* q,
+                              const void* k, const void* v, const void* g, const void* beta, void* pool,
+                              const int* slots, int num_slots, int H, void* o, int NH, hipStream_t stream);
 hipError_t launch_prefill(bool bf16_io, int Dk, int Dv, int g_group, int VS, const PrefillArgs& a,
                           hipStream_t stream);
 hipError_t launch_prefill_pipe(int Dk, int Dv, int g_group, int VS, const PrefillArgs& a, hipStream_t stream);

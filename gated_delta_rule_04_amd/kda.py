@@ -27,8 +27,8 @@ _STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
-EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step", "kda_status_str",
-            "kda_abi_version"]
+EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_step_pool",
+            "kda_status_str", "kda_abi_version"]
 
 _lib = None
 
@@ -60,6 +60,8 @@ def lib():
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
     L.kda_recurrent_step.restype = i
     L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    L.kda_recurrent_step_pool.restype = i
+    L.kda_recurrent_step_pool.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, vp]
     _lib = L
     return L
 
@@ -149,4 +151,30 @@ def recurrent_step(q, k, v, g, beta, state, out=None):
                                   Dv, g_group, dt, _stream())
     if st != 0:
         raise KdaError(st, "kda_recurrent_step")
+    return o
+
+
+def recurrent_step_pool(q, k, v, g, beta, state_pool, slots, out=None):
+    """One KDA decode step over a state pool: sequence n updates
+    state_pool[slots[n]] in place ([num_slots, H, Dk, Dv], float32 or
+    bfloat16).  A slot outside [0, num_slots) marks the sequence inactive:
+    its output row is zero and no state is touched."""
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
+        raise ValueError("g's last dim must divide Dk")
+    g_group = Dk // g.shape[-1]
+    dt = _dt(q)
+    sdt = _dt(state_pool)
+    if slots.dtype != torch.int32 or slots.shape != (N,):
+        raise TypeError("slots must be int32 of shape [N]")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, Dk, Dv):
+        raise ValueError("state_pool must be [num_slots, H, Dk, Dv]")
+    _check_dev(q, k, v, g, beta, state_pool, slots)
+    o = out if out is not None else torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
+    st = lib().kda_recurrent_step_pool(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                       _ptr(slots), state_pool.shape[0], _ptr(o), N, H, Dk, Dv, g_group, dt, sdt,
+                                       _stream())
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_step_pool")
     return o

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -108,6 +108,30 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
                               float* state, void* o, int N, int H, int Dk, int Dv, int g_group, kda_dtype dt,
                               void* stream);
+
+/* One recurrent decode step over a serving state pool.  The K3-Tiny-L13 card
+ * (serving notes under "Measured on 1x B300") reports decode concurrency
+ * capped by the pool of per-sequence KDA states, with the state dtype as a
+ * serving knob; this entry point is that pool's step.  Sequence n reads and
+ * writes pool slot slots[n]; the step itself is the one of kda_recurrent_step.
+ *
+ *   q, k, v, g, beta, o   as for kda_recurrent_step ([N, H, ...], dt);
+ *   state_pool  [num_slots, H, Dk, Dv] of state_dt, updated in place for the
+ *          slots named by active sequences; every other slot is untouched.
+ *   slots  device int32 [N]: the pool slot of each sequence.  A value outside
+ *          [0, num_slots) marks the sequence inactive: its o row is written
+ *          as zeros and no state is read or written.  Two active sequences
+ *          must not name the same slot (their updates would race).
+ *   num_slots  pool size (>= 0; state_pool may be NULL when it is 0).
+ *   state_dt   KDA_F32 or KDA_BF16.  A bf16 state is widened to fp32 for
+ *          the step and rounded to nearest even when written back.
+ * N = 0 is a no-op.  Errors: KDA_ERR_NULL (q, k, v, g, beta, slots or o NULL,
+ * or state_pool NULL with num_slots > 0), KDA_ERR_SHAPE, KDA_ERR_DTYPE (dt
+ * or state_dt), KDA_ERR_UNSUPPORTED, KDA_ERR_HIP as elsewhere.
+ */
+kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                   void* state_pool, const int* slots, int num_slots, void* o, int N, int H,
+                                   int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* kda_status_str(kda_status s);

@@ -16,9 +16,8 @@ Sources (the page text the method is defined on):
   bullet: the state update is one gradient-descent step on the squared error
   of the state's read-out against v, with per-channel gated decay; a chunked
   parallel form for training and a fixed-size recurrence for decoding.
-* The matrix form of that bullet (stated in the task description of this
-  project): S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
-  + beta_t k_t v_t^T,  o_t = S_t^T q_t.
+* The matrix form of that bullet: S_t = (I - beta_t k_t k_t^T) Diag(alpha_t)
+  S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t.
 * Mini-K3-1H-mamba2 README excerpt (packed-document paragraph): packed
   documents are causally isolated and recurrent state flow is reset at every
   document boundary.
@@ -156,3 +155,48 @@ def kda_decode_step(state, q, k, v, g, beta, g_group=1):
     dk = q.shape[-1]
     g = expand_decay(g, dk, g_group)
     return kda_step(_f64(state), q, k, v, g, beta)
+
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps float32's 8-bit exponent and 8 significant bits (7 stored).
+    For a normal value x = m * 2^e with 0.5 <= |m| < 1 (frexp), the nearest
+    bfloat16 is round(m * 2^8) * 2^(e - 8) with ties to even, which is what
+    numpy's round does.  (Subnormal and overflowing values do not occur in
+    the states this is applied to; zeros stay zeros.)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+def kda_decode_step_pool(pool, slots, q, k, v, g, beta, g_group=1, state_bf16=False):
+    """One decode step over a pool of states (serving form).
+
+    pool: [num_slots, H, dk, dv]; slots: [N] ints; q, k: [N, H, dk];
+    v: [N, H, dv]; g: [N, H, dk // g_group]; beta: [N, H].
+    Sequence n steps the state in pool slot slots[n] (the K3-Tiny-L13 card's
+    serving notes: decode concurrency is bounded by a pool of per-sequence
+    KDA states whose dtype is a serving knob).  A slot outside [0, num_slots)
+    marks the sequence inactive: its output row is zero and no state changes.
+    With state_bf16 the pool holds bfloat16 values: the step runs on them
+    exactly and the new state is rounded to the nearest bfloat16 (ties to
+    even); the output is the exact step's output.
+    Returns (new_pool, o [N, H, dv]).
+    """
+    pool = _f64(pool).copy()
+    slots = np.asarray(slots)
+    N, H = np.asarray(q).shape[:2]
+    dv = np.asarray(v).shape[-1]
+    o = np.zeros((N, H, dv))
+    for n in range(N):
+        s = int(slots[n])
+        if s < 0 or s >= pool.shape[0]:
+            continue
+        S_new, o_n = kda_decode_step(pool[s][None], np.asarray(q)[n:n + 1], np.asarray(k)[n:n + 1],
+                                     np.asarray(v)[n:n + 1], np.asarray(g)[n:n + 1], np.asarray(beta)[n:n + 1],
+                                     g_group)
+        pool[s] = round_bf16(S_new[0]) if state_bf16 else S_new[0]
+        o[n] = o_n[0]
+    return pool, o

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 1
+    assert L.kda_abi_version() == 2
     for s in range(7):
         assert L.kda_status_str(s).decode().startswith(("KDA_OK", "KDA_ERR"))
     assert L.kda_status_str(99)
@@ -87,3 +87,20 @@ def test_recurrent_step_validation():
     assert step(q=None) == NULL
     assert step(state=None) == NULL
     assert step(N=0, q=None, state=None) == OK
+
+
+def test_recurrent_step_pool_validation():
+    L = kda.lib()
+    step = lambda q=P, pool=P, slots=P, ns=4, N=1, H=1, Dk=64, Dv=64, gg=1, dt=1, sdt=1: L.kda_recurrent_step_pool(
+        q, P, P, P, P, pool, slots, ns, P, N, H, Dk, Dv, gg, dt, sdt, None)
+    assert step(dt=2) == DTYPE
+    assert step(sdt=5) == DTYPE
+    assert step(N=-1) == SHAPE
+    assert step(H=0) == SHAPE
+    assert step(ns=-1) == SHAPE
+    assert step(Dv=96) == UNSUPPORTED
+    assert step(gg=128) == UNSUPPORTED
+    assert step(q=None) == NULL
+    assert step(slots=None) == NULL
+    assert step(pool=None) == NULL                    # a pool is required when num_slots > 0
+    assert step(N=0, q=None, pool=None, slots=None) == OK

@@ -1,0 +1,100 @@
+"""Serving-pool decode step on the GPU (through the C-ABI) against the CPU
+oracle: slot indirection, inactive sequences, and a bfloat16 state pool."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.kda_oracle as orc
+from gated_delta_rule_04_amd import inputs, kda
+from tests._parity import assert_close, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(st):
+    return {n: st[n].cuda() for n in st}
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_pool_identity_slots_equal_plain_step(dk, dv):
+    r = inputs.make_decode(6, 3, dk, dv, steps=1, dtype="bf16", g_group=1, seed=300 + dk)
+    d = _dev(r["steps"][0])
+    a = r["state"].cuda()
+    b = r["state"].cuda()
+    o1 = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], a)
+    o2 = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], b,
+                                 torch.arange(6, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dk,dv,g_group", [(64, 128, 1), (128, 64, 64), (128, 128, 1)])
+def test_pool_permuted_and_inactive_slots(dk, dv, g_group):
+    N, H, ns = 7, 2, 9
+    r = inputs.make_decode(N, H, dk, dv, steps=1, dtype="bf16", g_group=g_group, seed=310 + dk + dv)
+    st = r["steps"][0]
+    d = _dev(st)
+    pool0 = torch.from_numpy(np.random.default_rng(11).standard_normal((ns, H, dk, dv)) * 0.02).float()
+    slots = np.array([5, -1, 0, 8, ns, 2, -7], dtype=np.int32)  # ns and negatives are inactive
+    pool = pool0.cuda()
+    o = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool,
+                                torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    ref_pool, ref_o = orc.kda_decode_step_pool(f64(pool0), slots, f64(st["q"]), f64(st["k"]), f64(st["v"]),
+                                               f64(st["g"]), f64(st["beta"]), g_group=g_group)
+    active = [n for n in range(N) if 0 <= slots[n] < ns]
+    assert_close("o active", o.cpu()[active], ref_o[active], torch.bfloat16)
+    inactive = [n for n in range(N) if n not in active]
+    assert torch.all(o.cpu()[inactive] == 0)
+    used = sorted(int(slots[n]) for n in active)
+    assert_close("pool used slots", pool.cpu()[used], ref_pool[used], torch.bfloat16)
+    untouched = [s for s in range(ns) if s not in used]
+    assert torch.equal(pool.cpu()[untouched], pool0[untouched])
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_pool_bf16_state_steps(dk, dv):
+    N, H, steps = 5, 3, 12
+    r = inputs.make_decode(N, H, dk, dv, steps=steps, dtype="bf16", g_group=1, seed=330 + dk + dv)
+    ns = N + 2
+    slots = np.array([3, 0, 6, 1, 4], dtype=np.int32)
+    pool0 = torch.from_numpy(orc.round_bf16(np.random.default_rng(12).standard_normal((ns, H, dk, dv)) * 0.02))
+    pool = pool0.to(torch.bfloat16).cuda()
+    ref_pool = f64(pool0)
+    sl = torch.from_numpy(slots).cuda()
+    for s, st in enumerate(r["steps"]):
+        d = _dev(st)
+        o = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, sl)
+        ref_pool, ref_o = orc.kda_decode_step_pool(ref_pool, slots, f64(st["q"]), f64(st["k"]), f64(st["v"]),
+                                                   f64(st["g"]), f64(st["beta"]), state_bf16=True)
+        torch.cuda.synchronize()
+        assert_close("o step %d" % s, o.cpu(), ref_o, torch.bfloat16)
+    assert_close("bf16 pool", pool.cpu()[slots], ref_pool[slots], torch.bfloat16)
+    untouched = [s for s in range(ns) if s not in slots]
+    assert torch.equal(pool.cpu()[untouched], pool0.to(torch.bfloat16)[untouched])
+
+
+def test_k3_pool_bf16_state_sampled():
+    """Full-size serving step: 256 sequences x 96 heads over a 300-slot bf16
+    pool in shuffled slots, 4 steps; oracle on sampled (sequence, head) pairs."""
+    r = inputs.workload_decode("k3_decode_bf16", steps=4)
+    N, H = r["state"].shape[:2]
+    ns = 300
+    perm = np.random.default_rng(13).permutation(ns)[:N].astype(np.int32)
+    pool_host = torch.zeros((ns, H) + tuple(r["state"].shape[2:]), dtype=torch.bfloat16)
+    pool_host[torch.from_numpy(perm).long()] = r["state"].to(torch.bfloat16)
+    pool = pool_host.cuda()
+    sl = torch.from_numpy(perm).cuda()
+    seqs, heads = np.array([0, 131, 255]), np.array([0, 47, 95])
+    S = f64(pool_host[torch.from_numpy(perm[seqs]).long()][:, heads])
+    for s, st in enumerate(r["steps"]):
+        d = _dev(st)
+        o = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, sl)
+        sub = {n: f64(st[n][seqs][:, heads]) for n in st}
+        S, o_ref = orc.kda_decode_step(S, sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"])
+        S = orc.round_bf16(S)
+        torch.cuda.synchronize()
+        assert_close("k3 pool o step %d" % s, o.cpu()[seqs][:, heads], o_ref, torch.bfloat16)
+    got = pool.cpu()[torch.from_numpy(perm[seqs]).long()][:, heads]
+    assert_close("k3 pool state", got, S, torch.bfloat16)

@@ -1,0 +1,65 @@
+"""Pins of the oracle's serving-pool decode step and its bfloat16 rounding
+(CPU only).  The K3-Tiny-L13 card's serving notes bound decode concurrency by
+a pool of per-sequence KDA states whose dtype is a serving knob; the pool
+step is the plain decode step on the state in each sequence's slot."""
+
+import numpy as np
+import torch
+
+import oracle.kda_oracle as orc
+from gated_delta_rule_04_amd import inputs
+
+
+def test_round_bf16_matches_torch_on_float32_values():
+    # torch's float32 -> bfloat16 conversion rounds to nearest, ties to even
+    x = np.random.default_rng(7).standard_normal(200000) * np.exp(np.random.default_rng(8).uniform(-30, 30, 200000))
+    x32 = x.astype(np.float32).astype(np.float64)
+    ref = torch.tensor(x32, dtype=torch.float32).bfloat16().double().numpy()
+    assert np.array_equal(orc.round_bf16(x32), ref)
+
+
+def test_round_bf16_ties_and_exact_values():
+    # bfloat16 spacing is 2^-7 in [1, 2) and 2^-6 in [2, 4)
+    x = np.array([1.0, 1 + 2.0 ** -7, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -9, 3 + 2.0 ** -7,
+                  3 + 3 * 2.0 ** -7, -(1 + 2.0 ** -8), 0.0, 2.0 ** -100])
+    want = np.array([1.0, 1 + 2.0 ** -7, 1.0, 1 + 2.0 ** -6, 1.0, 3.0, 3 + 2.0 ** -5, -1.0, 0.0, 2.0 ** -100])
+    assert np.array_equal(orc.round_bf16(x), want)
+    # idempotent, and within half a spacing of the input
+    y = np.random.default_rng(9).standard_normal(1000)
+    r = orc.round_bf16(y)
+    assert np.array_equal(orc.round_bf16(r), r)
+    m, e = np.frexp(y)
+    assert np.all(np.abs(r - y) <= np.ldexp(0.5, e - 8) * (1 + 1e-12))
+
+
+def _step_inputs(N, H, dk, dv, seed):
+    r = inputs.make_decode(N, H, dk, dv, steps=1, dtype="f32", g_group=1, seed=seed)
+    st = r["steps"][0]
+    return {n: st[n].double().numpy() for n in st}, r["state"].double().numpy()
+
+
+def test_pool_step_routes_each_sequence_to_its_slot():
+    x, S = _step_inputs(4, 2, 8, 8, seed=41)
+    pool = np.random.default_rng(3).standard_normal((6, 2, 8, 8)) * 0.1
+    slots = np.array([4, -1, 0, 6])  # 6 == num_slots: inactive, like -1
+    new, o = orc.kda_decode_step_pool(pool, slots, x["q"], x["k"], x["v"], x["g"], x["beta"])
+    for n, s in enumerate(slots):
+        if 0 <= s < 6:
+            S1, o1 = orc.kda_decode_step(pool[s][None], x["q"][n:n + 1], x["k"][n:n + 1], x["v"][n:n + 1],
+                                         x["g"][n:n + 1], x["beta"][n:n + 1])
+            assert np.array_equal(new[s], S1[0]) and np.array_equal(o[n], o1[0])
+        else:
+            assert np.all(o[n] == 0)
+    for s in (1, 2, 3, 5):  # slots no active sequence names are unchanged
+        assert np.array_equal(new[s], pool[s])
+
+
+def test_pool_step_bf16_state_is_the_rounded_exact_step():
+    x, S = _step_inputs(3, 2, 16, 8, seed=42)
+    pool = orc.round_bf16(np.random.default_rng(4).standard_normal((3, 2, 16, 8)) * 0.05)
+    new, o = orc.kda_decode_step_pool(pool, np.array([2, 0, 1]), x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                      state_bf16=True)
+    exact, o_exact = orc.kda_decode_step_pool(pool, np.array([2, 0, 1]), x["q"], x["k"], x["v"], x["g"], x["beta"])
+    assert np.array_equal(o, o_exact)                  # the output is the exact step's
+    assert np.array_equal(new, orc.round_bf16(exact))  # the state is its bf16 rounding
+    assert not np.array_equal(new, exact)
