@@ -312,6 +312,34 @@ def main():
         "alg_bytes_per_launch": pool_bytes,
         "hbm_frac_alg": pool_bytes / (pool_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
+    # Short causal convolution (outside the timed step): one K3 projection's
+    # width over the prefill tokens, W = 4.
+    Cc, Wc = H * dk, 4
+    gc = torch.Generator().manual_seed(19)
+    xc = torch.randn((B, T, Cc), generator=gc).to(torch.bfloat16).to(dev)
+    wc = (0.5 * torch.randn((Cc, Wc), generator=gc)).to(torch.bfloat16).to(dev)
+    yc = torch.empty_like(xc)
+    for _ in range(args.warmup):
+        kda.short_conv_fwd(xc, wc, out=yc)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        cev[i][0].record()
+        kda.short_conv_fwd(xc, wc, out=yc)
+        cev[i][1].record()
+    torch.cuda.synchronize()
+    conv_ms = [e[0].elapsed_time(e[1]) for e in cev]
+    conv_avg = mean(conv_ms)
+    conv_bytes = 2 * (2 * B * T * Cc) + 2 * Cc * Wc
+    line["short_conv_bf16"] = {
+        "kernel": "short_conv_fwd_kernel",
+        "config": {"B": B, "T": T, "C": Cc, "W": Wc},
+        "tokens_per_s": B * T / (conv_avg * 1e-3),
+        "ms": conv_avg,
+        "ms_min": min(conv_ms),
+        "alg_bytes_per_launch": conv_bytes,
+        "hbm_frac_alg": conv_bytes / (conv_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    del xc, yc
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, dec)
     print(json.dumps(line), flush=True)

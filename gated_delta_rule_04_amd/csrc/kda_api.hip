@@ -151,4 +151,45 @@ kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, 
   return KDA_OK;
 }
 
+static bool conv_dims_ok(int C, int W) { return C > 0 && C % 8 == 0 && W >= 1 && W <= 8; }
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+kda_status kda_short_conv_fwd(const void* x, const void* weight, const void* conv0, void* y, void* conv_final,
+                              const int* cu_seqlens, int num_seqs, int B, int T, int C, int W, kda_dtype dt,
+                              void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 0 || T < 0 || num_seqs < 0 || C <= 0) return KDA_ERR_SHAPE;
+  if (!conv_dims_ok(C, W)) return KDA_ERR_UNSUPPORTED;
+  if (cu_seqlens) {
+    if (B != 1) return KDA_ERR_SHAPE;
+  } else if (num_seqs != B) {
+    return KDA_ERR_SHAPE;
+  }
+  if (!prod_fits({B, T}, INT_MAX) || !prod_fits({B, T, C}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  if (!prod_fits({num_seqs, W, C}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  const bool has_tokens = (long long)B * T > 0;
+  if (has_tokens && (!x || !weight || !y)) return KDA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(conv0) || !aligned16(conv_final)) return KDA_ERR_UNSUPPORTED;
+  if (!has_tokens && !(conv_final && W > 1 && num_seqs > 0)) return KDA_OK;
+  if (kda::launch_short_conv_fwd(dt == KDA_BF16, x, weight, conv0, y, conv_final, cu_seqlens, num_seqs, B, T, C, W,
+                                 static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_short_conv_step(const void* x, const void* weight, void* conv_state, void* y, int N, int C, int W,
+                               kda_dtype dt, void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (N < 0 || C <= 0) return KDA_ERR_SHAPE;
+  if (!conv_dims_ok(C, W)) return KDA_ERR_UNSUPPORTED;
+  if (!prod_fits({N, C}, INT_MAX) || !prod_fits({N, W, C}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  if (N == 0) return KDA_OK;
+  if (!x || !weight || !y || (W > 1 && !conv_state)) return KDA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(conv_state)) return KDA_ERR_UNSUPPORTED;
+  if (kda::launch_short_conv_step(dt == KDA_BF16, x, weight, conv_state, y, N, C, W,
+                                  static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
 }  // extern "C"

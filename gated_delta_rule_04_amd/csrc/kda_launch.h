@@ -27,6 +27,11 @@ hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* 
 hipError_t launch_decode_pool(bool bf16_io, bool bf16_state, int Dk, int Dv, int g_group, const void* q,
                               const void* k, const void* v, const void* g, const void* beta, void* pool,
                               const int* slots, int num_slots, int H, void* o, int NH, hipStream_t stream);
+hipError_t launch_short_conv_fwd(bool bf16_io, const void* x, const void* weight, const void* conv0, void* y,
+                                 void* conv_final, const int* cu, int num_seqs, int B, int T, int C, int W,
+                                 hipStream_t s);
+hipError_t launch_short_conv_step(bool bf16_io, const void* x, const void* weight, void* state, void* y, int N,
+                                  int C, int W, hipStream_t s);
 hipError_t launch_prefill(bool bf16_io, int Dk, int Dv, int g_group, int VS, const PrefillArgs& a,
                           hipStream_t stream);
 hipError_t launch_prefill_pipe(int Dk, int Dv, int g_group, int VS, const PrefillArgs& a, hipStream_t stream);

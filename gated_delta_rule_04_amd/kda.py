@@ -28,7 +28,7 @@ _STATUS = {
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
 EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_step_pool",
-            "kda_status_str", "kda_abi_version"]
+            "kda_short_conv_fwd", "kda_short_conv_step", "kda_status_str", "kda_abi_version"]
 
 _lib = None
 
@@ -62,6 +62,10 @@ def lib():
     L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.kda_recurrent_step_pool.restype = i
     L.kda_recurrent_step_pool.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, vp]
+    L.kda_short_conv_fwd.restype = i
+    L.kda_short_conv_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    L.kda_short_conv_step.restype = i
+    L.kda_short_conv_step.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     _lib = L
     return L
 
@@ -178,3 +182,47 @@ def recurrent_step_pool(q, k, v, g, beta, state_pool, slots, out=None):
     if st != 0:
         raise KdaError(st, "kda_recurrent_step_pool")
     return o
+
+
+def short_conv_fwd(x, weight, conv0=None, output_final_state=False, cu_seqlens=None, out=None, conv_final=None):
+    """Short causal depthwise convolution along tokens with document reset.
+    x [B, T, C]; weight [C, W]; conv0 / conv_final [N, W-1, C] (same dtype).
+    Returns (y, conv_final) -- conv_final is None unless requested."""
+    B, T, C = x.shape
+    W = weight.shape[-1]
+    dt = _dt(x)
+    for t in (weight, conv0, conv_final, out):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError("x, weight, conv states and y must share one dtype")
+    if weight.shape != (C, W):
+        raise ValueError("weight must be [C, W]")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    y = out if out is not None else torch.empty_like(x)
+    cf = conv_final
+    if output_final_state and cf is None:
+        cf = torch.empty((N, max(W - 1, 0), C), dtype=x.dtype, device=x.device)
+    _check_dev(x, weight, conv0, y, cf, cu_seqlens)
+    st = lib().kda_short_conv_fwd(_ptr(x), _ptr(weight), _ptr(conv0), _ptr(y), _ptr(cf), _ptr(cu_seqlens), N, B, T,
+                                  C, W, dt, _stream())
+    if st != 0:
+        raise KdaError(st, "kda_short_conv_fwd")
+    return y, cf
+
+
+def short_conv_step(x, weight, conv_state, out=None):
+    """One decode step of the short convolution: x [N, C]; conv_state
+    [N, W-1, C] updated in place.  Returns y [N, C]."""
+    N, C = x.shape
+    W = weight.shape[-1]
+    dt = _dt(x)
+    y = out if out is not None else torch.empty_like(x)
+    _check_dev(x, weight, conv_state, y)
+    st = lib().kda_short_conv_step(_ptr(x), _ptr(weight), _ptr(conv_state), _ptr(y), N, C, W, dt, _stream())
+    if st != 0:
+        raise KdaError(st, "kda_short_conv_step")
+    return y

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -132,6 +132,48 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
 kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                    void* state_pool, const int* slots, int num_slots, void* o, int N, int H,
                                    int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt, void* stream);
+
+/* Short causal depthwise convolution along the token axis, with document
+ * reset.  The miniKimiK3 card ("Limitations") says order information reaches
+ * the model only through KDA's decay and short convolutions plus the causal
+ * mask; the Mini-K3-1H-mamba2 README (packed-document paragraph) resets
+ * convolution history at every document boundary; the Mini-K3-1H cards list
+ * convolution length as an ablation axis.  Per channel c and token t of a
+ * sequence (or document) that starts at s:
+ *
+ *   y[t][c] = sum_{w=0}^{W-1} weight[c][w] * x[t - (W-1) + w][c]
+ *
+ * where a position p < s reads the initial conv state: conv0[n][p - s + W-1][c]
+ * (the W-1 inputs that preceded the sequence), or zero when conv0 is NULL.
+ * No bias, no activation.  Accumulation is fp32.
+ *
+ *   x      [B, T, C]   dt        (C: channels, e.g. H * D of one projection)
+ *   weight [C, W]      dt
+ *   conv0  [N, W-1, C] dt or NULL
+ *   y      [B, T, C]   dt        output (may not alias x)
+ *   conv_final [N, W-1, C] dt or NULL: each sequence's last W-1 inputs
+ *          (positions before its start taken from conv0 / zeros); may not
+ *          alias conv0.
+ *   cu_seqlens, num_seqs, B, T: as for kda_chunk_fwd (device int32
+ *          [num_seqs + 1] or NULL; non-NULL requires B = 1; clamped into
+ *          [0, T] on the device).
+ * Supported: 1 <= W <= 8, C a positive multiple of 8, and x, y, conv0,
+ * conv_final 16-byte aligned.  Errors as for kda_chunk_fwd; KDA_ERR_UNSUPPORTED
+ * for W, C or alignment outside that set.
+ */
+kda_status kda_short_conv_fwd(const void* x, const void* weight, const void* conv0, void* y, void* conv_final,
+                              const int* cu_seqlens, int num_seqs, int B, int T, int C, int W, kda_dtype dt,
+                              void* stream);
+
+/* One decode step of the short convolution for N sequences, state in place:
+ * with the window [conv_state[n][0..W-2], x[n]], y[n] = sum_w weight[:, w] *
+ * window[w] and conv_state[n] <- window[1..W-1].
+ *   x [N, C] dt;  weight [C, W] dt;  conv_state [N, W-1, C] dt;  y [N, C] dt.
+ * conv_state may be NULL only when W = 1.  N = 0 is a no-op.  Supported W,
+ * C and alignment (x, y, conv_state) as for kda_short_conv_fwd.
+ */
+kda_status kda_short_conv_step(const void* x, const void* weight, void* conv_state, void* y, int N, int C, int W,
+                               kda_dtype dt, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* kda_status_str(kda_status s);

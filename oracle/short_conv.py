@@ -1,0 +1,67 @@
+"""CPU fp64 oracle of the short causal convolution (test infrastructure only:
+used by tests/, never by the product path).
+
+Sources: the miniKimiK3 card ("Limitations") -- order information reaches the
+model only through KDA's decay and short convolutions plus the causal mask;
+the Mini-K3-1H-mamba2 README (packed-document paragraph) -- convolution
+history resets at every document boundary; the Mini-K3-1H cards list
+convolution length as an ablation axis.
+
+Readings (the pages give no formula): a depthwise causal convolution along
+the token axis, per channel c with weights w[c, 0..W-1]:
+
+    y[t, c] = sum_w w[c, w] * x[t - (W-1) + w, c]
+
+with the W-1 positions before a sequence's first token taken from an initial
+conv state (the inputs that preceded it) or zero; no bias, no activation.
+"""
+
+import numpy as np
+
+
+def _f64(a):
+    return np.asarray(a.detach().cpu().double().numpy() if hasattr(a, "detach") else a, dtype=np.float64)
+
+
+def _windowed(ext, w):
+    """y[t] = sum_j w[:, j] * ext[t + j] for t = 0 .. len(ext) - W."""
+    W = w.shape[1]
+    L = ext.shape[0] - (W - 1)
+    y = np.zeros((L, ext.shape[1]))
+    for j in range(W):
+        y += w[:, j][None, :] * ext[j:j + L]
+    return y
+
+
+def short_conv_forward(x, weight, conv0=None, cu_seqlens=None):
+    """x: [B, T, C]; weight: [C, W]; conv0: [N, W-1, C] or None.
+    Returns (y [B, T, C], conv_final [N, W-1, C]): conv_final holds each
+    sequence's last W-1 inputs (earlier positions from conv0 or zeros)."""
+    x = _f64(x)
+    w = _f64(weight)
+    B, T, C = x.shape
+    W = w.shape[1]
+    if cu_seqlens is not None:
+        cu = [int(c) for c in np.asarray(cu_seqlens)]
+        seqs = [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+    else:
+        seqs = [(b, 0, T) for b in range(B)]
+    y = np.zeros((B, T, C))
+    final = np.zeros((len(seqs), W - 1, C))
+    for n, (b, s, e) in enumerate(seqs):
+        hist = _f64(conv0)[n] if conv0 is not None else np.zeros((W - 1, C))
+        ext = np.concatenate([hist, x[b, s:e]], axis=0)
+        y[b, s:e] = _windowed(ext, w)
+        final[n] = ext[ext.shape[0] - (W - 1):]
+    return y, final
+
+
+def short_conv_step(x, weight, conv_state):
+    """One decode step: x [N, C]; weight [C, W]; conv_state [N, W-1, C].
+    Returns (y [N, C], new_state [N, W-1, C])."""
+    x = _f64(x)
+    w = _f64(weight)
+    st = _f64(conv_state)
+    win = np.concatenate([st, x[:, None, :]], axis=1)  # [N, W, C]
+    y = np.einsum("cw,nwc->nc", w, win)
+    return y, win[:, 1:]
