@@ -44,3 +44,99 @@ def chunked_forward(q, k, v, g, beta, S0, C):
         o[s:e] = Qt @ S + P @ U
         S = np.exp(G[-1])[:, None] * S + Kb.T @ U
     return o, S
+
+
+def chunked_backward(q, k, v, g, beta, S0, do, dST, C):
+    """Gradients of <do, o> + <dST, S_L> through the chunked form, for one
+    head: q, k [L, dk]; v, do [L, dv]; g [L, dk] (expanded); beta [L];
+    S0, dST [dk, dv].  Returns a dict of dq, dk, dv, dg, dbeta, dh0.
+
+    The decomposition the GPU backward uses:
+
+    1. forward, keeping the state S_c entering every chunk;
+    2. per chunk, independently: the transfer of the state cotangent
+       F^T = (I - W^T Kh) Diag(gam) with W = T Kt, and the offset
+       b = Z^T dO with Z = Qt - P W, so that the reverse state pass is
+       dS_c = F^T dS_{c+1} + b  (F = Diag(gam)(I - Kh^T W) is the chunk's
+       forward transfer S -> Diag(gam) S + Kb^T U restricted to S);
+    3. the reverse state pass over chunks, keeping dS_{c+1} for every chunk;
+    4. per chunk, independently, with dSt = Diag(gam) dS_{c+1}:
+         R = V - Kt S;  U = T R;  dU = Kh dSt + P^T dO;  dR = T^T dU  (= dv)
+         dP = lower_incl(dO U^T);  dT = lower_incl(dU R^T)
+         dbeta_j = sum_i dT_ij X_ij;  dA = -strict(X^T dT Diag(beta) X^T)
+         dbeta_r += sum_i dA_ri B_ri  (B = Kt Kh^T);  dB = Diag(beta) dA
+         dQt = dO S^T + dP Kh;  dKt = -dR S^T + dB Kh
+         dKH = dB^T Kt + dP^T Qt + U dSt^T
+         dq = dQt e^G;  dk = dKt e^G + dKH e^-G
+         dG = q dq + k (dKt e^G - dKH e^-G), and on the chunk's last row
+              + sum_r (U dSt^T * Kh)_r + rowsum(S * dSt)
+         dg = reverse cumulative sum of dG over the chunk.
+    """
+    L, dk = q.shape
+    starts = list(range(0, L, C))
+    S_in = []
+    S = np.array(S0, dtype=np.float64, copy=True)
+    blocks = []
+    for s in starts:
+        e = min(L, s + C)
+        c = e - s
+        G = np.cumsum(g[s:e], axis=0)
+        eG, emG = np.exp(G), np.exp(-G)
+        gam = eG[-1]
+        Kt, Qt, Kh = k[s:e] * eG, q[s:e] * eG, k[s:e] * emG
+        b = beta[s:e]
+        Bm = np.tril(Kt @ Kh.T, -1)
+        A = b[:, None] * Bm
+        P = np.tril(Qt @ Kh.T, 0)
+        X = np.linalg.inv(np.eye(c) + A)
+        T = X * b[None, :]
+        blocks.append(dict(s=s, e=e, G=G, eG=eG, emG=emG, gam=gam, Kt=Kt, Qt=Qt, Kh=Kh, B=Bm, P=P, X=X, T=T))
+        S_in.append(S.copy())
+        U = T @ (v[s:e] - Kt @ S)
+        S = gam[:, None] * S + (Kh * gam[None, :]).T @ U
+    # 2. per-chunk transfer and offset of the state cotangent
+    Ft, off = [], []
+    for bl in blocks:
+        W = bl["T"] @ bl["Kt"]
+        Z = bl["Qt"] - bl["P"] @ W
+        Ft.append((np.eye(dk) - W.T @ bl["Kh"]) * bl["gam"][None, :])
+        off.append(Z.T @ do[bl["s"]:bl["e"]])
+    # 3. reverse state pass
+    dS = np.array(dST, dtype=np.float64, copy=True)
+    dS_out = [None] * len(blocks)
+    for i in range(len(blocks) - 1, -1, -1):
+        dS_out[i] = dS.copy()
+        dS = Ft[i] @ dS + off[i]
+    res = {n: np.zeros(x.shape) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta))}
+    res["dh0"] = dS
+    # 4. chunk-local gradients
+    for i, bl in enumerate(blocks):
+        s, e = bl["s"], bl["e"]
+        Sc, dSt = S_in[i], bl["gam"][:, None] * dS_out[i]
+        dO = do[s:e]
+        T, X, P, Kh, Kt, Qt = bl["T"], bl["X"], bl["P"], bl["Kh"], bl["Kt"], bl["Qt"]
+        bb = beta[s:e]
+        R = v[s:e] - Kt @ Sc
+        U = T @ R
+        dU = Kh @ dSt + P.T @ dO
+        dR = T.T @ dU
+        dP = np.tril(dO @ U.T, 0)
+        dT = np.tril(dU @ R.T, 0)
+        db = np.sum(dT * X, axis=0)
+        dA = -np.tril(X.T @ (dT * bb[None, :]) @ X.T, -1)
+        db += np.sum(dA * bl["B"], axis=1)
+        dB = bb[:, None] * dA
+        dQt = dO @ Sc.T + dP @ Kh
+        dKt = -dR @ Sc.T + dB @ Kh
+        dKb = U @ dSt.T
+        dKH = dB.T @ Kt + dP.T @ Qt + dKb
+        dq = dQt * bl["eG"]
+        dkk = dKt * bl["eG"] + dKH * bl["emG"]
+        dG = q[s:e] * dq + k[s:e] * (dKt * bl["eG"] - dKH * bl["emG"])
+        dG[-1] += np.sum(dKb * Kh, axis=0) + np.sum(Sc * dSt, axis=1)
+        res["dq"][s:e] = dq
+        res["dk"][s:e] = dkk
+        res["dv"][s:e] = dR
+        res["dg"][s:e] = np.cumsum(dG[::-1], axis=0)[::-1]
+        res["dbeta"][s:e] = db
+    return res
