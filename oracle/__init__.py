@@ -5,4 +5,3 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 """
 
 from .kda_oracle import expand_decay, kda_step, kda_sequence, kda_forward, kda_decode_step  # noqa: F401
-from .kda_backward import kda_backward  # noqa: F401
