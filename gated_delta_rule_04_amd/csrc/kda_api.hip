@@ -114,6 +114,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
   a.num_units = (int)units;
   a.H = H;
   a.T = T;
+  a.hs = nullptr;
   const int vs = kda::prefill_slice_width(bf, Dk, Dv, units, device_cus());
   if (kda::launch_prefill(bf, Dk, Dv, g_group, vs, a, s) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
@@ -189,6 +190,127 @@ kda_status kda_short_conv_step(const void* x, const void* weight, void* conv_sta
   if (kda::launch_short_conv_step(dt == KDA_BF16, x, weight, conv_state, y, N, C, W,
                                   static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+struct BwdLayout {
+  size_t order, hs, fw, bw, dh, total;
+};
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+// Slots cover every 64-token chunk of every sequence: chunk c of sequence n
+// (first token t0) is slot t0 / 64 + n + c, below tokens / 64 + N + 1.
+bool bwd_layout(int B, int T, int H, int Dk, int Dv, int N, bool varlen, BwdLayout& L, long long& slots) {
+  if (B < 0 || T < 0 || H <= 0 || N < 0) return false;
+  if (!prod_fits({B, T}, INT_MAX)) return false;
+  slots = (long long)B * T / 64 + N + 1;
+  if (!prod_fits({slots, H, Dk, Dv}, LLONG_MAX / 16) || !prod_fits({slots, H}, INT_MAX)) return false;
+  const size_t sh = (size_t)slots * H;
+  L.order = varlen ? varlen_workspace(N) : 0;
+  L.hs = L.order;
+  L.fw = L.hs + align256(sh * Dk * Dv * 2);
+  L.bw = L.fw + align256(sh * Dk * Dk * 2);
+  L.dh = L.bw + align256(sh * Dk * Dv * 4);
+  L.total = L.dh + align256(sh * Dk * Dv * 2);
+  return true;
+}
+}  // namespace
+
+extern "C" {
+
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs, int varlen, kda_dtype dt) {
+  (void)dt;
+  BwdLayout L;
+  long long slots;
+  if (!bwd_layout(B, T, H, Dk, Dv, num_seqs, varlen != 0, L, slots)) return 0;
+  return L.total;
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* h0, const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                         void* dg, void* dbeta, float* dh0, const int* cu_seqlens, int num_seqs, int B, int T,
+                         int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
+  if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
+  if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen) {
+    if (B != 1) return KDA_ERR_SHAPE;
+  } else if (num_seqs != B) {
+    return KDA_ERR_SHAPE;
+  }
+  const int N = num_seqs;
+  if (!prod_fits({B, T, H, Dk > Dv ? Dk : Dv}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  if (!prod_fits({N, H, Dk, Dv}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  if (!prod_fits({N, H}, INT_MAX / 16)) return KDA_ERR_SHAPE;
+  BwdLayout L;
+  long long slots;
+  if (!bwd_layout(B, T, H, Dk, Dv, N, varlen, L, slots)) return KDA_ERR_SHAPE;
+  const bool has_tokens = (long long)B * T > 0;
+  if (has_tokens && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+    return KDA_ERR_NULL;
+  if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long long units = (long long)N * H;
+  if (units == 0) return KDA_OK;
+  char* ws = static_cast<char*>(workspace);
+  int* order = nullptr;
+  if (varlen) {
+    order = reinterpret_cast<int*>(ws + 0);
+    if (kda::launch_varlen_order(cu_seqlens, N, T, order, s) != hipSuccess) return KDA_ERR_HIP;
+  }
+  // 1. forward, keeping the state entering every chunk
+  if (has_tokens) {
+    kda::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.h0 = h0;
+    a.o = nullptr;
+    a.ht = nullptr;
+    a.cu_seqlens = cu_seqlens;
+    a.order = order;
+    a.num_units = (int)units;
+    a.H = H;
+    a.T = T;
+    a.hs = ws + L.hs;
+    const int vs = kda::prefill_slice_width(true, Dk, Dv, units, device_cus());
+    if (kda::launch_prefill(true, Dk, Dv, g_group, vs, a, s) != hipSuccess) return KDA_ERR_HIP;
+  }
+  // 2.-4. transfer and offset per chunk, reverse state pass, local gradients
+  kda::BwdArgs b;
+  b.q = static_cast<const kda::bf16*>(q);
+  b.k = static_cast<const kda::bf16*>(k);
+  b.v = static_cast<const kda::bf16*>(v);
+  b.g = static_cast<const kda::bf16*>(g);
+  b.beta = static_cast<const kda::bf16*>(beta);
+  b.dout = static_cast<const kda::bf16*>(dout);
+  b.dht = dht;
+  b.dq = static_cast<kda::bf16*>(dq);
+  b.dk = static_cast<kda::bf16*>(dk);
+  b.dv = static_cast<kda::bf16*>(dv);
+  b.dg = static_cast<kda::bf16*>(dg);
+  b.dbeta = static_cast<kda::bf16*>(dbeta);
+  b.dh0 = dh0;
+  b.cu_seqlens = cu_seqlens;
+  b.order = order;
+  b.hs = reinterpret_cast<const kda::bf16*>(ws + L.hs);
+  b.fw = reinterpret_cast<kda::bf16*>(ws + L.fw);
+  b.bw = reinterpret_cast<float*>(ws + L.bw);
+  b.dh = reinterpret_cast<kda::bf16*>(ws + L.dh);
+  b.N = N;
+  b.H = H;
+  b.T = T;
+  b.slots = has_tokens ? (int)slots : 0;
+  if (kda::launch_chunk_bwd(Dk, Dv, g_group, b, s) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
 

@@ -1,0 +1,916 @@
+// KDA backward pass of the chunked form, gfx950 (CDNA4), bf16 inputs.
+//
+// The miniKimiK3 card ("Architecture", Kimi Delta Attention bullet) states
+// that KDA trains through a chunked parallel form; training needs the
+// gradients of a loss L = <do, o> + <dht, ht> with respect to q, k, v, g,
+// beta and h0.  The block algebra below is the reverse mode of the chunked
+// forward (same notation: per head and chunk, G the chunk-local cumulative
+// log-decay, Qt = Q e^G, Kt = K e^G, Kh = K e^-G, gam = e^{G_last},
+// A = strictly_lower(Diag(b) Kt Kh^T), P = lower_incl(Qt Kh^T),
+// X = (I + A)^-1, T = X Diag(b)):
+//
+// 1. The forward keeps the state S entering every chunk (bf16, row-major).
+// 2. chunk_bwd_prep_kernel, per chunk, independently: with W = T Kt and
+//    Z = Qt - P W, the state cotangent crosses the chunk as
+//        dS_in = F^T dS_out + b,  F = Diag(gam)(I - Kh^T W),  b = Z^T dO
+//    (F is the chunk's forward map S -> Diag(gam) S + Kb^T U on S).
+// 3. chunk_bwd_dh_kernel walks each sequence's chunks backwards from dht,
+//    keeping dS_out of every chunk (bf16), and returns dh0 (fp32).
+// 4. chunk_bwd_local_kernel, per chunk, independently, with S and
+//    dSt = Diag(gam) dS_out:
+//        R = V - Kt S;  U = T R;  dU = Kh dSt + P^T dO;  dR = T^T dU (= dv)
+//        dP = lower_incl(dO U^T);  dT = lower_incl(dU R^T)
+//        dbeta_j = sum_i dT_ij X_ij + sum_i dA_ji B_ji  (B = Kt Kh^T)
+//        dA = -strict(X^T dT Diag(b) X^T);  dB = Diag(b) dA
+//        dQt = dO S^T + dP Kh;  dKt = -dR S^T + dB Kh
+//        dKh' = dB^T Kt + dP^T Qt;  dKb = U dSt^T
+//        dq = dQt e^G;  dk = dKt e^G + (dKh' + dKb) e^-G
+//        dG = q dq + k (dKt e^G - (dKh' + dKb) e^-G), plus on the chunk's
+//             last row sum_r (dKb * Kh)_r + rowsum(S * dSt);
+//        dg = reverse cumulative sum of dG over the chunk (summed over a
+//             decay group when one log-decay value serves 64 channels).
+//
+// Design for MI355X.  Steps 2 and 4 are fully parallel over (chunk, head):
+// one workgroup per chunk-head, one wavefront per 16 key channels, all
+// operand tiles in LDS and every product on v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulation.  LDS tiles are stored with their 4-element units
+// XOR-permuted by row / 4, so one copy serves both row reads and transposing
+// reads (ds_read_b64_tr_b16).  Step 4 walks the value columns in slices of 32
+// to stay inside the 160 KB of LDS per workgroup; everything that contracts
+// over the value axis accumulates in registers across the slices.  Step 3 is
+// the only recurrence: a short MFMA chain per chunk, with F staged through LDS
+// two chunks ahead.  The slot of chunk c of the sequence that starts at
+// token t0 and has index n is (t0 / 64) + n + c, so the per-chunk buffers
+// need no prefix sum over the sequences.
+
+#include "kda_prefill_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+template <int DK_, int DV_, int GG_>
+struct BwdCfg {
+  static constexpr int DK = DK_, DV = DV_, GG = GG_;
+  static constexpr int C = 64;
+  static constexpr int NW = DK / 16;   // wavefronts: one per 16 key channels
+  static constexpr int NT = 64 * NW;
+  static constexpr int NB = NT / DK;   // gating: token blocks per chunk
+  static constexpr int TB = C / NB;    // gating: tokens per block
+  static constexpr int KT = DK / 16;   // key-channel tiles
+  static constexpr int KHP = DK + 16;  // pitch of the [C][DK] operand tiles
+  static constexpr int CTP = C + 16;   // pitch of the [C][C] tiles
+  static constexpr int AP = C + 4;     // pitch of the fp32 A tile
+  static constexpr int VSL = 32;       // local kernel: value columns per slice
+  static constexpr int SP = VSL + 16;  // pitch of the slice tiles
+  static constexpr int NSL = DV / VSL;
+  static constexpr int DVP = DV + 16;  // pitch of the [C][DV] dO tile (prep)
+  static_assert(NB == 4 && TB == 16, "gating map");
+};
+
+typedef Frag<bf16> F;
+typedef F::V FV;
+
+// Element offset of column c within row r of a unit-swizzled tile.
+__device__ __forceinline__ int swz(int r, int c) { return 4 * ((c >> 2) ^ kh_swizzle(r)) + (c & 3); }
+
+// Row fragment (slab s) of row `row` of a unit-swizzled tile with pitch P.
+template <int P>
+__device__ __forceinline__ FV ld_row(const bf16* tile, int row, int s, int kg) {
+  return F::ld_sw(tile + row * P, s, kg, kh_swizzle(row));
+}
+
+// Four consecutive values of row r, columns c .. c+3 (c % 4 == 0) of a swizzled tile.
+template <int P>
+__device__ __forceinline__ void st_row4(bf16* tile, int r, int c, const f32x4& v) {
+  store4<bf16>(tile + r * P + swz(r, c), v);
+}
+
+// An accumulator tile M (lane: M[4kg+i][l16]) at block (R0, C0) of a swizzled
+// tile, written as rows through the exact transposing product.
+template <int P>
+__device__ __forceinline__ void st_acc(bf16* tile, int R0, int C0, const f32x4& m, const f32x4& ident, int l16,
+                                       int kg) {
+  st_row4<P>(tile, R0 + l16, C0 + 4 * kg, Reg16<bf16>::prod(m, ident));
+}
+// The same tile written transposed: tile[C0 + j][R0 + i] = M[i][j].
+template <int P>
+__device__ __forceinline__ void st_acc_t(bf16* tile, int R0, int C0, const f32x4& m, int l16, int kg) {
+  st_row4<P>(tile, C0 + l16, R0 + 4 * kg, m);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// The lower 16x16 tiles (I >= J) of a 64x64 matrix, the diagonal ones first.
+__device__ __forceinline__ void lower_tile(int j, int& I, int& J) {
+  // 0..3: (0,0) (1,1) (2,2) (3,3); 4..9: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+  if (j < 4) {
+    I = J = j;
+  } else {
+    const int o = j - 4;
+    I = o < 1 ? 1 : (o < 3 ? 2 : 3);
+    J = o - (I == 1 ? 0 : (I == 2 ? 1 : 3));
+  }
+}
+
+// Sequence geometry shared by the kernels.
+struct Seq {
+  int seq, tok0, len;
+};
+__device__ __forceinline__ Seq seq_info(const int* cu, int n, int T) {
+  Seq s;
+  s.seq = n;
+  if (cu) {
+    const int a = min(max(cu[n], 0), T);
+    const int b = min(max(cu[n + 1], a), T);
+    s.tok0 = a;
+    s.len = b - a;
+  } else {
+    s.tok0 = n * T;
+    s.len = T;
+  }
+  return s;
+}
+// The sequence and chunk of a slot: the last n with base(n) = t0(n) / 64 + n
+// <= slot (base is strictly increasing); the slot is unused if its chunk
+// index is past the sequence's chunks.
+__device__ __forceinline__ bool slot_chunk(const int* cu, int N, int T, int slot, Seq& s, int& c) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const Seq m = seq_info(cu, mid, T);
+    if ((m.tok0 >> 6) + mid <= slot)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  s = seq_info(cu, lo, T);
+  c = slot - ((s.tok0 >> 6) + lo);
+  return c >= 0 && c * 64 < s.len;
+}
+
+}  // namespace
+
+
+// ---------------------------------------------------------------------------
+// The chunk front shared by the parallel kernels: gating, the k-k and q-k
+// blocks and the UT solve, all into LDS.  LOCAL selects the tiles the local
+// kernel needs (T, T^T, P^T, X); otherwise (prep) T and P.
+// ---------------------------------------------------------------------------
+template <class Cfg>
+struct FrontTiles {
+  static constexpr int C = Cfg::C, KHP = Cfg::KHP, CTP = Cfg::CTP, DK = Cfg::DK;
+  bf16 qt[C * KHP], kt[C * KHP], kh[C * KHP];  // swizzled token-major
+  bf16 t[C * CTP];   // T rows
+  bf16 u1[C * CTP];  // local: T^T rows; prep: P rows
+  bf16 u2[C * CTP];  // local: P^T rows
+  bf16 x[C * CTP];   // local: X rows
+  alignas(16) float gam[DK];
+  alignas(16) float beta[C];
+  alignas(16) float gsum[Cfg::NB][DK];
+};
+template <class Cfg>
+struct FrontScratch {
+  alignas(16) float a[Cfg::C * Cfg::AP];  // A = Diag(b) B below the diagonal blocks (fp32)
+  alignas(16) float xd[4][16][20];        // diagonal blocks of X (fp32)
+};
+
+template <class Cfg, bool LOCAL>
+__device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int h, int c, FrontTiles<Cfg>& ft,
+                                            FrontScratch<Cfg>& fs, float (&G2)[Cfg::TB], const f32x4& ident) {
+  constexpr int DK = Cfg::DK, C = Cfg::C, GG = Cfg::GG, KHP = Cfg::KHP, CTP = Cfg::CTP, AP = Cfg::AP;
+  constexpr int NW = Cfg::NW, NT = Cfg::NT, TB = Cfg::TB, SK = DK / 32;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = A.H;
+
+  // ---- zero the C x C tiles (their zero parts are never written) ----
+  {
+    bf16* base = ft.t;
+    constexpr int n = 4 * C * CTP / 4;  // 8-byte units of t, u1, u2, x (contiguous)
+    static_assert(sizeof(bf16) * C * CTP * 4 == 8 * n, "tile block");
+    for (int i = tid; i < n; i += NT) *reinterpret_cast<u32x2*>(base + 4 * i) = u32x2{0u, 0u};
+  }
+
+  // ---- gating: thread = (key channel, block of 16 tokens) ----
+  const int nv = min(C, sq.len - c * C);
+  const size_t row0 = (size_t)(sq.tok0 + c * C) * H + h;
+  const int rsk = H * DK * 2, rsg = H * (DK / GG) * 2, rsb = H * 2;
+  const rsrc_t bq = make_rsrc(A.q + row0 * DK, (nv - 1) * rsk + DK * 2);
+  const rsrc_t bk = make_rsrc(A.k + row0 * DK, (nv - 1) * rsk + DK * 2);
+  const rsrc_t bg = make_rsrc(A.g + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * 2);
+  const int ch = tid % DK, tb = tid / DK;
+  {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int r = tb * TB + j;
+      acc += to_f32(bload<bf16>(bg, r * rsg + (ch / GG) * 2)) * kLog2e;
+      G2[j] = acc;
+    }
+    ft.gsum[tb][ch] = acc;
+    if (tid < C) {
+      const rsrc_t bb = make_rsrc(A.beta + row0, (nv - 1) * rsb + 2);
+      ft.beta[tid] = to_f32(bload<bf16>(bb, tid * rsb));
+    }
+  }
+  __syncthreads();
+  {
+    float off = 0.f;
+    for (int b = 0; b < tb; ++b) off += ft.gsum[b][ch];
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      G2[j] += off;
+      const int r = tb * TB + j;
+      const float q = to_f32(bload<bf16>(bq, r * rsk + ch * 2));
+      const float kk = to_f32(bload<bf16>(bk, r * rsk + ch * 2));
+      const float eg = fast_exp2(G2[j]), emg = fast_exp2(-G2[j]);
+      const int o = r * KHP + swz(r, ch);
+      ft.qt[o] = (bf16)(q * eg);
+      ft.kt[o] = (bf16)(kk * eg);
+      ft.kh[o] = (bf16)(kk * emg);
+    }
+    if (tb == Cfg::NB - 1) ft.gam[ch] = fast_exp2(G2[TB - 1]);
+  }
+  __syncthreads();
+
+  auto rows = [&](FV (&fr)[SK], const bf16* tile, int blk) {
+#pragma unroll
+    for (int s = 0; s < SK; ++s) fr[s] = ld_row<KHP>(tile, 16 * blk + l16, s, kg);
+  };
+  auto mma_rows = [&](const FV (&a)[SK], const FV (&b)[SK]) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < SK; ++s) acc = F::mma(a[s], b[s], acc);
+    return acc;
+  };
+
+  // ---- diagonal blocks (waves 0..3) and the blocks below them ----
+  f32x4 Xdiag = zero4();
+  for (int j = wave; j < 10; j += NW) {
+    int I, J;
+    lower_tile(j, I, J);
+    if (j < 4) {
+      FV ktr[SK], khr[SK], qtr[SK];
+      rows(ktr, ft.kt, I);
+      rows(khr, ft.kh, I);
+      rows(qtr, ft.qt, I);
+      f32x4 N = mma_rows(ktr, khr), Nt = mma_rows(khr, ktr);
+      const float bl = ft.beta[16 * I + l16];
+      const f32x4 br = *reinterpret_cast<const f32x4*>(&ft.beta[16 * I + 4 * kg]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * kg + i;
+        N[i] = l16 < r ? N[i] * br[i] : 0.f;
+        Nt[i] = r < l16 ? Nt[i] * bl : 0.f;
+      }
+      if constexpr (LOCAL) {
+        // P^T rows: acc form of P (lane: P[4kg+i][l16]), lower including the diagonal
+        f32x4 Pa = mma_rows(qtr, khr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Pa[i] = l16 <= 4 * kg + i ? Pa[i] : 0.f;
+        st_acc_t<CTP>(ft.u2, 16 * I, 16 * I, Pa, l16, kg);
+      } else {
+        // P rows: lane holds P[l16][4kg+i]
+        f32x4 Pt = mma_rows(khr, qtr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Pt[i] = 4 * kg + i <= l16 ? Pt[i] : 0.f;
+        st_row4<CTP>(ft.u1, 16 * I + l16, 16 * I + 4 * kg, Pt);
+      }
+      Xdiag = unit_lower_inverse16<bf16>(N, Nt, ident);
+      *reinterpret_cast<f32x4*>(&fs.xd[I][l16][4 * kg]) = Reg16<bf16>::prod(Xdiag, ident);
+      const f32x4 Td = Xdiag * bl;  // T_II = X_II Diag(b), columns scaled
+      st_acc<CTP>(ft.t, 16 * I, 16 * I, Td, ident, l16, kg);
+      if constexpr (LOCAL) {
+        st_acc_t<CTP>(ft.u1, 16 * I, 16 * I, Td, l16, kg);
+        st_acc<CTP>(ft.x, 16 * I, 16 * I, Xdiag, ident, l16, kg);
+      }
+    } else {
+      FV ktr[SK], khr[SK];
+      rows(ktr, ft.kt, I);
+      rows(khr, ft.kh, J);
+      // A_IJ rows: lane holds B[16I + l16][16J + 4kg + i], scaled by b of its row
+      const f32x4 Bt = mma_rows(khr, ktr) * ft.beta[16 * I + l16];
+      *reinterpret_cast<f32x4*>(&fs.a[(16 * I + l16) * AP + 16 * J + 4 * kg]) = Bt;
+      FV qtr[SK];
+      rows(qtr, ft.qt, I);
+      if constexpr (LOCAL)
+        st_acc_t<CTP>(ft.u2, 16 * I, 16 * J, mma_rows(qtr, khr), l16, kg);  // P^T rows
+      else
+        st_row4<CTP>(ft.u1, 16 * I + l16, 16 * J + 4 * kg, mma_rows(khr, qtr));  // P rows
+    }
+  }
+  __syncthreads();
+
+  // ---- blocks of X below the diagonal, column J on wave J:
+  //      X_IJ = -X_II sum_{K=J}^{I-1} A_IK X_KJ ----
+  static_switch<3>(wave, [&](auto Jc) {
+    constexpr int J = decltype(Jc)::value;
+    const float bj = ft.beta[16 * J + l16];
+    f32x4 Xc[4 - J];
+    Xc[0] = Xdiag;
+#pragma unroll
+    for (int d = 1; d < 4 - J; ++d) {
+      const int I = J + d;
+      f32x4 M = zero4();
+#pragma unroll
+      for (int e = 0; e < d; ++e) {
+        const f32x4 At = *reinterpret_cast<const f32x4*>(&fs.a[(16 * I + l16) * AP + 16 * (J + e) + 4 * kg]);
+        M += Reg16<bf16>::prod(At, Xc[e]);
+      }
+      const f32x4 XIt = *reinterpret_cast<const f32x4*>(&fs.xd[I][l16][4 * kg]);
+      Xc[d] = -Reg16<bf16>::prod(XIt, M);
+      const f32x4 Tn = Xc[d] * bj;
+      st_acc<CTP>(ft.t, 16 * I, 16 * J, Tn, ident, l16, kg);
+      if constexpr (LOCAL) {
+        st_acc_t<CTP>(ft.u1, 16 * I, 16 * J, Tn, l16, kg);
+        st_acc<CTP>(ft.x, 16 * I, 16 * J, Xc[d], ident, l16, kg);
+      }
+    }
+  });
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Step 2: per chunk-head, the transfer F^T and the offset b of the state
+// cotangent.  Wave w owns key-channel tile w: W and Z columns, F column tile
+// w (its F^T row tile), and b row tile w.
+// ---------------------------------------------------------------------------
+template <class Cfg>
+struct PrepSmem {
+  FrontTiles<Cfg> ft;
+  union {
+    FrontScratch<Cfg> fs;
+    bf16 dO[Cfg::C * Cfg::DVP];
+  } u;
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
+  constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, KHP = Cfg::KHP, CTP = Cfg::CTP, DVP = Cfg::DVP;
+  constexpr int NT = Cfg::NT, KS = DK / 32;
+  __shared__ PrepSmem<Cfg> sm;
+  const int h = blockIdx.x % A.H, slot = blockIdx.x / A.H;
+  Seq sq;
+  int c;
+  if (!slot_chunk(A.cu_seqlens, A.N, A.T, slot, sq, c)) return;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f32x4 ident;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
+  float G2[Cfg::TB];
+  chunk_front<Cfg, false>(A, sq, h, c, sm.ft, sm.u.fs, G2, ident);
+
+  // dO of the chunk into LDS (swizzled token-major), 16-byte pieces
+  const int nv = min(C, sq.len - c * C);
+  const size_t row0 = (size_t)(sq.tok0 + c * C) * A.H + h;
+  const int rsv = A.H * DV * 2;
+  {
+    const rsrc_t bo = make_rsrc(A.dout + row0 * DV, (nv - 1) * rsv + DV * 2);
+    for (int p = tid; p < C * DV / 8; p += NT) {
+      const int r = p / (DV / 8), c8 = 8 * (p % (DV / 8));
+      const u32x4 x = bload<u32x4>(bo, r * rsv + c8 * 2);
+      *reinterpret_cast<u32x2*>(&sm.u.dO[r * DVP + swz(r, c8)]) = u32x2{x[0], x[1]};
+      *reinterpret_cast<u32x2*>(&sm.u.dO[r * DVP + swz(r, c8 + 4)]) = u32x2{x[2], x[3]};
+    }
+  }
+
+  // W = T Kt (column tile w, all token tiles), Z = Qt - P W
+  f32x4 W[4], Z[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (32 * s <= 16 * tt + 15) acc = F::mma(ld_row<CTP>(sm.ft.t, 16 * tt + l16, s, kg),
+                                               F::ld_tr<KHP>(sm.ft.kt, 16 * w, s, l16, kg), acc);
+    W[tt] = acc;
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    f32x4 pw = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (32 * s <= 16 * tt + 15)
+        pw = F::mma(ld_row<CTP>(sm.ft.u1, 16 * tt + l16, s, kg), F::acc2(W[2 * s], W[2 * s + 1]), pw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * tt + 4 * kg + i;
+      Z[tt][i] = (float)sm.ft.qt[r * KHP + swz(r, 16 * w + l16)] - pw[i];
+    }
+  }
+  __syncthreads();  // dO complete
+
+  const size_t uh = (size_t)slot * A.H + h;
+  // F tile (r, w) = Diag(gam)(I - Kh^T W): stored as A-operand fragments of
+  // F^T, [row tile w][slab][lane][8]: elements 0..3 from tile r = 2s, 4..7 from r = 2s + 1.
+  bf16* fw = A.fw + uh * DK * DK;
+#pragma unroll
+  for (int r = 0; r < DK / 16; ++r) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) acc = F::mma(F::ld_tr<KHP>(sm.ft.kh, 16 * r, s, l16, kg), F::acc2(W[2 * s], W[2 * s + 1]), acc);
+    const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.ft.gam[16 * r + 4 * kg]);
+    f32x4 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = gm[i] * ((16 * r + 4 * kg + i == 16 * w + l16 ? 1.f : 0.f) - acc[i]);
+    store4<bf16>(fw + ((size_t)(w * KS + r / 2) * 64 + lane) * 8 + 4 * (r & 1), f);
+  }
+  // b = Z^T dO, accumulator tiles [row tile w][column tile][lane][4]
+  float* bw = A.bw + uh * DK * DV;
+#pragma unroll
+  for (int ct = 0; ct < DV / 16; ++ct) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) acc = F::mma(F::acc2(Z[2 * s], Z[2 * s + 1]), F::ld_tr<DVP>(sm.u.dO, 16 * ct, s, l16, kg), acc);
+    *reinterpret_cast<f32x4*>(bw + ((size_t)(w * (DV / 16) + ct) * 64 + lane) * 4) = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Step 3: the reverse state pass, per (sequence, head, 64-column slice):
+// dS_in = F^T dS_out + b, chunk by chunk from the last.  Four wavefronts,
+// one 16-column tile each; F^T fragments are shared through LDS and fetched
+// two chunks ahead (registers, then LDS).
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(BwdArgs A) {
+  constexpr int KS = DK / 32, KT = DK / 16, NS = DV / 64;
+  constexpr int FU = DK * DK / 8;     // 16-byte fragment units of F^T per chunk
+  constexpr int FPT = FU / 256;       // per thread
+  __shared__ u32x4 fbuf[2][FU];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the NS slices of a (sequence, head) share an XCD (and its L2)
+  const int grp = blockIdx.x / (8 * NS), w8 = blockIdx.x % (8 * NS);
+  const int unit = grp * 8 + (w8 & 7), slice = w8 >> 3;
+  if (unit >= A.N * A.H) return;
+  const int rank = unit / A.H, h = unit % A.H;
+  const int n = A.cu_seqlens && A.order ? A.order[rank] : rank;
+  const Seq sq = seq_info(A.cu_seqlens, n, A.T);
+  const int nch = (sq.len + 63) / 64;
+  const int slot0 = (sq.tok0 >> 6) + n;
+  const int ct = slice * 4 + w;  // this wave's 16-column tile
+  f32x4 ident;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
+
+  f32x4 dS[KT];
+  {
+    const float* d = A.dht ? A.dht + ((size_t)n * A.H + h) * DK * DV : nullptr;
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dS[mt][i] = d ? d[(size_t)(16 * mt + 4 * kg + i) * DV + 16 * ct + l16] : 0.f;
+  }
+  auto fsrc = [&](int cc) { return reinterpret_cast<const u32x4*>(A.fw + ((size_t)(slot0 + cc) * A.H + h) * DK * DK); };
+  auto bsrc = [&](int cc) { return A.bw + ((size_t)(slot0 + cc) * A.H + h) * DK * DV; };
+  u32x4 fr[FPT];
+  f32x4 bn[KT], bc[KT];
+  auto load_f = [&](int cc) {
+    const u32x4* p = fsrc(cc);
+#pragma unroll
+    for (int j = 0; j < FPT; ++j) fr[j] = __builtin_nontemporal_load(p + tid + 256 * j);
+  };
+  auto load_b = [&](f32x4 (&dst)[KT], int cc) {
+    const float* p = bsrc(cc);
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+      dst[mt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + ((size_t)(mt * (DV / 16) + ct) * 64 + lane) * 4));
+  };
+  auto put_f = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < FPT; ++j) fbuf[buf][tid + 256 * j] = fr[j];
+  };
+
+  if (nch > 0) {
+    load_f(nch - 1);
+    load_b(bc, nch - 1);
+    put_f((nch - 1) & 1);
+    if (nch > 1) {
+      load_f(nch - 2);
+      load_b(bn, nch - 2);
+    }
+  }
+  for (int cc = nch - 1; cc >= 0; --cc) {
+    __syncthreads();  // F^T of chunk cc is in fbuf[cc & 1]
+    // keep dS_out of chunk cc (bf16 rows of four columns)
+    bf16* dh = A.dh + ((size_t)(slot0 + cc) * A.H + h) * DK * DV;
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+      store4<bf16>(dh + (size_t)(16 * mt + l16) * DV + 16 * ct + 4 * kg, Reg16<bf16>::prod(dS[mt], ident));
+    // dS_in = F^T dS_out + b
+    FV SF[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) SF[s] = F::acc2(dS[2 * s], dS[2 * s + 1]);
+    const u32x4* fb = fbuf[cc & 1];
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+      f32x4 acc = bc[mt];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = F::mma(__builtin_bit_cast(FV, fb[(mt * KS + s) * 64 + lane]), SF[s], acc);
+      dS[mt] = acc;
+    }
+    if (cc >= 1) {
+      put_f((cc - 1) & 1);  // F^T of chunk cc - 1 (its buffer held chunk cc + 1)
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt) bc[mt] = bn[mt];
+      if (cc >= 2) {
+        load_f(cc - 2);
+        load_b(bn, cc - 2);
+      }
+    }
+  }
+  // dh0 (fp32); for an empty sequence it is dht
+  if (A.dh0) {
+    float* d0 = A.dh0 + ((size_t)n * A.H + h) * DK * DV;
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d0[(size_t)(16 * mt + 4 * kg + i) * DV + 16 * ct + l16] = dS[mt][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Step 4: per chunk-head, the chunk-local gradients.  Wave w owns key-channel
+// tile w of the [DK][C] results; the [C][32] slice products and the [C][C]
+// tiles are spread over the waves.
+// ---------------------------------------------------------------------------
+template <class Cfg>
+struct LocalSmem {
+  static constexpr int C = Cfg::C, DK = Cfg::DK, SP = Cfg::SP, CTP = Cfg::CTP;
+  struct Slice {
+    bf16 S[DK * SP], dS[DK * SP];  // S and Diag(gam) dS_out, value slice (rows: key channels)
+    bf16 dO[C * SP], R[C * SP], U[C * SP], dU[C * SP], dR[C * SP];
+  };
+  struct Grads {
+    bf16 dM[C * CTP], dP[C * CTP], dB[C * CTP], Y[C * CTP];
+  };
+  union {
+    struct {
+      FrontTiles<Cfg> ft;
+      union {
+        FrontScratch<Cfg> fs;
+        Slice sl;
+        Grads cc;
+      } u;
+    } m;
+    float fin[4][C][DK + 4];  // dQt, dKt, dKh' (= dB^T Kt + dP^T Qt), dKb; token-major
+  };
+  alignas(16) float dgc[DK];     // rowsum(S * Diag(gam) dS_out)
+  alignas(16) float dbt[4][C];   // dbeta partials from dT, by row block
+  alignas(16) float dba[4][C];   // dbeta partials from dA, by column block
+  alignas(16) float bsum[Cfg::NB][DK];
+};
+
+__device__ __forceinline__ void bstore_bf16(float v, rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)v), r, off, 0, 0);
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
+  constexpr int DK = Cfg::DK, DV = Cfg::DV, GG = Cfg::GG, C = Cfg::C, KHP = Cfg::KHP, CTP = Cfg::CTP;
+  constexpr int SP = Cfg::SP, VSL = Cfg::VSL, NW = Cfg::NW, NT = Cfg::NT, TB = Cfg::TB, NB = Cfg::NB;
+  constexpr int SK = DK / 32;
+  constexpr int MT = (20 + NW - 1) / NW;  // dP and dT tiles per wave
+  static_assert(sizeof(LocalSmem<Cfg>) <= 163840, "LDS");
+  __shared__ LocalSmem<Cfg> sm;
+  const int H = A.H;
+  const int h = blockIdx.x % H, slot = blockIdx.x / H;
+  Seq sq;
+  int c;
+  if (!slot_chunk(A.cu_seqlens, A.N, A.T, slot, sq, c)) return;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f32x4 ident;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
+  for (int i = tid; i < 4 * C; i += NT) {
+    (&sm.dbt[0][0])[i] = 0.f;
+    (&sm.dba[0][0])[i] = 0.f;
+  }
+  float G2[TB];
+  FrontTiles<Cfg>& ft = sm.m.ft;
+  chunk_front<Cfg, true>(A, sq, h, c, ft, sm.m.u.fs, G2, ident);
+  auto& sl = sm.m.u.sl;
+  auto& cc = sm.m.u.cc;
+
+  const int nv = min(C, sq.len - c * C);
+  const size_t row0 = (size_t)(sq.tok0 + c * C) * H + h;
+  const int rsv = H * DV * 2;
+  const rsrc_t bo = make_rsrc(A.dout + row0 * DV, (nv - 1) * rsv + DV * 2);
+  const rsrc_t bv = make_rsrc(A.v + row0 * DV, (nv - 1) * rsv + DV * 2);
+  const rsrc_t bdv = make_rsrc(A.dv + row0 * DV, (nv - 1) * rsv + DV * 2);
+  const size_t uh = (size_t)slot * H + h;
+  const bf16* hsS = A.hs + uh * DK * DV;
+  const bf16* dhS = A.dh + uh * DK * DV;
+
+  f32x4 cacc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) cacc[m] = zero4();
+  f32x4 dQtT[4], SdR[4], dKbT[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) dQtT[tt] = SdR[tt] = dKbT[tt] = zero4();
+  float rs = 0.f;  // rowsum(S * dSt): channel 16w + l16, columns 8kg .. 8kg + 7 of each slice
+
+  for (int v0 = 0; v0 < DV; v0 += VSL) {
+    __syncthreads();  // the front, or the previous slice, is done with the slice tiles
+    {
+      // S and dSt: one 8-element piece per thread
+      const int r = tid >> 2, p8 = 8 * (tid & 3);
+      const u32x4 s8 = *reinterpret_cast<const u32x4*>(hsS + (size_t)r * DV + v0 + p8);
+      const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(dhS + (size_t)r * DV + v0 + p8);
+      *reinterpret_cast<u32x2*>(&sl.S[r * SP + swz(r, p8)]) = u32x2{s8[0], s8[1]};
+      *reinterpret_cast<u32x2*>(&sl.S[r * SP + swz(r, p8 + 4)]) = u32x2{s8[2], s8[3]};
+      const float gm = ft.gam[r];
+      store4<bf16>(&sl.dS[r * SP + swz(r, p8)], f32x4{(float)d8[0], (float)d8[1], (float)d8[2], (float)d8[3]} * gm);
+      store4<bf16>(&sl.dS[r * SP + swz(r, p8 + 4)], f32x4{(float)d8[4], (float)d8[5], (float)d8[6], (float)d8[7]} * gm);
+      if (tid < 4 * C) {
+        const u32x4 x = bload<u32x4>(bo, r * rsv + (v0 + p8) * 2);
+        *reinterpret_cast<u32x2*>(&sl.dO[r * SP + swz(r, p8)]) = u32x2{x[0], x[1]};
+        *reinterpret_cast<u32x2*>(&sl.dO[r * SP + swz(r, p8 + 4)]) = u32x2{x[2], x[3]};
+      }
+    }
+    __syncthreads();
+    // R = V - Kt S
+    for (int job = w; job < 8; job += NW) {
+      const int tt = job >> 1, ct = job & 1;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < SK; ++s)
+        acc = F::mma(ld_row<KHP>(ft.kt, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.S, 16 * ct, s, l16, kg), acc);
+      const bf16x4 vr = bload<bf16x4>(bv, (16 * tt + l16) * rsv + (v0 + 16 * ct + 4 * kg) * 2);
+      st_acc<SP>(sl.R, 16 * tt, 16 * ct, Reg16<bf16>::rows(vr, ident, -acc), ident, l16, kg);
+    }
+    __syncthreads();
+    // U = T R;  dU = Kh dSt + P^T dO
+    for (int job = w; job < 8; job += NW) {
+      const int tt = job >> 1, ct = job & 1;
+      f32x4 u = zero4(), du = zero4();
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (32 * s <= 16 * tt + 15)
+          u = F::mma(ld_row<CTP>(ft.t, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.R, 16 * ct, s, l16, kg), u);
+      st_acc<SP>(sl.U, 16 * tt, 16 * ct, u, ident, l16, kg);
+#pragma unroll
+      for (int s = 0; s < SK; ++s)
+        du = F::mma(ld_row<KHP>(ft.kh, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.dS, 16 * ct, s, l16, kg), du);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (32 * s + 31 >= 16 * tt)
+          du = F::mma(ld_row<CTP>(ft.u2, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.dO, 16 * ct, s, l16, kg), du);
+      st_acc<SP>(sl.dU, 16 * tt, 16 * ct, du, ident, l16, kg);
+    }
+    __syncthreads();
+    // dR = T^T dU: the value gradient
+    for (int job = w; job < 8; job += NW) {
+      const int tt = job >> 1, ct = job & 1;
+      f32x4 dr = zero4();
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (32 * s + 31 >= 16 * tt)
+          dr = F::mma(ld_row<CTP>(ft.u1, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.dU, 16 * ct, s, l16, kg), dr);
+      const f32x4 rt = Reg16<bf16>::prod(dr, ident);  // rows of four columns
+      st_row4<SP>(sl.dR, 16 * tt + l16, 16 * ct + 4 * kg, rt);
+      bstore4(rt, bdv, (16 * tt + l16) * rsv + (v0 + 16 * ct + 4 * kg) * 2, bf16());
+    }
+    __syncthreads();
+    // products over the slice's value columns
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int j = w + NW * m;
+      if (j < 20) {
+        int I, J;
+        lower_tile(j % 10, I, J);
+        const bf16* a = j < 10 ? sl.dO : sl.dU;
+        const bf16* b = j < 10 ? sl.U : sl.R;
+        cacc[m] = F::mma(ld_row<SP>(a, 16 * I + l16, 0, kg), ld_row<SP>(b, 16 * J + l16, 0, kg), cacc[m]);
+      }
+    }
+    {
+      const FV srow = ld_row<SP>(sl.S, 16 * w + l16, 0, kg);
+      const FV drow = ld_row<SP>(sl.dS, 16 * w + l16, 0, kg);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        dQtT[tt] = F::mma(srow, ld_row<SP>(sl.dO, 16 * tt + l16, 0, kg), dQtT[tt]);
+        SdR[tt] = F::mma(srow, ld_row<SP>(sl.dR, 16 * tt + l16, 0, kg), SdR[tt]);
+        dKbT[tt] = F::mma(drow, ld_row<SP>(sl.U, 16 * tt + l16, 0, kg), dKbT[tt]);
+      }
+      const int r = 16 * w + l16;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int o = r * SP + swz(r, 8 * kg + 4 * e);
+        const bf16x4 a = *reinterpret_cast<const bf16x4*>(&sl.S[o]);
+        const bf16x4 b = *reinterpret_cast<const bf16x4*>(&sl.dS[o]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs += (float)a[i] * (float)b[i];
+      }
+    }
+  }
+  rs += __shfl_xor(rs, 16);
+  rs += __shfl_xor(rs, 32);
+  if (kg == 0) sm.dgc[16 * w + l16] = rs;
+  __syncthreads();  // slice tiles are free: the C x C gradient tiles take their place
+
+  // zero the C x C gradient tiles (their zero blocks are never written)
+  for (int i = tid; i < 4 * C * CTP / 4; i += NT) *reinterpret_cast<u32x2*>(&cc.dM[4 * i]) = u32x2{0u, 0u};
+  __syncthreads();
+  // dP, dT: masks; dbeta from T = X Diag(b); dM = dT Diag(b)
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int j = w + NW * m;
+    if (j < 20) {
+      int I, J;
+      lower_tile(j % 10, I, J);
+      f32x4 x = cacc[m];
+      if (I == J) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = l16 <= 4 * kg + i ? x[i] : 0.f;
+      }
+      if (j < 10) {
+        st_acc<CTP>(cc.dP, 16 * I, 16 * J, x, ident, l16, kg);
+      } else {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * I + 4 * kg + i;
+          part += x[i] * (float)ft.x[r * CTP + swz(r, 16 * J + l16)];
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (kg == 0) sm.dbt[I][16 * J + l16] = part;
+        st_acc<CTP>(cc.dM, 16 * I, 16 * J, x * ft.beta[16 * J + l16], ident, l16, kg);
+      }
+    }
+  }
+  __syncthreads();
+  // Y = X^T dM
+  for (int j = w; j < 16; j += NW) {
+    const int I = j >> 2, J = j & 3, mx = I > J ? I : J;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (32 * s + 31 >= 16 * mx)
+        acc = F::mma(F::ld_tr<CTP>(ft.x, 16 * I, s, l16, kg), F::ld_tr<CTP>(cc.dM, 16 * J, s, l16, kg), acc);
+    st_acc<CTP>(cc.Y, 16 * I, 16 * J, acc, ident, l16, kg);
+  }
+  __syncthreads();
+  // dA = -strict_lower(Y X^T); dbeta from A = Diag(b) B; dB = Diag(b) dA
+  for (int j = w; j < 10; j += NW) {
+    int I, J;
+    lower_tile(j, I, J);
+    f32x4 acc = zero4(), bm = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (32 * s <= 16 * J + 15)
+        acc = F::mma(ld_row<CTP>(cc.Y, 16 * I + l16, s, kg), ld_row<CTP>(ft.x, 16 * J + l16, s, kg), acc);
+#pragma unroll
+    for (int s = 0; s < SK; ++s)
+      bm = F::mma(ld_row<KHP>(ft.kt, 16 * I + l16, s, kg), ld_row<KHP>(ft.kh, 16 * J + l16, s, kg), bm);
+    f32x4 dA = -acc;
+    if (I == J) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dA[i] = l16 < 4 * kg + i ? dA[i] : 0.f;
+    }
+    f32x4 pr = dA * bm;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] += __shfl_xor(pr[i], o);
+    if (l16 == 0) *reinterpret_cast<f32x4*>(&sm.dba[J][16 * I + 4 * kg]) = pr;
+    const f32x4 br = *reinterpret_cast<const f32x4*>(&ft.beta[16 * I + 4 * kg]);
+    st_acc<CTP>(cc.dB, 16 * I, 16 * J, dA * br, ident, l16, kg);
+  }
+  __syncthreads();
+  // the [DK][C] results of wave w
+  f32x4 dKtT[4], dKhT[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    dKtT[tt] = -SdR[tt];
+    dKhT[tt] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const FV khT = F::ld_tr<KHP>(ft.kh, 16 * w, s, l16, kg);
+      dQtT[tt] = F::mma(khT, ld_row<CTP>(cc.dP, 16 * tt + l16, s, kg), dQtT[tt]);
+      dKtT[tt] = F::mma(khT, ld_row<CTP>(cc.dB, 16 * tt + l16, s, kg), dKtT[tt]);
+      dKhT[tt] = F::mma(F::ld_tr<KHP>(ft.kt, 16 * w, s, l16, kg), F::ld_tr<CTP>(cc.dB, 16 * tt, s, l16, kg), dKhT[tt]);
+      dKhT[tt] = F::mma(F::ld_tr<KHP>(ft.qt, 16 * w, s, l16, kg), F::ld_tr<CTP>(cc.dP, 16 * tt, s, l16, kg), dKhT[tt]);
+    }
+  }
+  __syncthreads();  // every tile is consumed: the final stage reuses the space
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int r = 16 * tt + l16, c0 = 16 * w + 4 * kg;
+    *reinterpret_cast<f32x4*>(&sm.fin[0][r][c0]) = dQtT[tt];
+    *reinterpret_cast<f32x4*>(&sm.fin[1][r][c0]) = dKtT[tt];
+    *reinterpret_cast<f32x4*>(&sm.fin[2][r][c0]) = dKhT[tt];
+    *reinterpret_cast<f32x4*>(&sm.fin[3][r][c0]) = dKbT[tt];
+  }
+  __syncthreads();
+
+  // ---- final stage: thread = (key channel, block of 16 tokens) ----
+  const int ch = tid % DK, tb = tid / DK;
+  const int rsk = H * DK * 2, rsg = H * (DK / GG) * 2, rsb = H * 2;
+  const rsrc_t bq = make_rsrc(A.q + row0 * DK, (nv - 1) * rsk + DK * 2);
+  const rsrc_t bk = make_rsrc(A.k + row0 * DK, (nv - 1) * rsk + DK * 2);
+  const rsrc_t bdq = make_rsrc(A.dq + row0 * DK, (nv - 1) * rsk + DK * 2);
+  const rsrc_t bdk = make_rsrc(A.dk + row0 * DK, (nv - 1) * rsk + DK * 2);
+  const rsrc_t bdg = make_rsrc(A.dg + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * 2);
+  float dG[TB];
+  float skb = 0.f;
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int r = tb * TB + j;
+    const float dqt = sm.fin[0][r][ch], dkt = sm.fin[1][r][ch], dkb = sm.fin[3][r][ch];
+    const float dkh = sm.fin[2][r][ch] + dkb;
+    const float eg = fast_exp2(G2[j]), emg = fast_exp2(-G2[j]);
+    const float q = to_f32(bload<bf16>(bq, r * rsk + ch * 2));
+    const float kk = to_f32(bload<bf16>(bk, r * rsk + ch * 2));
+    const float dq = dqt * eg, a = dkt * eg, b = dkh * emg;
+    dG[j] = q * dq + kk * (a - b);
+    skb += dkb * kk * emg;
+    bstore_bf16(dq, bdq, r * rsk + ch * 2);
+    bstore_bf16(a + b, bdk, r * rsk + ch * 2);
+  }
+  // reverse cumulative sum over the chunk; the chunk-total terms enter at
+  // the last row and so reach every row
+  float suf = 0.f;
+#pragma unroll
+  for (int j = TB - 1; j >= 0; --j) {
+    suf += dG[j];
+    dG[j] = suf;
+  }
+  sm.bsum[tb][ch] = skb;
+  __syncthreads();
+  float later = sm.dgc[ch];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) later += sm.bsum[b][ch];
+  __syncthreads();
+  sm.bsum[tb][ch] = suf;
+  __syncthreads();
+  for (int b = tb + 1; b < NB; ++b) later += sm.bsum[b][ch];
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int r = tb * TB + j;
+    float x = dG[j] + later;
+    if constexpr (GG == 1) {
+      bstore_bf16(x, bdg, r * rsg + ch * 2);
+    } else {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+      if (lane == 0) bstore_bf16(x, bdg, r * rsg + (ch / GG) * 2);
+    }
+  }
+  if (tid < C) {
+    float db = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) db += sm.dbt[b][tid];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) db += sm.dba[b][tid];
+    const rsrc_t bdb = make_rsrc(A.dbeta + row0, (nv - 1) * rsb + 2);
+    bstore_bf16(db, bdb, tid * rsb);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int GG>
+static hipError_t launch_bwd_cfg(const BwdArgs& a, hipStream_t s) {
+  typedef BwdCfg<DK, DV, GG> Cfg;
+  const long long grid = (long long)a.slots * a.H;
+  if (grid > 0) {
+    hipLaunchKernelGGL(chunk_bwd_prep_kernel<Cfg>, dim3((unsigned)grid), dim3(Cfg::NT), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int units = a.N * a.H;
+  if (units > 0) {
+    const int grid2 = (units + 7) / 8 * 8 * (DV / 64);
+    hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, DV>), dim3(grid2), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (grid > 0) {
+    hipLaunchKernelGGL(chunk_bwd_local_kernel<Cfg>, dim3((unsigned)grid), dim3(Cfg::NT), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <int GG>
+static hipError_t launch_bwd_g(int Dk, int Dv, const BwdArgs& a, hipStream_t s) {
+  if (Dk == 64 && Dv == 64) return launch_bwd_cfg<64, 64, GG>(a, s);
+  if (Dk == 64 && Dv == 128) return launch_bwd_cfg<64, 128, GG>(a, s);
+  if (Dk == 128 && Dv == 64) return launch_bwd_cfg<128, 64, GG>(a, s);
+  if (Dk == 128 && Dv == 128) return launch_bwd_cfg<128, 128, GG>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_bwd(int Dk, int Dv, int g_group, const BwdArgs& a, hipStream_t s) {
+  return g_group == 1 ? launch_bwd_g<1>(Dk, Dv, a, s) : launch_bwd_g<64>(Dk, Dv, a, s);
+}
+
+}  // namespace kda

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "kda_common.h"
+
 namespace kda {
 
 struct PrefillArgs {
@@ -20,8 +22,37 @@ struct PrefillArgs {
   int num_units;          // N * H
   int H;
   int T;                  // batch mode: tokens per sequence; varlen: total tokens
+  // Optional (bf16 path): the state entering every chunk, rounded to the
+  // operand type, row-major [slot][H][Dk][Dv]; chunk c of the sequence with
+  // first token t0 and index n uses slot (t0 / 64) + n + c.  NULL: not kept.
+  void* hs;
 };
 
+// Backward pass (bf16): inputs, gradients and the per-chunk workspaces.
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* g;
+  const bf16* beta;
+  const bf16* dout;
+  const float* dht;
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  bf16* dg;
+  bf16* dbeta;
+  float* dh0;
+  const int* cu_seqlens;
+  const int* order;
+  const bf16* hs;   // [slot][H][DK][DV]: state entering each chunk
+  bf16* fw;         // [slot][H]: F^T as MFMA A-operand fragments (DK x DK)
+  float* bw;        // [slot][H]: b in accumulator tiles (DK x DV)
+  bf16* dh;         // [slot][H][DK][DV]: cotangent of the state leaving each chunk
+  int N, H, T, slots;
+};
+
+hipError_t launch_chunk_bwd(int Dk, int Dv, int g_group, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream);
 hipError_t launch_decode_pool(bool bf16_io, bool bf16_state, int Dk, int Dv, int g_group, const void* q,

@@ -93,6 +93,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     len = args.T;
   }
   const int col0 = slice * VS;  // first value column of this slice
+  // chunk c of this sequence keeps its entering state in slot hs_slot0 + c
+  const int hs_slot0 = (tok0 >> 6) + seq;
   const int nchunks = (len + C - 1) / C;
 
   const T* __restrict__ gq = static_cast<const T*>(args.q);
@@ -478,9 +480,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
 #pragma unroll
           for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(UF[j][s], pb, O[j][t]);
         }
+        if (go) {
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
-          bstore4(O[j][t], bo, (16 * t + l16) * rsv + (16 * (TPW * bw + j) + 4 * kg) * (int)sizeof(T), T());
+          for (int j = 0; j < TPW; ++j)
+            bstore4(O[j][t], bo, (16 * t + l16) * rsv + (16 * (TPW * bw + j) + 4 * kg) * (int)sizeof(T), T());
+        }
       }
       // ---- S <- Diag(e^{G_C}) (S + Kh^T U) ----
 #pragma unroll
@@ -499,6 +503,17 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     lds_barrier();  // ------------------------------------------------------ Q
     if (i + 1 >= 0 && i + 1 < nchunks) {
       const int b = (i + 1) & 1;
+      // ---- optional: the state entering chunk i + 1, in the operand type
+      // (rows of four columns through an exact transposing product) ----
+      if (args.hs) {
+        E* hs = static_cast<E*>(args.hs) + ((size_t)(hs_slot0 + i + 1) * H + h) * DK * DV;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+          for (int mt = 0; mt < KT; ++mt)
+            store4<E>(hs + (size_t)(16 * mt + l16) * DV + col0 + 16 * (TPW * bw + j) + 4 * kg,
+                      Reg16<E>::prod(S[j][mt], ident));
+      }
       // ---- R = V - Kt S (V enters through an exact identity product) ----
       {
         FV SF[TPW][SK];  // -S as B-operand fragments

@@ -27,7 +27,10 @@ _STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
-EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_step_pool",
+# KDA_ABI_VERSION of include/kda.h that these bindings are written for.
+ABI_VERSION = 4
+
+EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_recurrent_step", "kda_recurrent_step_pool",
             "kda_short_conv_fwd", "kda_short_conv_step", "kda_status_str", "kda_abi_version"]
 
 _lib = None
@@ -58,6 +61,10 @@ def lib():
     L.kda_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_fwd.restype = i
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    L.kda_chunk_bwd_workspace_bytes.restype = sz
+    L.kda_chunk_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    L.kda_chunk_bwd.restype = i
+    L.kda_chunk_bwd.argtypes = [vp] * 14 + [vp, i, i, i, i, i, i, i, i, vp, sz, vp]
     L.kda_recurrent_step.restype = i
     L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.kda_recurrent_step_pool.restype = i
@@ -137,6 +144,56 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=False, cu
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd")
     return o, ht
+
+
+def bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, varlen, dtype):
+    """Bytes of device workspace chunk_bwd needs."""
+    return int(lib().kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, int(bool(varlen)),
+                                                   KDA_BF16 if dtype == torch.bfloat16 else KDA_F32))
+
+
+def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, workspace=None, out=None):
+    """Gradients of <do, o> + <dht, ht> for chunk_fwd(q, k, v, g, beta,
+    initial_state, cu_seqlens) (bf16 inputs).  Returns a dict with dq, dk,
+    dv, dg, dbeta (bf16, shaped like the inputs) and dh0 (float32
+    [N, H, Dk, Dv]).  `out` may hold preallocated tensors under those names."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
+        raise ValueError("g's last dim must divide Dk")
+    g_group = Dk // g.shape[-1]
+    dt = _dt(q)
+    for t in (k, v, g, beta, do):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, g, beta, do must share one dtype")
+    for t in (initial_state, dht):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("initial_state and dht must be float32")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _check_dev(q, k, v, g, beta, do, initial_state, dht, cu_seqlens)
+    out = dict(out or {})
+    for name, like in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta)):
+        if out.get(name) is None:
+            out[name] = torch.empty_like(like)
+    if out.get("dh0") is None:
+        out["dh0"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _check_dev(*out.values())
+    need = bwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, q.dtype)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(do),
+                             _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                             _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(cu_seqlens), N, B, T, H, Dk, Dv,
+                             g_group, dt, _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    if st != 0:
+        raise KdaError(st, "kda_chunk_bwd")
+    return out
 
 
 def recurrent_step(q, k, v, g, beta, state, out=None):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
   KDA_OK = 0,
@@ -94,6 +94,45 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B,
                          int T, int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace kda_chunk_bwd needs for these sizes: the
+ * per-chunk states and cotangents of the backward pass (64-token chunks of
+ * every sequence, dt = KDA_BF16), plus the varlen ordering table.  0 for
+ * invalid sizes. */
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs, int varlen,
+                                     kda_dtype dt);
+
+/* Backward pass of the chunked prefill (the miniKimiK3 card's KDA bullet:
+ * KDA trains through the chunked parallel form).  Returns the gradients of
+ * L = <do, o> + <dht, ht> for the forward kda_chunk_fwd(q, k, v, g, beta,
+ * h0, cu_seqlens, ...) would compute; the forward's states are recomputed
+ * internally, so o is not an input.
+ *
+ *   q, k, v, g, beta, h0, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group:
+ *          as for kda_chunk_fwd (same layouts, same chunk-decay domain).
+ *   dout   [B, T, H, Dv]   bf16  cotangent of o
+ *   dht    [N, H, Dk, Dv]  f32 or NULL (NULL = zero)  cotangent of ht
+ *   dq, dk [B, T, H, Dk]   bf16  gradients (every token written)
+ *   dv     [B, T, H, Dv]   bf16
+ *   dg     [B, T, H, Dk/g_group] bf16  (summed over a decay group)
+ *   dbeta  [B, T, H]       bf16
+ *   dh0    [N, H, Dk, Dv]  f32 or NULL: gradient of h0 (for a zero-length
+ *          document it is dht[n])
+ *   dt     KDA_BF16 only (KDA_F32 returns KDA_ERR_UNSUPPORTED).
+ *   workspace  device memory of at least kda_chunk_bwd_workspace_bytes(...)
+ *          bytes, 256-byte aligned; contents are scratch.
+ *
+ * Gradients of different documents never mix: with cu_seqlens, every
+ * gradient of document n depends only on document n's inputs and
+ * cotangents.  All pointers are caller-owned device memory; nothing is
+ * allocated.  Errors: as for kda_chunk_fwd, plus KDA_ERR_NULL for a missing
+ * gradient output when there are tokens.
+ */
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* h0, const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                         void* dg, void* dbeta, float* dh0, const int* cu_seqlens, int num_seqs, int B, int T,
+                         int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /* One recurrent decode step for N sequences x H heads (the recurrence of the
