@@ -157,6 +157,15 @@ def make_prefill(B, T, H, dk, dv, dtype="bf16", g_group=1, seed=0, decay="config
     return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0_t, cu_seqlens=cu, g_group=g_group)
 
 
+def make_cotangents(B, T, H, dk, dv, N, dtype="bf16", seed=0, state_std=0.02, final_state=True):
+    """Synthetic output cotangents for a backward pass: do [B,T,H,dv] ~ N(0, 1)
+    in `dtype` and, if final_state, dht [N,H,dk,dv] float32 ~ N(0, state_std^2)."""
+    rng = np.random.default_rng(seed)
+    do = _draw(rng, (B * T, H, dv), dtype).view(B, T, H, dv)
+    dht = _draw(rng, (N, H, dk, dv), "f32", lambda z: state_std * z) if final_state else None
+    return dict(do=do, dht=dht)
+
+
 def make_decode(N, H, dk, dv, steps, dtype="bf16", g_group=1, seed=0, state_std=0.02, decay="config"):
     """Synthetic decode run: initial fp32 state [N,H,dk,dv] ~ N(0, state_std^2)
     and `steps` per-step input dicts (q, k [N,H,dk]; v [N,H,dv]; g; beta)."""

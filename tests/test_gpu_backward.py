@@ -1,0 +1,216 @@
+"""Backward pass on the GPU (through the C-ABI) against the CPU fp64 oracle.
+
+Tolerance for the bf16 backward.  The pages state none for gradients, so it
+is derived from the arithmetic.
+* Every gradient is a short chain of products whose operands are rounded to
+  bf16 (relative error up to 2^-9 each) and accumulated in fp32.
+* The result itself is rounded to bf16.
+* About four such roundings give a relative L2 error of about 3.5e-3.
+* dg is a reverse cumulative sum of terms that partly cancel.  That raises
+  its relative error by the ratio of the summed magnitudes to the result,
+  about 2 to 3.
+
+Bound, per gradient tensor:
+* rel-L2 <= 1e-2 (dg: 2e-2);
+* max-abs <= 1e-2 * max|ref| (dg: 2e-2 * max|ref|).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.kda_oracle as orc
+from oracle.kda_backward import kda_backward
+from gated_delta_rule_04_amd import inputs, kda
+from tests._parity import errors, f64
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+REL = {"dg": 2e-2}
+MAXREL = {"dg": 2e-2}
+
+
+def check_grad(tag, name, got, ref):
+    got = f64(got)
+    assert np.all(np.isfinite(got)), "%s %s: non-finite" % (tag, name)
+    ma, rel = errors(got, ref)
+    scale = max(1.0, float(np.max(np.abs(ref)))) if ref.size else 1.0
+    print("PARITY %-34s %-6s max-abs %.3e (%.2e of max) rel-L2 %.3e" % (tag, name, ma, ma / scale, rel), flush=True)
+    assert rel <= REL.get(name, 1e-2), "%s %s: rel-L2 %.3e" % (tag, name, rel)
+    assert ma <= MAXREL.get(name, 1e-2) * scale, "%s %s: max-abs %.3e" % (tag, name, ma)
+
+
+def run_gpu(d, ct):
+    dev = lambda t: None if t is None else t.cuda()
+    out = kda.chunk_bwd(dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["g"]), dev(d["beta"]), dev(ct["do"]),
+                        initial_state=dev(d.get("h0")), dht=dev(ct.get("dht")), cu_seqlens=dev(d.get("cu_seqlens")))
+    torch.cuda.synchronize()
+    return {n: t.cpu() for n, t in out.items()}
+
+
+def run_oracle(d, ct):
+    cu = d.get("cu_seqlens")
+    return kda_backward(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(d["g"]), f64(d["beta"]), f64(ct["do"]),
+                        h0=None if d.get("h0") is None else f64(d["h0"]),
+                        dht=None if ct.get("dht") is None else f64(ct["dht"]),
+                        cu_seqlens=None if cu is None else cu.numpy(), g_group=d["g_group"])
+
+
+def case(B, T, H, dk, dv, gg=1, h0=True, dht=True, cu=None, seed=0, decay="config"):
+    N = B if cu is None else len(cu) - 1
+    d = inputs.make_prefill(B, T, H, dk, dv, "bf16", gg, seed=seed, h0=h0, cu_seqlens=cu, decay=decay)
+    ct = inputs.make_cotangents(B, T, H, dk, dv, N, "bf16", seed=seed + 1000, final_state=dht, state_std=1.0)
+    return d, ct
+
+
+def compare(tag, d, ct):
+    got = run_gpu(d, ct)
+    ref = run_oracle(d, ct)
+    for n in NAMES:
+        check_grad(tag, n, got[n], ref[n])
+    return got
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_head_sizes_ragged(dk, dv):
+    # several chunks and a ragged tail, two sequences, h0 and dht
+    d, ct = case(2, 201, 2, dk, dv, seed=dk + dv)
+    compare("B2 T201 H2 dk%d dv%d" % (dk, dv), d, ct)
+
+
+def test_single_chunk_no_states():
+    d, ct = case(1, 64, 1, 64, 64, h0=False, dht=False, seed=1)
+    compare("one chunk", d, ct)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 65, 127])
+def test_short_and_boundary_lengths(T):
+    # 32 heads, so that the whole-tensor criteria see a few dozen values even at T = 1
+    d, ct = case(1, T, 32, 128, 128, seed=T)
+    compare("T%d" % T, d, ct)
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_decay_groups_of_64(dk):
+    d, ct = case(1, 256, 2, dk, 128, gg=64, seed=7 + dk)
+    compare("g64 dk%d" % dk, d, ct)
+
+
+def test_g64_matches_expanded_decay():
+    """Compact g64 gives the group sums of the expanded run's dg, and the
+    same other gradients (up to the bf16 rounding of the summed dg)."""
+    d, ct = case(1, 190, 2, 128, 128, gg=64, seed=21)
+    e = dict(d)
+    e["g"] = d["g"].repeat_interleave(64, dim=-1).contiguous()
+    e["g_group"] = 1
+    a, b = run_gpu(d, ct), run_gpu(e, ct)
+    for n in ("dq", "dk", "dv", "dbeta", "dh0"):
+        assert torch.equal(a[n], b[n]), n
+    summed = f64(b["dg"]).reshape(1, 190, 2, 2, 64).sum(-1)
+    ma, rel = errors(f64(a["dg"]), summed)
+    assert rel <= 1e-2, rel
+
+
+def test_packed_documents():
+    cu = [0, 50, 50, 51, 180, 300]  # an empty document and a one-token one
+    d, ct = case(1, 300, 2, 128, 128, cu=cu, seed=31)
+    compare("varlen", d, ct)
+
+
+def test_packed_documents_have_zero_cross_gradient():
+    """Perturbing one document's inputs and cotangents leaves every gradient
+    of the other documents bitwise unchanged."""
+    cu = [0, 70, 70, 200, 333]
+    d, ct = case(1, 333, 2, 128, 64, cu=cu, seed=41)
+    a = run_gpu(d, ct)
+    d2 = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ct2 = {k: v.clone() for k, v in ct.items()}
+    sl = slice(70, 200)  # document 2
+    for n in ("q", "k", "v", "beta", "g"):
+        d2[n][:, sl] = d2[n][:, sl].flip(1)
+    ct2["do"][:, sl] = -ct2["do"][:, sl]
+    d2["h0"][2] = -d2["h0"][2]
+    ct2["dht"][2] = 2 * ct2["dht"][2]
+    b = run_gpu(d2, ct2)
+    keep = torch.ones(333, dtype=torch.bool)
+    keep[sl] = False
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert torch.equal(a[n][:, keep], b[n][:, keep]), n
+        assert not torch.equal(a[n][:, sl], b[n][:, sl]), n
+    for doc in (0, 1, 3):
+        assert torch.equal(a["dh0"][doc], b["dh0"][doc])
+
+
+def test_frozen_state_exact_zeros():
+    """alpha = 1, beta = 0: the state never changes, so dk = dv = 0 exactly;
+    dq, dbeta, dg, dh0 against the oracle (whose closed forms are pinned)."""
+    d, ct = case(1, 150, 2, 128, 128, seed=51, decay="none")
+    d["beta"].zero_()
+    got = run_gpu(d, ct)
+    assert torch.count_nonzero(got["dk"]) == 0 and torch.count_nonzero(got["dv"]) == 0
+    ref = run_oracle(d, ct)
+    for n in ("dq", "dbeta", "dg", "dh0"):
+        check_grad("frozen", n, got[n], ref[n])
+
+
+@pytest.mark.parametrize("which", ["do_only", "dht_only"])
+def test_each_cotangent_path(which):
+    """The output path and the final-state path separately: each one's
+    gradients are checked alone, so a wrong term in either cannot hide
+    behind the other."""
+    d, ct = case(1, 230, 2, 128, 128, seed=61)
+    if which == "do_only":
+        ct["dht"] = None
+    else:
+        ct["do"].zero_()
+    compare(which, d, ct)
+
+
+def test_empty_sequence_passes_dht_through():
+    d, ct = case(2, 0, 3, 64, 64, seed=71)
+    got = run_gpu(d, ct)
+    assert torch.equal(got["dh0"], ct["dht"])
+
+
+def test_deterministic():
+    d, ct = case(1, 300, 3, 128, 128, seed=81)
+    a, b = run_gpu(d, ct), run_gpu(d, ct)
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_forward_unchanged_by_state_keeping():
+    """The backward's internal forward writes chunk states only: a forward
+    call after it still matches the oracle (and the forward output path is
+    independent of that option)."""
+    d, ct = case(1, 200, 2, 128, 128, seed=91)
+    run_gpu(d, ct)
+    dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else v) for n, v in d.items()}
+    o, ht = kda.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], initial_state=dev["h0"],
+                          output_final_state=True)
+    o_ref, h_ref = orc.kda_forward(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(d["g"]), f64(d["beta"]),
+                                   h0=f64(d["h0"]))
+    assert errors(o.cpu(), o_ref)[1] <= 5e-3 and errors(ht.cpu(), h_ref)[1] <= 5e-3
+
+
+def test_kimi_k3_heads_last_window():
+    """At the bench's prefill shape (B=1, T=32768, H=96, dk=dv=128): the
+    gradients of the last 512 tokens of two sampled heads against the oracle
+    run on that window from the state that enters it (the forward oracle,
+    streamed) and the same dht; plus finiteness of every gradient."""
+    B, T, H, dk, dv = 1, 32768, 96, 128, 128
+    d, ct = case(B, T, H, dk, dv, seed=2024, h0=False)
+    got = run_gpu(d, ct)
+    for n in NAMES:
+        assert torch.isfinite(got[n]).all(), n
+    heads = [5, 77]
+    W = 512
+    sel = lambda t: f64(t[:, :, heads])
+    q, k, v, g, beta, do = (sel(x) for x in (d["q"], d["k"], d["v"], d["g"], d["beta"], ct["do"]))
+    _, h_mid = orc.kda_forward(q[:, :T - W], k[:, :T - W], v[:, :T - W], g[:, :T - W], beta[:, :T - W])
+    w = slice(T - W, T)
+    ref = kda_backward(q[:, w], k[:, w], v[:, w], g[:, w], beta[:, w], do[:, w], h0=h_mid,
+                       dht=f64(ct["dht"][:, heads]))
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        check_grad("K3 heads last 512", n, got[n][:, w][:, :, heads], ref[n])
