@@ -61,6 +61,16 @@ def alg_decode_pool(N, H, dk, dv, g_group, state_elem=2, elem=2):
     return N * H * per
 
 
+def alg_backward(B, T, H, dk, dv, g_group, N=None, elem=2):
+    """Algorithmic bytes of one backward call: per head-token q, k, v, g,
+    beta and do read, dq, dk, dv, dg, dbeta written (elem bytes each); per
+    (sequence, head) the fp32 dht read and dh0 written."""
+    N = B if N is None else N
+    per_in = elem * (2 * dk + dv + dk // g_group + 1 + dv)
+    per_out = elem * (2 * dk + dv + dk // g_group + 1)
+    return B * T * H * (per_in + per_out) + N * H * dk * dv * 8
+
+
 def sha256_files(paths):
     """sha256 of the concatenated contents of paths (in order)."""
     h = hashlib.sha256()
@@ -340,6 +350,37 @@ def main():
         "hbm_frac_alg": conv_bytes / (conv_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
     del xc, yc
+    # Backward pass of the prefill (outside the timed step): the same inputs,
+    # seeded cotangents of o and of the final state.
+    gb = torch.Generator().manual_seed(23)
+    dob = torch.randn((B, T, H, dv), generator=gb).to(torch.bfloat16).to(dev)
+    dhtb = torch.randn((B, H, dk, dv), generator=gb).to(dev)
+    wsb = torch.empty(kda.bwd_workspace_bytes(B, T, H, dk, dv, B, False, torch.bfloat16), dtype=torch.uint8,
+                      device=dev)
+    gout = None
+    for _ in range(args.warmup):
+        gout = kda.chunk_bwd(P["q"], P["k"], P["v"], P["g"], P["beta"], dob, dht=dhtb, workspace=wsb, out=gout)
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        bev[i][0].record()
+        gout = kda.chunk_bwd(P["q"], P["k"], P["v"], P["g"], P["beta"], dob, dht=dhtb, workspace=wsb, out=gout)
+        bev[i][1].record()
+    torch.cuda.synchronize()
+    bwd_ms = [e[0].elapsed_time(e[1]) for e in bev]
+    bwd_avg = mean(bwd_ms)
+    bwd_bytes = alg_backward(B, T, H, dk, dv, g_group)
+    line["chunk_bwd_bf16"] = {
+        "kernels": "chunk_fwd_pipe_kernel (keeping chunk states), chunk_bwd_prep_kernel, chunk_bwd_dh_kernel, "
+                   "chunk_bwd_local_kernel",
+        "config": {"B": B, "T": T, "H": H, "dk": dk, "dv": dv, "g_group": g_group, "dht": True},
+        "tokens_per_s": B * T / (bwd_avg * 1e-3),
+        "ms": bwd_avg,
+        "ms_min": min(bwd_ms),
+        "alg_bytes_per_call": bwd_bytes,
+        "hbm_frac_alg": bwd_bytes / (bwd_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "workspace_bytes": wsb.numel(),
+    }
+    del dob, dhtb, wsb, gout
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, dec)
     print(json.dumps(line), flush=True)

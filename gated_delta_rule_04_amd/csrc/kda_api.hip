@@ -212,7 +212,7 @@ bool bwd_layout(int B, int T, int H, int Dk, int Dv, int N, bool varlen, BwdLayo
   L.hs = L.order;
   L.fw = L.hs + align256(sh * Dk * Dv * 2);
   L.bw = L.fw + align256(sh * Dk * Dk * 2);
-  L.dh = L.bw + align256(sh * Dk * Dv * 4);
+  L.dh = L.bw + align256(sh * Dk * Dv * 2);
   L.total = L.dh + align256(sh * Dk * Dv * 2);
   return true;
 }
@@ -304,7 +304,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
   b.order = order;
   b.hs = reinterpret_cast<const kda::bf16*>(ws + L.hs);
   b.fw = reinterpret_cast<kda::bf16*>(ws + L.fw);
-  b.bw = reinterpret_cast<float*>(ws + L.bw);
+  b.bw = reinterpret_cast<kda::bf16*>(ws + L.bw);
   b.dh = reinterpret_cast<kda::bf16*>(ws + L.dh);
   b.N = N;
   b.H = H;

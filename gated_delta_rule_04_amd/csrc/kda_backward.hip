@@ -37,9 +37,10 @@
 // XOR-permuted by row / 4, so one copy serves both row reads and transposing
 // reads (ds_read_b64_tr_b16).  Step 4 walks the value columns in slices of 32
 // to stay inside the 160 KB of LDS per workgroup; everything that contracts
-// over the value axis accumulates in registers across the slices.  Step 3 is
-// the only recurrence: a short MFMA chain per chunk, with F staged through LDS
-// two chunks ahead.  The slot of chunk c of the sequence that starts at
+// over the value axis accumulates in registers across the slices; the next
+// slice's global loads are in flight while the current one is computed.
+// Step 3 is the only recurrence: a short MFMA chain per chunk, with F^T
+// staged through LDS one chunk ahead and b kept in bf16.  The slot of chunk c of the sequence that starts at
 // token t0 and has index n is (t0 / 64) + n + c, so the per-chunk buffers
 // need no prefix sum over the sequences.
 
@@ -201,6 +202,13 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
   const rsrc_t bk = make_rsrc(A.k + row0 * DK, (nv - 1) * rsk + DK * 2);
   const rsrc_t bg = make_rsrc(A.g + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * 2);
   const int ch = tid % DK, tb = tid / DK;
+  bf16 qv[TB], kv[TB];
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int r = tb * TB + j;
+    qv[j] = bload<bf16>(bq, r * rsk + ch * 2);
+    kv[j] = bload<bf16>(bk, r * rsk + ch * 2);
+  }
   {
     float acc = 0.f;
 #pragma unroll
@@ -223,8 +231,7 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
     for (int j = 0; j < TB; ++j) {
       G2[j] += off;
       const int r = tb * TB + j;
-      const float q = to_f32(bload<bf16>(bq, r * rsk + ch * 2));
-      const float kk = to_f32(bload<bf16>(bk, r * rsk + ch * 2));
+      const float q = to_f32(qv[j]), kk = to_f32(kv[j]);
       const float eg = fast_exp2(G2[j]), emg = fast_exp2(-G2[j]);
       const int o = r * KHP + swz(r, ch);
       ft.qt[o] = (bf16)(q * eg);
@@ -360,21 +367,29 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
   f32x4 ident;
 #pragma unroll
   for (int i = 0; i < 4; ++i) ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
-  float G2[Cfg::TB];
-  chunk_front<Cfg, false>(A, sq, h, c, sm.ft, sm.u.fs, G2, ident);
-
-  // dO of the chunk into LDS (swizzled token-major), 16-byte pieces
+  // dO of the chunk, 16-byte pieces, fetched before the front and stored to
+  // LDS (swizzled token-major) after it
+  constexpr int NP = C * DV / 8 / NT;
+  static_assert(NP * NT * 8 == C * DV, "dO pieces");
   const int nv = min(C, sq.len - c * C);
   const size_t row0 = (size_t)(sq.tok0 + c * C) * A.H + h;
   const int rsv = A.H * DV * 2;
+  u32x4 op[NP];
   {
     const rsrc_t bo = make_rsrc(A.dout + row0 * DV, (nv - 1) * rsv + DV * 2);
-    for (int p = tid; p < C * DV / 8; p += NT) {
-      const int r = p / (DV / 8), c8 = 8 * (p % (DV / 8));
-      const u32x4 x = bload<u32x4>(bo, r * rsv + c8 * 2);
-      *reinterpret_cast<u32x2*>(&sm.u.dO[r * DVP + swz(r, c8)]) = u32x2{x[0], x[1]};
-      *reinterpret_cast<u32x2*>(&sm.u.dO[r * DVP + swz(r, c8 + 4)]) = u32x2{x[2], x[3]};
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int p = tid + NT * j, r = p / (DV / 8), c8 = 8 * (p % (DV / 8));
+      op[j] = bload<u32x4>(bo, r * rsv + c8 * 2);
     }
+  }
+  float G2[Cfg::TB];
+  chunk_front<Cfg, false>(A, sq, h, c, sm.ft, sm.u.fs, G2, ident);
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int p = tid + NT * j, r = p / (DV / 8), c8 = 8 * (p % (DV / 8));
+    *reinterpret_cast<u32x2*>(&sm.u.dO[r * DVP + swz(r, c8)]) = u32x2{op[j][0], op[j][1]};
+    *reinterpret_cast<u32x2*>(&sm.u.dO[r * DVP + swz(r, c8 + 4)]) = u32x2{op[j][2], op[j][3]};
   }
 
   // W = T Kt (column tile w, all token tiles), Z = Qt - P W
@@ -418,28 +433,29 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
     for (int i = 0; i < 4; ++i) f[i] = gm[i] * ((16 * r + 4 * kg + i == 16 * w + l16 ? 1.f : 0.f) - acc[i]);
     store4<bf16>(fw + ((size_t)(w * KS + r / 2) * 64 + lane) * 8 + 4 * (r & 1), f);
   }
-  // b = Z^T dO, accumulator tiles [row tile w][column tile][lane][4]
-  float* bw = A.bw + uh * DK * DV;
+  // b = Z^T dO, bf16 accumulator tiles [row tile w][column tile][lane][4]
+  bf16* bw = A.bw + uh * DK * DV;
 #pragma unroll
   for (int ct = 0; ct < DV / 16; ++ct) {
     f32x4 acc = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s) acc = F::mma(F::acc2(Z[2 * s], Z[2 * s + 1]), F::ld_tr<DVP>(sm.u.dO, 16 * ct, s, l16, kg), acc);
-    *reinterpret_cast<f32x4*>(bw + ((size_t)(w * (DV / 16) + ct) * 64 + lane) * 4) = acc;
+    store4<bf16>(bw + ((size_t)(w * (DV / 16) + ct) * 64 + lane) * 4, acc);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Step 3: the reverse state pass, per (sequence, head, 64-column slice):
-// dS_in = F^T dS_out + b, chunk by chunk from the last.  Four wavefronts,
-// one 16-column tile each; F^T fragments are shared through LDS and fetched
-// two chunks ahead (registers, then LDS).
+// Step 3: the reverse state pass, per (sequence, head, 32-column slice):
+// dS_in = F^T dS_out + b, chunk by chunk from the last.  Two wavefronts, one
+// 16-column tile each; F^T fragments are shared through LDS and fetched one
+// chunk ahead (registers, then LDS); the slices of a head read F^T through
+// the same XCD's L2.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(BwdArgs A) {
-  constexpr int KS = DK / 32, KT = DK / 16, NS = DV / 64;
+__global__ __launch_bounds__(128) void chunk_bwd_dh_kernel(BwdArgs A) {
+  constexpr int KS = DK / 32, KT = DK / 16, NWD = 2, NTD = 64 * NWD, NS = DV / (16 * NWD);
   constexpr int FU = DK * DK / 8;     // 16-byte fragment units of F^T per chunk
-  constexpr int FPT = FU / 256;       // per thread
+  constexpr int FPT = FU / NTD;       // per thread
   __shared__ u32x4 fbuf[2][FU];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -452,7 +468,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(BwdArgs A) {
   const Seq sq = seq_info(A.cu_seqlens, n, A.T);
   const int nch = (sq.len + 63) / 64;
   const int slot0 = (sq.tok0 >> 6) + n;
-  const int ct = slice * 4 + w;  // this wave's 16-column tile
+  const int ct = slice * NWD + w;  // this wave's 16-column tile
   f32x4 ident;
 #pragma unroll
   for (int i = 0; i < 4; ++i) ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
@@ -468,21 +484,22 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(BwdArgs A) {
   auto fsrc = [&](int cc) { return reinterpret_cast<const u32x4*>(A.fw + ((size_t)(slot0 + cc) * A.H + h) * DK * DK); };
   auto bsrc = [&](int cc) { return A.bw + ((size_t)(slot0 + cc) * A.H + h) * DK * DV; };
   u32x4 fr[FPT];
-  f32x4 bn[KT], bc[KT];
+  bf16x4 bn[KT], bc[KT];
   auto load_f = [&](int cc) {
     const u32x4* p = fsrc(cc);
 #pragma unroll
-    for (int j = 0; j < FPT; ++j) fr[j] = __builtin_nontemporal_load(p + tid + 256 * j);
+    for (int j = 0; j < FPT; ++j) fr[j] = p[tid + NTD * j];
   };
-  auto load_b = [&](f32x4 (&dst)[KT], int cc) {
-    const float* p = bsrc(cc);
+  auto load_b = [&](bf16x4 (&dst)[KT], int cc) {
+    const bf16* p = bsrc(cc);
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
-      dst[mt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + ((size_t)(mt * (DV / 16) + ct) * 64 + lane) * 4));
+      dst[mt] = __builtin_bit_cast(bf16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+                                               p + ((size_t)(mt * (DV / 16) + ct) * 64 + lane) * 4)));
   };
   auto put_f = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < FPT; ++j) fbuf[buf][tid + 256 * j] = fr[j];
+    for (int j = 0; j < FPT; ++j) fbuf[buf][tid + NTD * j] = fr[j];
   };
 
   if (nch > 0) {
@@ -508,7 +525,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(BwdArgs A) {
     const u32x4* fb = fbuf[cc & 1];
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt) {
-      f32x4 acc = bc[mt];
+      f32x4 acc = {(float)bc[mt][0], (float)bc[mt][1], (float)bc[mt][2], (float)bc[mt][3]};
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = F::mma(__builtin_bit_cast(FV, fb[(mt * KS + s) * 64 + lane]), SF[s], acc);
       dS[mt] = acc;
@@ -591,12 +608,6 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     (&sm.dbt[0][0])[i] = 0.f;
     (&sm.dba[0][0])[i] = 0.f;
   }
-  float G2[TB];
-  FrontTiles<Cfg>& ft = sm.m.ft;
-  chunk_front<Cfg, true>(A, sq, h, c, ft, sm.m.u.fs, G2, ident);
-  auto& sl = sm.m.u.sl;
-  auto& cc = sm.m.u.cc;
-
   const int nv = min(C, sq.len - c * C);
   const size_t row0 = (size_t)(sq.tok0 + c * C) * H + h;
   const int rsv = H * DV * 2;
@@ -606,6 +617,34 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   const size_t uh = (size_t)slot * H + h;
   const bf16* hsS = A.hs + uh * DK * DV;
   const bf16* dhS = A.dh + uh * DK * DV;
+  // The next value slice is fetched into registers one slice ahead (the
+  // first one before the front): S and dS_out, one 8-element piece per
+  // thread; dO (first 4C threads); V rows of this wave's R tiles.
+  constexpr int NJ = 8 / NW;
+  const int pr = tid >> 2, pp8 = 8 * (tid & 3);
+  u32x4 s8, o8 = {0u, 0u, 0u, 0u};
+  bf16x8 d8;
+  bf16x4 vr[NJ];
+  auto load_slice = [&](int v0) {
+    s8 = *reinterpret_cast<const u32x4*>(hsS + (size_t)pr * DV + v0 + pp8);
+    d8 = *reinterpret_cast<const bf16x8*>(dhS + (size_t)pr * DV + v0 + pp8);
+    if (tid < 4 * C) o8 = bload<u32x4>(bo, pr * rsv + (v0 + pp8) * 2);
+  };
+  auto load_v = [&](int v0) {
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
+      vr[jj] = bload<bf16x4>(bv, (16 * tt + l16) * rsv + (v0 + 16 * ct + 4 * kg) * 2);
+    }
+  };
+  load_slice(0);
+  load_v(0);
+
+  float G2[TB];
+  FrontTiles<Cfg>& ft = sm.m.ft;
+  chunk_front<Cfg, true>(A, sq, h, c, ft, sm.m.u.fs, G2, ident);
+  auto& sl = sm.m.u.sl;
+  auto& cc = sm.m.u.cc;
 
   f32x4 cacc[MT];
 #pragma unroll
@@ -618,36 +657,36 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   for (int v0 = 0; v0 < DV; v0 += VSL) {
     __syncthreads();  // the front, or the previous slice, is done with the slice tiles
     {
-      // S and dSt: one 8-element piece per thread
-      const int r = tid >> 2, p8 = 8 * (tid & 3);
-      const u32x4 s8 = *reinterpret_cast<const u32x4*>(hsS + (size_t)r * DV + v0 + p8);
-      const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(dhS + (size_t)r * DV + v0 + p8);
+      // S and dSt = Diag(gam) dS_out; dO
+      const int r = pr, p8 = pp8;
       *reinterpret_cast<u32x2*>(&sl.S[r * SP + swz(r, p8)]) = u32x2{s8[0], s8[1]};
       *reinterpret_cast<u32x2*>(&sl.S[r * SP + swz(r, p8 + 4)]) = u32x2{s8[2], s8[3]};
       const float gm = ft.gam[r];
       store4<bf16>(&sl.dS[r * SP + swz(r, p8)], f32x4{(float)d8[0], (float)d8[1], (float)d8[2], (float)d8[3]} * gm);
       store4<bf16>(&sl.dS[r * SP + swz(r, p8 + 4)], f32x4{(float)d8[4], (float)d8[5], (float)d8[6], (float)d8[7]} * gm);
       if (tid < 4 * C) {
-        const u32x4 x = bload<u32x4>(bo, r * rsv + (v0 + p8) * 2);
-        *reinterpret_cast<u32x2*>(&sl.dO[r * SP + swz(r, p8)]) = u32x2{x[0], x[1]};
-        *reinterpret_cast<u32x2*>(&sl.dO[r * SP + swz(r, p8 + 4)]) = u32x2{x[2], x[3]};
+        *reinterpret_cast<u32x2*>(&sl.dO[r * SP + swz(r, p8)]) = u32x2{o8[0], o8[1]};
+        *reinterpret_cast<u32x2*>(&sl.dO[r * SP + swz(r, p8 + 4)]) = u32x2{o8[2], o8[3]};
       }
     }
+    if (v0 + VSL < DV) load_slice(v0 + VSL);
     __syncthreads();
     // R = V - Kt S
-    for (int job = w; job < 8; job += NW) {
-      const int tt = job >> 1, ct = job & 1;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < SK; ++s)
         acc = F::mma(ld_row<KHP>(ft.kt, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.S, 16 * ct, s, l16, kg), acc);
-      const bf16x4 vr = bload<bf16x4>(bv, (16 * tt + l16) * rsv + (v0 + 16 * ct + 4 * kg) * 2);
-      st_acc<SP>(sl.R, 16 * tt, 16 * ct, Reg16<bf16>::rows(vr, ident, -acc), ident, l16, kg);
+      st_acc<SP>(sl.R, 16 * tt, 16 * ct, Reg16<bf16>::rows(vr[jj], ident, -acc), ident, l16, kg);
     }
+    if (v0 + VSL < DV) load_v(v0 + VSL);
     __syncthreads();
     // U = T R;  dU = Kh dSt + P^T dO
-    for (int job = w; job < 8; job += NW) {
-      const int tt = job >> 1, ct = job & 1;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
       f32x4 u = zero4(), du = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -665,8 +704,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     }
     __syncthreads();
     // dR = T^T dU: the value gradient
-    for (int job = w; job < 8; job += NW) {
-      const int tt = job >> 1, ct = job & 1;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
       f32x4 dr = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -707,6 +747,20 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) rs += (float)a[i] * (float)b[i];
       }
+    }
+  }
+  // q, k of the final stage (thread = key channel, block of 16 tokens),
+  // fetched now so that the loads overlap the C x C stage
+  const int ch = tid % DK, tb = tid / DK;
+  const int rsk = H * DK * 2, rsg = H * (DK / GG) * 2, rsb = H * 2;
+  bf16 qf[TB], kf[TB];
+  {
+    const rsrc_t bq = make_rsrc(A.q + row0 * DK, (nv - 1) * rsk + DK * 2);
+    const rsrc_t bk = make_rsrc(A.k + row0 * DK, (nv - 1) * rsk + DK * 2);
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      qf[j] = bload<bf16>(bq, (tb * TB + j) * rsk + ch * 2);
+      kf[j] = bload<bf16>(bk, (tb * TB + j) * rsk + ch * 2);
     }
   }
   rs += __shfl_xor(rs, 16);
@@ -811,10 +865,6 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   __syncthreads();
 
   // ---- final stage: thread = (key channel, block of 16 tokens) ----
-  const int ch = tid % DK, tb = tid / DK;
-  const int rsk = H * DK * 2, rsg = H * (DK / GG) * 2, rsb = H * 2;
-  const rsrc_t bq = make_rsrc(A.q + row0 * DK, (nv - 1) * rsk + DK * 2);
-  const rsrc_t bk = make_rsrc(A.k + row0 * DK, (nv - 1) * rsk + DK * 2);
   const rsrc_t bdq = make_rsrc(A.dq + row0 * DK, (nv - 1) * rsk + DK * 2);
   const rsrc_t bdk = make_rsrc(A.dk + row0 * DK, (nv - 1) * rsk + DK * 2);
   const rsrc_t bdg = make_rsrc(A.dg + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * 2);
@@ -826,8 +876,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     const float dqt = sm.fin[0][r][ch], dkt = sm.fin[1][r][ch], dkb = sm.fin[3][r][ch];
     const float dkh = sm.fin[2][r][ch] + dkb;
     const float eg = fast_exp2(G2[j]), emg = fast_exp2(-G2[j]);
-    const float q = to_f32(bload<bf16>(bq, r * rsk + ch * 2));
-    const float kk = to_f32(bload<bf16>(bk, r * rsk + ch * 2));
+    const float q = to_f32(qf[j]), kk = to_f32(kf[j]);
     const float dq = dqt * eg, a = dkt * eg, b = dkh * emg;
     dG[j] = q * dq + kk * (a - b);
     skb += dkb * kk * emg;
@@ -888,8 +937,8 @@ static hipError_t launch_bwd_cfg(const BwdArgs& a, hipStream_t s) {
   }
   const int units = a.N * a.H;
   if (units > 0) {
-    const int grid2 = (units + 7) / 8 * 8 * (DV / 64);
-    hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, DV>), dim3(grid2), dim3(256), 0, s, a);
+    const int grid2 = (units + 7) / 8 * 8 * (DV / 32);
+    hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, DV>), dim3(grid2), dim3(128), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -47,7 +47,7 @@ struct BwdArgs {
   const int* order;
   const bf16* hs;   // [slot][H][DK][DV]: state entering each chunk
   bf16* fw;         // [slot][H]: F^T as MFMA A-operand fragments (DK x DK)
-  float* bw;        // [slot][H]: b in accumulator tiles (DK x DV)
+  bf16* bw;         // [slot][H]: b in accumulator tiles (DK x DV)
   bf16* dh;         // [slot][H][DK][DV]: cotangent of the state leaving each chunk
   int N, H, T, slots;
 };
