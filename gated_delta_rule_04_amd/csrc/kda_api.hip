@@ -64,10 +64,13 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
   return varlen ? varlen_workspace(num_seqs) : 0;
 }
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                         const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T,
-                         int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T,
+                          int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                          void* stream, const float* A_log, const float* dt_bias) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
   if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
   if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
@@ -115,9 +118,34 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
   a.H = H;
   a.T = T;
   a.hs = nullptr;
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
   const int vs = kda::prefill_slice_width(bf, Dk, Dv, units, device_cus());
   if (kda::launch_prefill(bf, Dk, Dv, g_group, vs, a, s) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T,
+                         int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return chunk_fwd_impl(q, k, v, g, beta, h0, o, ht, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group, dt, workspace,
+                        workspace_bytes, stream, nullptr, nullptr);
+}
+
+kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
+                                  const void* b_raw, const float* A_log, const float* dt_bias, const float* h0,
+                                  void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T, int H,
+                                  int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (H > 0 && (!A_log || !dt_bias)) return KDA_ERR_NULL;
+  return chunk_fwd_impl(q_raw, k_raw, v, f, b_raw, h0, o, ht, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group, dt,
+                        workspace, workspace_bytes, stream, A_log, dt_bias);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -131,6 +159,22 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
   if (kda::launch_decode(dt == KDA_BF16, Dk, Dv, g_group, q, k, v, g, beta, state, o, N * H,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_recurrent_step_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
+                                       const void* b_raw, const float* A_log, const float* dt_bias, float* state,
+                                       void* o, int N, int H, int Dk, int Dv, int g_group, kda_dtype dt,
+                                       void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
+  if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
+  if (!prod_fits({N, H}, INT_MAX)) return KDA_ERR_SHAPE;
+  if (N == 0) return KDA_OK;
+  if (!q_raw || !k_raw || !v || !f || !b_raw || !A_log || !dt_bias || !state || !o) return KDA_ERR_NULL;
+  if (kda::launch_decode_prologue(dt == KDA_BF16, Dk, Dv, g_group, q_raw, k_raw, v, f, b_raw, state, o, N, H, A_log,
+                                  dt_bias, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_HIP;
   return KDA_OK;
 }

@@ -29,5 +29,18 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNormEps = 1e-6f;  // guard of the prologue's L2 normalisation
+
+// Prologue activations (fp32).  softplus(x) = log(1 + e^x): x itself above
+// 15 and e^x below -15 (where the rounded forms are exact to fp32), else
+// through the hardware exp2 / log2.
+__device__ __forceinline__ float softplus_f(float x) {
+  if (x > 15.f) return x;
+  const float e = fast_exp2(x * kLog2e);
+  if (x < -15.f) return e;
+  return __builtin_amdgcn_logf(1.f + e) * kLn2;
+}
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + fast_exp2(-x * kLog2e)); }
 
 }  // namespace kda

@@ -28,6 +28,11 @@
 // notes, with the state dtype as a knob).  A slot outside the pool marks an
 // inactive sequence: its output row is zero and no state is touched.  A bf16
 // pool is widened to fp32 for the step and rounded to nearest even after it.
+//
+// Prologue form (PRO): q and k arrive raw and are L2-normalised here, g holds
+// the gate logits f (g = -exp(A_log) softplus(f + dt_bias)) and beta the
+// logits b (beta = sigmoid(b)).  The inverse norms enter as scalar factors of
+// the two reductions and of the write, so the state stream is unchanged.
 
 #include "kda_common.h"
 #include "kda_launch.h"
@@ -50,12 +55,13 @@ __device__ __forceinline__ void store_state4(bf16* p, const f32x4& x) {
   *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};  // RNE
 }
 
-template <int DK, int DV, typename T, int GG, typename SE>
+template <int DK, int DV, typename T, int GG, typename SE, bool PRO>
 __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                           const T* __restrict__ v, const T* __restrict__ g,
                                                           const T* __restrict__ beta, SE* __restrict__ state,
                                                           const int* __restrict__ slots, int num_slots, int H,
-                                                          T* __restrict__ o) {
+                                                          T* __restrict__ o, const float* __restrict__ A_log,
+                                                          const float* __restrict__ dt_bias) {
   constexpr int NT = 512;
   constexpr int CG = DV / 4;         // column groups of 4 floats
   constexpr int RG = NT / CG;        // row groups
@@ -66,7 +72,7 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
 
   __shared__ float s_q[DK], s_k[DK], s_a[DK];
   __shared__ float s_red[WAVES][2][DV];
-  __shared__ float s_qk;
+  __shared__ float s_qk, s_iq, s_ik;
 
   const int tid = threadIdx.x;
   const size_t u = blockIdx.x;  // (sequence, head) pair
@@ -99,15 +105,41 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
   if (tid < DK) {
     s_q[tid] = to_f32(q[u * DK + tid]);
     s_k[tid] = to_f32(k[u * DK + tid]);
-    s_a[tid] = fast_exp2(kLog2e * to_f32(g[u * (DK / GG) + tid / GG]));
+    float gx = to_f32(g[u * (DK / GG) + tid / GG]);
+    if constexpr (PRO) {
+      const int gi = (int)(u % H) * (DK / GG) + tid / GG;
+      gx = -fast_exp2(A_log[gi] * kLog2e) * softplus_f(gx + dt_bias[gi]);
+    }
+    s_a[tid] = fast_exp2(kLog2e * gx);
   }
   __syncthreads();
   if (wave == 0) {
-    float p = 0.f;
-    for (int i = lane; i < DK; i += kWave) p += s_q[i] * s_k[i];
+    float p = 0.f, sq = 0.f, sk = 0.f;
+    for (int i = lane; i < DK; i += kWave) {
+      p += s_q[i] * s_k[i];
+      if constexpr (PRO) {
+        sq += s_q[i] * s_q[i];
+        sk += s_k[i] * s_k[i];
+      }
+    }
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
-    if (lane == 0) s_qk = p;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      p += __shfl_xor(p, off);
+      if constexpr (PRO) {
+        sq += __shfl_xor(sq, off);
+        sk += __shfl_xor(sk, off);
+      }
+    }
+    if (lane == 0) {
+      float iq = 1.f, ik = 1.f;
+      if constexpr (PRO) {
+        iq = __builtin_amdgcn_rsqf(sq + kNormEps);
+        ik = __builtin_amdgcn_rsqf(sk + kNormEps);
+      }
+      s_iq = iq;
+      s_ik = ik;
+      s_qk = p * iq * ik;
+    }
   }
 
   // Decay in registers and accumulate the two partial column reductions.
@@ -147,7 +179,13 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
     }
   }
 
-  const float b = to_f32(beta[u]);
+  float b = to_f32(beta[u]);
+  if constexpr (PRO) {
+    b = sigmoid_f(b);
+    et *= s_ik;  // reductions against the raw q, k rescaled to the unit rows
+    yt *= s_iq;
+  }
+  const float kscale = PRO ? s_ik : 1.f;
   f32x4 vv;
 #pragma unroll
   for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[u * DV + 4 * cg + c]);
@@ -161,26 +199,38 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + RG * m;
-    store_state4(S + (size_t)r * DV + 4 * cg, s[m] + s_k[r] * uu);
+    store_state4(S + (size_t)r * DV + 4 * cg, s[m] + (s_k[r] * kscale) * uu);
   }
 }
+
+// Gate parameters of the prologue form (NULL A_log: the plain step).
+struct Prologue {
+  const float* A_log;
+  const float* dt_bias;
+};
 
 template <int DK, int DV, typename T, int GG, typename SE>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                   void* state, const int* slots, int num_slots, int H, void* o, int NH,
-                                  hipStream_t stream) {
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, GG, SE>), dim3(NH), dim3(512), 0, stream, (const T*)q,
-                     (const T*)k, (const T*)v, (const T*)g, (const T*)beta, (SE*)state, slots, num_slots, H, (T*)o);
+                                  hipStream_t stream, Prologue pro) {
+  if (pro.A_log)
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, GG, SE, true>), dim3(NH), dim3(512), 0, stream, (const T*)q,
+                       (const T*)k, (const T*)v, (const T*)g, (const T*)beta, (SE*)state, slots, num_slots, H,
+                       (T*)o, pro.A_log, pro.dt_bias);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, GG, SE, false>), dim3(NH), dim3(512), 0, stream, (const T*)q,
+                       (const T*)k, (const T*)v, (const T*)g, (const T*)beta, (SE*)state, slots, num_slots, H,
+                       (T*)o, nullptr, nullptr);
   return hipGetLastError();
 }
 
 template <typename T, int GG, typename SE>
 static hipError_t launch_decode_g(int Dk, int Dv, const void* q, const void* k, const void* v, const void* g,
                                   const void* beta, void* state, const int* slots, int num_slots, int H, void* o,
-                                  int NH, hipStream_t stream) {
+                                  int NH, hipStream_t stream, Prologue pro) {
 #define KDA_DEC(DK_, DV_)      \
   if (Dk == DK_ && Dv == DV_) \
-    return launch_decode_t<DK_, DV_, T, GG, SE>(q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream);
+    return launch_decode_t<DK_, DV_, T, GG, SE>(q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro);
   KDA_DEC(64, 64)
   KDA_DEC(64, 128)
   KDA_DEC(128, 64)
@@ -192,19 +242,26 @@ static hipError_t launch_decode_g(int Dk, int Dv, const void* q, const void* k, 
 template <typename SE>
 static hipError_t launch_decode_s(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k,
                                   const void* v, const void* g, const void* beta, void* state, const int* slots,
-                                  int num_slots, int H, void* o, int NH, hipStream_t stream) {
+                                  int num_slots, int H, void* o, int NH, hipStream_t stream, Prologue pro = {}) {
   if (bf16_io)
     return g_group == 1
-               ? launch_decode_g<bf16, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream)
-               : launch_decode_g<bf16, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream);
+               ? launch_decode_g<bf16, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro)
+               : launch_decode_g<bf16, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro);
   return g_group == 1
-             ? launch_decode_g<float, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream)
-             : launch_decode_g<float, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream);
+             ? launch_decode_g<float, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro)
+             : launch_decode_g<float, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro);
 }
 
 hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream) {
   return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, state, nullptr, 0, 1, o, NH, stream);
+}
+
+hipError_t launch_decode_prologue(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k,
+                                  const void* v, const void* g, const void* beta, float* state, void* o, int N, int H,
+                                  const float* A_log, const float* dt_bias, hipStream_t stream) {
+  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, state, nullptr, 0, H, o, N * H, stream,
+                                Prologue{A_log, dt_bias});
 }
 
 hipError_t launch_decode_pool(bool bf16_io, bool bf16_state, int Dk, int Dv, int g_group, const void* q,

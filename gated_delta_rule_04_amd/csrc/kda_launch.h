@@ -25,7 +25,13 @@ struct PrefillArgs {
   // Optional (bf16 path): the state entering every chunk, rounded to the
   // operand type, row-major [slot][H][Dk][Dv]; chunk c of the sequence with
   // first token t0 and index n uses slot (t0 / 64) + n + c.  NULL: not kept.
-  void* hs;
+  void* hs = nullptr;
+  // Optional (bf16 path): the fused gate and normalisation prologue.  When
+  // A_log is set, q and k are raw (L2-normalised per token in the kernel),
+  // g holds the gate logits f (g = -exp(A_log) softplus(f + dt_bias)) and
+  // beta the logits b (beta = sigmoid(b)); A_log, dt_bias: [H][Dk / g_group].
+  const float* A_log = nullptr;
+  const float* dt_bias = nullptr;
 };
 
 // Backward pass (bf16): inputs, gradients and the per-chunk workspaces.
@@ -55,6 +61,9 @@ struct BwdArgs {
 hipError_t launch_chunk_bwd(int Dk, int Dv, int g_group, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream);
+hipError_t launch_decode_prologue(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k,
+                                  const void* v, const void* g, const void* beta, float* state, void* o, int N, int H,
+                                  const float* A_log, const float* dt_bias, hipStream_t stream);
 hipError_t launch_decode_pool(bool bf16_io, bool bf16_state, int Dk, int Dv, int g_group, const void* q,
                               const void* k, const void* v, const void* g, const void* beta, void* pool,
                               const int* slots, int num_slots, int H, void* o, int NH, hipStream_t stream);

@@ -49,7 +49,7 @@ struct PipeSmem {
   alignas(16) float gsum[Cfg::NPW][Cfg::DK];  // per-wavefront log2-decay totals
 };
 
-template <class Cfg>
+template <class Cfg, bool PRO>
 __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs args) {
   typedef typename Cfg::T T;
   typedef typename Cfg::E E;
@@ -153,6 +153,17 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     const int rsk = H * DK * (int)sizeof(T);         // token stride of q, k (bytes)
     const int rsg = H * (DK / GG) * (int)sizeof(T);  // token stride of g
     const int rsb = H * (int)sizeof(T);              // token stride of beta
+    // prologue: exp(A_log) and dt_bias of this thread's channels (or group)
+    constexpr int NGC = PRO ? (GG == 1 ? 8 : 1) : 1;
+    float gA[NGC], gD[NGC];
+    if constexpr (PRO) {
+#pragma unroll
+      for (int c = 0; c < NGC; ++c) {
+        const int gi = h * (DK / GG) + (GG == 1 ? ch + c : ch / GG);
+        gA[c] = fast_exp2(args.A_log[gi] * kLog2e);
+        gD[c] = args.dt_bias[gi];
+      }
+    }
     auto chunk_rows = [&](int ck) { return min(C, len - ck * C); };
     auto chunk_row0 = [&](int ck) { return (size_t)(tok0 + ck * C) * H + h; };
     auto load_gb = [&](int ck) {  // g, beta
@@ -311,11 +322,24 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         float acc[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+        // rows past the end of the sequence stay inert under the prologue too:
+        // their (zero) gate logits must not become a decay
+        const int nvG = chunk_rows(cG);
 #pragma unroll
         for (int j = 0; j < RPB; ++j) {
+          const bool live = !PRO || rb * RPB + j < nvG;
+          float grow = 0.f;  // decay-group gate of row j
+          if constexpr (GG != 1) {
+            grow = to_f32(rgs[j]);
+            if constexpr (PRO) grow = live ? -gA[0] * softplus_f(grow + gD[0]) : 0.f;
+          }
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            const float gx = GG == 1 ? elem(rg[j], c) : to_f32(rgs[j]);
+            float gx = grow;
+            if constexpr (GG == 1) {
+              gx = elem(rg[j], c);
+              if constexpr (PRO) gx = live ? -gA[c] * softplus_f(gx + gD[c]) : 0.f;
+            }
             acc[c] += gx * kLog2e;
             G[j][c] = acc[c];
           }
@@ -336,7 +360,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) off[c] -= acc[c];  // exclusive within the wavefront
-        if (tid < C) sm.beta[bG][tid] = to_f32(rbeta);
+        if (tid < C) sm.beta[bG][tid] = PRO ? (tid < nvG ? sigmoid_f(to_f32(rbeta)) : 0.f) : to_f32(rbeta);
         if (cG + 1 < nchunks) load_gb(cG + 1);  // prefetch (g, beta registers are free)
       }
       lds_barrier();  // ---------------------------------------------------- Q
@@ -365,6 +389,29 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
             off[c + 4] += b[c];
           }
         }
+        // prologue: inverse L2 norms of this thread's q and k rows (a row's
+        // channels are spread over CGN consecutive lanes)
+        float iq[RPB], ik[RPB];
+#pragma unroll
+        for (int j = 0; j < RPB; ++j) iq[j] = ik[j] = 1.f;
+        if constexpr (PRO) {
+#pragma unroll
+          for (int j = 0; j < RPB; ++j) {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              sq += elem(rq[j], c) * elem(rq[j], c);
+              sk += elem(rk[j], c) * elem(rk[j], c);
+            }
+#pragma unroll
+            for (int o = 1; o < CGN; o <<= 1) {
+              sq += __shfl_xor(sq, o);
+              sk += __shfl_xor(sk, o);
+            }
+            iq[j] = __builtin_amdgcn_rsqf(sq + kNormEps);
+            ik[j] = __builtin_amdgcn_rsqf(sk + kNormEps);
+          }
+        }
         // gated operands Qt, Kt, Kh (token-major)
         float eL[8];  // e^G of this thread's last row
 #pragma unroll
@@ -381,8 +428,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
           float qo[8], ko[8], ho[8];
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            const float kx = elem(rk[j], c);
-            qo[c] = elem(rq[j], c) * e[c];
+            const float kx = elem(rk[j], c) * ik[j];
+            qo[c] = elem(rq[j], c) * iq[j] * e[c];
             ko[c] = kx * e[c];
             ho[c] = kx * n[c];
           }
@@ -580,7 +627,10 @@ template <class Cfg>
 static hipError_t launch_pipe_cfg(const PrefillArgs& a, hipStream_t stream) {
   const int groups = (a.num_units + 7) / 8;
   const int grid = groups * 8 * Cfg::NS;
-  hipLaunchKernelGGL(chunk_fwd_pipe_kernel<Cfg>, dim3(grid), dim3(Cfg::NT), 0, stream, a);
+  if (a.A_log)
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<Cfg, true>), dim3(grid), dim3(Cfg::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<Cfg, false>), dim3(grid), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

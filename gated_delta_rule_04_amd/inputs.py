@@ -157,6 +157,35 @@ def make_prefill(B, T, H, dk, dv, dtype="bf16", g_group=1, seed=0, decay="config
     return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0_t, cu_seqlens=cu, g_group=g_group)
 
 
+def make_prologue(B, T, H, dk, dv, dtype="bf16", g_group=1, seed=0, h0=False, cu_seqlens=None, state_std=0.02,
+                  qk_scale=(0.25, 8.0)):
+    """Raw inputs of the fused gate/normalisation prologue.  q_raw, k_raw
+    [B,T,H,dk]: N(0,1) rows times a per-row scale drawn log-uniformly from
+    qk_scale (not normalised); v [B,T,H,dv] N(0,1); gate logits f
+    [B,T,H,dk//g_group] N(0,1); beta logits b_raw [B,T,H] N(0,1); A_log,
+    dt_bias [H, dk//g_group] float32 ~ N(0, 0.1^2) and N(-2, 0.1^2), so that
+    the gate reproduces the -softplus(z - 2) decay of the other workloads."""
+    rng = np.random.default_rng(seed)
+    rows = B * T
+    lo, hi = np.log(qk_scale[0]), np.log(qk_scale[1])
+    scaled = lambda z: z * np.exp(rng.uniform(lo, hi, z.shape[:-1] + (1,)))
+    q = _draw(rng, (rows, H, dk), dtype, scaled).view(B, T, H, dk)
+    k = _draw(rng, (rows, H, dk), dtype, scaled).view(B, T, H, dk)
+    v = _draw(rng, (rows, H, dv), dtype).view(B, T, H, dv)
+    b = _draw(rng, (rows, H), dtype).view(B, T, H)
+    f = _draw(rng, (rows, H, dk // g_group), dtype).view(B, T, H, dk // g_group)
+    A_log = torch.as_tensor(0.1 * rng.standard_normal((H, dk // g_group)), dtype=torch.float32)
+    dt_bias = torch.as_tensor(-2.0 + 0.1 * rng.standard_normal((H, dk // g_group)), dtype=torch.float32)
+    cu = None
+    N = B
+    if cu_seqlens is not None:
+        cu = torch.as_tensor(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.numel() - 1
+    h0_t = _draw(rng, (N, H, dk, dv), "f32", lambda z: state_std * z) if h0 else None
+    return dict(q_raw=q, k_raw=k, v=v, f=f, b_raw=b, A_log=A_log, dt_bias=dt_bias, h0=h0_t, cu_seqlens=cu,
+                g_group=g_group)
+
+
 def make_cotangents(B, T, H, dk, dv, N, dtype="bf16", seed=0, state_std=0.02, final_state=True):
     """Synthetic output cotangents for a backward pass: do [B,T,H,dv] ~ N(0, 1)
     in `dtype` and, if final_state, dht [N,H,dk,dv] float32 ~ N(0, state_std^2)."""

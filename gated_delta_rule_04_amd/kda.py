@@ -28,9 +28,9 @@ _STATUS = {
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
 # KDA_ABI_VERSION of include/kda.h that these bindings are written for.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
-EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_recurrent_step", "kda_recurrent_step_pool",
+EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_recurrent_step", "kda_recurrent_step_pool",
             "kda_short_conv_fwd", "kda_short_conv_step", "kda_status_str", "kda_abi_version"]
 
 _lib = None
@@ -61,6 +61,10 @@ def lib():
     L.kda_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_fwd.restype = i
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    L.kda_chunk_fwd_prologue.restype = i
+    L.kda_chunk_fwd_prologue.argtypes = [vp] * 11 + [i, i, i, i, i, i, i, i, vp, sz, vp]
+    L.kda_recurrent_step_prologue.restype = i
+    L.kda_recurrent_step_prologue.argtypes = [vp] * 9 + [i, i, i, i, i, i, vp]
     L.kda_chunk_bwd_workspace_bytes.restype = sz
     L.kda_chunk_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_bwd.restype = i
@@ -144,6 +148,81 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=False, cu
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd")
     return o, ht
+
+
+def _gate_params(A_log, dt_bias, H, n):
+    for t in (A_log, dt_bias):
+        if t.dtype != torch.float32 or tuple(t.shape) != (H, n):
+            raise TypeError("A_log and dt_bias must be float32 [H, Dk / g_group]")
+        if not t.is_contiguous():
+            raise ValueError("A_log and dt_bias must be contiguous")
+
+
+def chunk_fwd_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, initial_state=None, output_final_state=False,
+                       cu_seqlens=None, out=None, final_state=None, workspace=None):
+    """Chunked prefill with the fused prologue (bf16): q, k L2-normalised per
+    token, g = -exp(A_log) softplus(f + dt_bias), beta = sigmoid(b_raw), all
+    inside the kernel.  Returns (o, ht)."""
+    B, T, H, Dk = q_raw.shape
+    Dv = v.shape[-1]
+    if f.shape[-1] <= 0 or Dk % f.shape[-1]:
+        raise ValueError("f's last dim must divide Dk")
+    g_group = Dk // f.shape[-1]
+    dt = _dt(q_raw)
+    for t in (k_raw, v, f, b_raw):
+        if t.dtype != q_raw.dtype:
+            raise TypeError("q_raw, k_raw, v, f, b_raw must share one dtype")
+    _gate_params(A_log, dt_bias, H, f.shape[-1])
+    if initial_state is not None and initial_state.dtype != torch.float32:
+        raise TypeError("initial_state must be float32")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _check_dev(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, initial_state, cu_seqlens)
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=q_raw.dtype, device=q_raw.device)
+    ht = final_state
+    if output_final_state and ht is None:
+        ht = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q_raw.device)
+    _check_dev(o, ht)
+    need = workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, q_raw.dtype)
+    ws = workspace
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q_raw.device)
+    st = lib().kda_chunk_fwd_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(f), _ptr(b_raw), _ptr(A_log),
+                                      _ptr(dt_bias), _ptr(initial_state), _ptr(o), _ptr(ht), _ptr(cu_seqlens), N, B,
+                                      T, H, Dk, Dv, g_group, dt, _ptr(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_prologue")
+    return o, ht
+
+
+def recurrent_step_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, state, out=None):
+    """One decode step with the fused prologue; state [N, H, Dk, Dv] float32
+    updated in place.  Returns o [N, H, Dv]."""
+    N, H, Dk = q_raw.shape
+    Dv = v.shape[-1]
+    if f.shape[-1] <= 0 or Dk % f.shape[-1]:
+        raise ValueError("f's last dim must divide Dk")
+    g_group = Dk // f.shape[-1]
+    dt = _dt(q_raw)
+    for t in (k_raw, v, f, b_raw):
+        if t.dtype != q_raw.dtype:
+            raise TypeError("q_raw, k_raw, v, f, b_raw must share one dtype")
+    _gate_params(A_log, dt_bias, H, f.shape[-1])
+    if state.dtype != torch.float32:
+        raise TypeError("state must be float32")
+    o = out if out is not None else torch.empty((N, H, Dv), dtype=q_raw.dtype, device=q_raw.device)
+    _check_dev(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, state, o)
+    st = lib().kda_recurrent_step_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(f), _ptr(b_raw), _ptr(A_log),
+                                           _ptr(dt_bias), _ptr(state), _ptr(o), N, H, Dk, Dv, g_group, dt,
+                                           _stream())
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_step_prologue")
+    return o
 
 
 def bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, varlen, dtype):

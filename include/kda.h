@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
   KDA_OK = 0,
@@ -134,6 +134,41 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
                          void* dg, void* dbeta, float* dh0, const int* cu_seqlens, int num_seqs, int B, int T,
                          int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Chunked prefill with the fused gate and normalisation prologue.  The
+ * prologue turns a layer's raw projections into KDA's inputs inside the
+ * prefill kernel, so there is no separate elementwise pass over q, k and g:
+ *   q = q_raw / sqrt(|q_raw|^2 + 1e-6),  k likewise (per token and head);
+ *   g = -exp(A_log) * softplus(f + dt_bias)   (per key channel or group);
+ *   beta = sigmoid(b_raw).
+ * Sources: the configurations' per-token L2-normalised q and k; A_log and
+ * dt_bias as KDA's state controls (Kimi-K3-Tiny-L13 card, real weights
+ * section; Mini-K3-1H-mamba2 README, optimiser paragraph).  The gate formula
+ * itself is not on the pages; this is the Mamba-style reading.
+ *
+ *   q_raw, k_raw [B, T, H, Dk] dt; v [B, T, H, Dv] dt;
+ *   f      [B, T, H, Dk/g_group] dt  gate logits
+ *   b_raw  [B, T, H] dt              write-strength logits
+ *   A_log, dt_bias  [H, Dk/g_group] f32 (device)
+ *   everything else as for kda_chunk_fwd.
+ * dt = KDA_BF16 only (KDA_F32: KDA_ERR_UNSUPPORTED).  The chunk-decay domain
+ * of kda_chunk_fwd applies to the g the prologue produces.
+ */
+kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
+                                  const void* b_raw, const float* A_log, const float* dt_bias, const float* h0,
+                                  void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T, int H,
+                                  int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* One decode step with the same fused prologue (q_raw, k_raw [N, H, Dk];
+ * v [N, H, Dv]; f [N, H, Dk/g_group]; b_raw [N, H]; A_log, dt_bias
+ * [H, Dk/g_group] f32; state [N, H, Dk, Dv] f32 in place; o [N, H, Dv]).
+ * dt = KDA_F32 or KDA_BF16.  Errors as for kda_recurrent_step.
+ */
+kda_status kda_recurrent_step_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
+                                       const void* b_raw, const float* A_log, const float* dt_bias, float* state,
+                                       void* o, int N, int H, int Dk, int Dv, int g_group, kda_dtype dt,
+                                       void* stream);
 
 /* One recurrent decode step for N sequences x H heads (the recurrence of the
  * miniKimiK3 card's KDA bullet: constant cost per token), state in place.

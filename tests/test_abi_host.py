@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 4 == kda.ABI_VERSION
+    assert L.kda_abi_version() == 5 == kda.ABI_VERSION
     for s in range(7):
         assert L.kda_status_str(s).decode().startswith(("KDA_OK", "KDA_ERR"))
     assert L.kda_status_str(99)

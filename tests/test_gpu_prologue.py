@@ -1,0 +1,105 @@
+"""Fused gate/normalisation prologue on the GPU (through the C-ABI) against
+the CPU fp64 prologue oracle.  Tolerances are the forward's (o and final
+states): bf16 max-abs <= 2e-2 and rel-L2 <= 5e-3; fp32 max-abs <= 1e-4."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.prologue as pro
+from gated_delta_rule_04_amd import inputs, kda
+from tests._parity import assert_close, errors, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(t):
+    return None if t is None else t.cuda()
+
+
+def _gpu_chunk(d):
+    o, ht = kda.chunk_fwd_prologue(_dev(d["q_raw"]), _dev(d["k_raw"]), _dev(d["v"]), _dev(d["f"]),
+                                   _dev(d["b_raw"]), _dev(d["A_log"]), _dev(d["dt_bias"]),
+                                   initial_state=_dev(d["h0"]), output_final_state=True,
+                                   cu_seqlens=_dev(d["cu_seqlens"]))
+    torch.cuda.synchronize()
+    return o.cpu(), ht.cpu()
+
+
+def _oracle_chunk(d):
+    cu = d["cu_seqlens"]
+    return pro.kda_forward_prologue(f64(d["q_raw"]), f64(d["k_raw"]), f64(d["v"]), f64(d["f"]), f64(d["b_raw"]),
+                                    f64(d["A_log"]), f64(d["dt_bias"]),
+                                    h0=None if d["h0"] is None else f64(d["h0"]),
+                                    cu_seqlens=None if cu is None else cu.numpy(), g_group=d["g_group"])
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_chunk_prologue_head_sizes(dk, dv):
+    d = inputs.make_prologue(2, 200, 3, dk, dv, "bf16", seed=dk + dv, h0=True)
+    o, ht = _gpu_chunk(d)
+    o_ref, h_ref = _oracle_chunk(d)
+    assert_close("prologue dk%d dv%d o" % (dk, dv), o, o_ref, torch.bfloat16)
+    assert_close("prologue dk%d dv%d ht" % (dk, dv), ht, h_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_chunk_prologue_decay_groups(dk):
+    d = inputs.make_prologue(1, 300, 2, dk, 128, "bf16", g_group=64, seed=5 + dk)
+    o, ht = _gpu_chunk(d)
+    o_ref, h_ref = _oracle_chunk(d)
+    assert_close("prologue g64 dk%d o" % dk, o, o_ref, torch.bfloat16)
+    assert_close("prologue g64 dk%d ht" % dk, ht, h_ref, torch.bfloat16)
+
+
+def test_chunk_prologue_packed_documents():
+    cu = [0, 40, 40, 170, 400]
+    d = inputs.make_prologue(1, 400, 2, 128, 128, "bf16", seed=9, h0=True, cu_seqlens=cu)
+    o, ht = _gpu_chunk(d)
+    o_ref, h_ref = _oracle_chunk(d)
+    assert_close("prologue varlen o", o, o_ref, torch.bfloat16)
+    assert_close("prologue varlen ht", ht, h_ref, torch.bfloat16)
+
+
+def test_chunk_prologue_scale_invariance():
+    """Raw q scaled by 4 and k by 1/4 (exact in bf16): the normalised rows,
+    hence the outputs, are unchanged up to the normalisation guard."""
+    d = inputs.make_prologue(1, 256, 2, 128, 128, "bf16", seed=11, h0=True)
+    o1, h1 = _gpu_chunk(d)
+    e = dict(d)
+    e["q_raw"] = d["q_raw"] * 4
+    e["k_raw"] = d["k_raw"] * 0.25
+    o2, h2 = _gpu_chunk(e)
+    for a, b, n in ((o1, o2, "o"), (h1, h2, "ht")):
+        ma, rel = errors(a, b)
+        print("PARITY prologue scale invariance %s max-abs %.3e rel-L2 %.3e" % (n, ma, rel))
+        assert rel <= 2e-3, n
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gg", [1, 64])
+def test_decode_prologue(dtype, gg):
+    N, H, dk, dv = 5, 3, 128, 64
+    d = inputs.make_prologue(1, N, H, dk, dv, dtype, g_group=gg, seed=21 + gg)
+    squeeze = lambda t: t[0]
+    q, k, v, f, b = (squeeze(d[n]) for n in ("q_raw", "k_raw", "v", "f", "b_raw"))
+    rng = np.random.default_rng(3)
+    S0 = torch.as_tensor(0.02 * rng.standard_normal((N, H, dk, dv)), dtype=torch.float32)
+    state = S0.cuda()
+    states_ref = f64(S0)
+    for step in range(3):
+        o = kda.recurrent_step_prologue(_dev(q), _dev(k), _dev(v), _dev(f), _dev(b), _dev(d["A_log"]),
+                                        _dev(d["dt_bias"]), state)
+        torch.cuda.synchronize()
+        states_ref, o_ref = pro.kda_decode_step_prologue(states_ref, f64(q), f64(k), f64(v), f64(f), f64(b),
+                                                         f64(d["A_log"]), f64(d["dt_bias"]), g_group=gg)
+        dt = torch.float32 if dtype == "f32" else torch.bfloat16
+        assert_close("decode prologue %s g%d step %d o" % (dtype, gg, step), o.cpu(), o_ref, dt)
+        assert_close("decode prologue %s g%d step %d S" % (dtype, gg, step), state.cpu(), states_ref, dt)
+        q, k = k, q  # vary the next step's inputs
+
+
+def test_prologue_rejects_fp32_prefill():
+    d = inputs.make_prologue(1, 64, 1, 64, 64, "f32", seed=1)
+    with pytest.raises(kda.KdaError):
+        _gpu_chunk(d)
