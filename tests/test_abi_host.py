@@ -104,3 +104,47 @@ def test_recurrent_step_pool_validation():
     assert step(slots=None) == NULL
     assert step(pool=None) == NULL                    # a pool is required when num_slots > 0
     assert step(N=0, q=None, pool=None, slots=None) == OK
+
+
+def test_chunk_bwd_validation():
+    L = kda.lib()
+
+    def bwd(q=P, do=P, dq=P, dg=P, cu=None, N=1, B=1, T=64, H=1, Dk=64, Dv=64, gg=1, dt=1, ws=P, wsb=None):
+        if wsb is None:
+            wsb = L.kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, N, int(cu is not None), dt)
+        return L.kda_chunk_bwd(q, P, P, P, P, None, do, None, dq, P, P, dg, P, None, cu, N, B, T, H, Dk, Dv, gg, dt,
+                               ws, wsb, None)
+
+    assert bwd(dt=7) == DTYPE
+    assert bwd(T=-1) == SHAPE
+    assert bwd(Dk=96) == UNSUPPORTED
+    assert bwd(dt=0) == UNSUPPORTED                   # the backward is bf16 only
+    assert bwd(N=2, B=1) == SHAPE
+    assert bwd(cu=P, B=2, N=2) == SHAPE
+    assert bwd(do=None) == NULL
+    assert bwd(dq=None) == NULL
+    assert bwd(dg=None) == NULL
+    need = L.kda_chunk_bwd_workspace_bytes(1, 64, 1, 64, 64, 1, 0, 1)
+    # chunk states, F^T, b and the state cotangents for (64/64 + 1 + 1) slots
+    assert need >= 3 * (64 * 64 * 2 * 4)
+    assert bwd(wsb=need - 1) == WORKSPACE
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(ws=ctypes.c_void_p(0x1008)) == WORKSPACE  # not 256-byte aligned
+    assert L.kda_chunk_bwd_workspace_bytes(1, -1, 1, 64, 64, 1, 0, 1) == 0
+
+
+def test_prologue_validation():
+    L = kda.lib()
+    pf = lambda dt=1, A=P, Dk=64: L.kda_chunk_fwd_prologue(P, P, P, P, P, A, P, None, P, None, None, 1, 1, 64, 1, Dk,
+                                                           64, 1, dt, None, 0, None)
+    assert pf(dt=9) == DTYPE
+    assert pf(dt=0) == UNSUPPORTED                    # the fused prefill prologue is bf16 only
+    assert pf(A=None) == NULL
+    assert pf(Dk=32) == UNSUPPORTED
+    ps = lambda dt=1, A=P, N=1, H=1, q=P: L.kda_recurrent_step_prologue(q, P, P, P, P, A, P, P, P, N, H, 64, 64, 1,
+                                                                        dt, None)
+    assert ps(dt=9) == DTYPE
+    assert ps(H=0) == SHAPE
+    assert ps(A=None) == NULL
+    assert ps(q=None) == NULL
+    assert ps(N=0, q=None, A=None) == OK
