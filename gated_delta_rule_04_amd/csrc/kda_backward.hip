@@ -47,6 +47,10 @@
 #include "kda_prefill_common.h"
 #include "kda_launch.h"
 
+#ifndef KDA_BWD_DH_WAVES
+#define KDA_BWD_DH_WAVES 4  // wavefronts (16-column tiles) per reverse-state-pass workgroup
+#endif
+
 namespace kda {
 
 namespace {
@@ -445,17 +449,21 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Step 3: the reverse state pass, per (sequence, head, 32-column slice):
-// dS_in = F^T dS_out + b, chunk by chunk from the last.  Two wavefronts, one
-// 16-column tile each; F^T fragments are shared through LDS and fetched one
-// chunk ahead (registers, then LDS); the slices of a head read F^T through
-// the same XCD's L2.
+// Step 3: the reverse state pass, per (sequence, head, 16*NWD-column slice;
+// NWD = 4):
+// dS_in = F^T dS_out + b, chunk by chunk from the last.  NWD wavefronts, one
+// 16-column tile each.  F^T fragments are shared through LDS (double
+// buffered); the loads of chunk c - 2 are issued while chunk c is computed,
+// into two register stages that alternate (the loop is unrolled by two), so
+// each load has two iterations to land.  The slices of a head read F^T
+// through the same XCD's L2.
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
-__global__ __launch_bounds__(128) void chunk_bwd_dh_kernel(BwdArgs A) {
-  constexpr int KS = DK / 32, KT = DK / 16, NWD = 2, NTD = 64 * NWD, NS = DV / (16 * NWD);
+template <int DK, int DV, int NWD>
+__global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
+  constexpr int KS = DK / 32, KT = DK / 16, NTD = 64 * NWD, NS = DV / (16 * NWD);
   constexpr int FU = DK * DK / 8;     // 16-byte fragment units of F^T per chunk
   constexpr int FPT = FU / NTD;       // per thread
+  static_assert(FPT * NTD == FU && NS * 16 * NWD == DV, "dh geometry");
   __shared__ u32x4 fbuf[2][FU];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -481,44 +489,32 @@ __global__ __launch_bounds__(128) void chunk_bwd_dh_kernel(BwdArgs A) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[mt][i] = d ? d[(size_t)(16 * mt + 4 * kg + i) * DV + 16 * ct + l16] : 0.f;
   }
-  auto fsrc = [&](int cc) { return reinterpret_cast<const u32x4*>(A.fw + ((size_t)(slot0 + cc) * A.H + h) * DK * DK); };
-  auto bsrc = [&](int cc) { return A.bw + ((size_t)(slot0 + cc) * A.H + h) * DK * DV; };
-  u32x4 fr[FPT];
-  bf16x4 bn[KT], bc[KT];
-  auto load_f = [&](int cc) {
-    const u32x4* p = fsrc(cc);
+  auto load_f = [&](u32x4 (&dst)[FPT], int cc) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(A.fw + ((size_t)(slot0 + cc) * A.H + h) * DK * DK);
 #pragma unroll
-    for (int j = 0; j < FPT; ++j) fr[j] = p[tid + NTD * j];
+    for (int j = 0; j < FPT; ++j) dst[j] = p[tid + NTD * j];
   };
   auto load_b = [&](bf16x4 (&dst)[KT], int cc) {
-    const bf16* p = bsrc(cc);
+    const bf16* p = A.bw + ((size_t)(slot0 + cc) * A.H + h) * DK * DV;
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
       dst[mt] = __builtin_bit_cast(bf16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
                                                p + ((size_t)(mt * (DV / 16) + ct) * 64 + lane) * 4)));
   };
-  auto put_f = [&](int buf) {
+  auto put_f = [&](const u32x4 (&src)[FPT], int buf) {
 #pragma unroll
-    for (int j = 0; j < FPT; ++j) fbuf[buf][tid + NTD * j] = fr[j];
+    for (int j = 0; j < FPT; ++j) fbuf[buf][tid + NTD * j] = src[j];
   };
-
-  if (nch > 0) {
-    load_f(nch - 1);
-    load_b(bc, nch - 1);
-    put_f((nch - 1) & 1);
-    if (nch > 1) {
-      load_f(nch - 2);
-      load_b(bn, nch - 2);
-    }
-  }
-  for (int cc = nch - 1; cc >= 0; --cc) {
+  bf16x4 bc[KT];  // b of the chunk being computed
+  // one chunk: dS_out is kept, then dS_in = F^T dS_out + b; afterwards the
+  // next chunk's F^T goes to LDS from stage (fs, bs), which is then refilled
+  // with the chunk three below
+  auto step = [&](int cc, u32x4 (&fs)[FPT], bf16x4 (&bs)[KT]) {
     __syncthreads();  // F^T of chunk cc is in fbuf[cc & 1]
-    // keep dS_out of chunk cc (bf16 rows of four columns)
     bf16* dh = A.dh + ((size_t)(slot0 + cc) * A.H + h) * DK * DV;
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
       store4<bf16>(dh + (size_t)(16 * mt + l16) * DV + 16 * ct + 4 * kg, Reg16<bf16>::prod(dS[mt], ident));
-    // dS_in = F^T dS_out + b
     FV SF[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) SF[s] = F::acc2(dS[2 * s], dS[2 * s + 1]);
@@ -531,14 +527,35 @@ __global__ __launch_bounds__(128) void chunk_bwd_dh_kernel(BwdArgs A) {
       dS[mt] = acc;
     }
     if (cc >= 1) {
-      put_f((cc - 1) & 1);  // F^T of chunk cc - 1 (its buffer held chunk cc + 1)
+      put_f(fs, (cc - 1) & 1);  // its buffer held chunk cc + 1, done before this iteration's barrier
 #pragma unroll
-      for (int mt = 0; mt < KT; ++mt) bc[mt] = bn[mt];
-      if (cc >= 2) {
-        load_f(cc - 2);
-        load_b(bn, cc - 2);
+      for (int mt = 0; mt < KT; ++mt) bc[mt] = bs[mt];
+      if (cc >= 3) {
+        load_f(fs, cc - 3);
+        load_b(bs, cc - 3);
       }
     }
+  };
+
+  u32x4 fa[FPT], fb2[FPT];
+  bf16x4 ba[KT], bb[KT];
+  if (nch > 0) {
+    load_f(fa, nch - 1);
+    load_b(bc, nch - 1);
+    put_f(fa, (nch - 1) & 1);
+    if (nch > 1) {
+      load_f(fa, nch - 2);
+      load_b(ba, nch - 2);
+    }
+    if (nch > 2) {
+      load_f(fb2, nch - 3);
+      load_b(bb, nch - 3);
+    }
+  }
+  // stage a holds chunk nch - 2, stage b chunk nch - 3; they alternate
+  for (int cc = nch - 1; cc >= 0; cc -= 2) {
+    step(cc, fa, ba);
+    if (cc >= 1) step(cc - 1, fb2, bb);
   }
   // dh0 (fp32); for an empty sequence it is dht
   if (A.dh0) {
@@ -937,8 +954,9 @@ static hipError_t launch_bwd_cfg(const BwdArgs& a, hipStream_t s) {
   }
   const int units = a.N * a.H;
   if (units > 0) {
-    const int grid2 = (units + 7) / 8 * 8 * (DV / 32);
-    hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, DV>), dim3(grid2), dim3(128), 0, s, a);
+    constexpr int NWD = KDA_BWD_DH_WAVES;
+    const int grid2 = (units + 7) / 8 * 8 * (DV / (16 * NWD));
+    hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, DV, NWD>), dim3(grid2), dim3(64 * NWD), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
