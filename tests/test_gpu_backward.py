@@ -214,3 +214,31 @@ def test_kimi_k3_heads_last_window():
                        dht=f64(ct["dht"][:, heads]))
     for n in ("dq", "dk", "dv", "dg", "dbeta"):
         check_grad("K3 heads last 512", n, got[n][:, w][:, :, heads], ref[n])
+
+
+def test_packed_documents_workload_full_size():
+    """The packed-document workload at full size (65,536 tokens, 12 heads,
+    about 46 documents of 16..8192 tokens), with seeded cotangents and no
+    states.  Gradients never cross documents, so the oracle runs on whole
+    documents alone: the three shortest and the longest, on two heads."""
+    d = inputs.workload_prefill("varlen_bf16")
+    cu = d["cu_seqlens"].numpy()
+    N = len(cu) - 1
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    ct = inputs.make_cotangents(B, T, H, dk, dv, N, "bf16", seed=3003, final_state=True, state_std=1.0)
+    got = run_gpu(d, ct)
+    for n in NAMES:
+        assert torch.isfinite(got[n]).all(), n
+    lens = np.diff(cu)
+    docs = list(np.argsort(lens, kind="stable")[:3]) + [int(np.argmax(lens))]
+    heads = [3, 10]
+    for doc in docs:
+        a, b = int(cu[doc]), int(cu[doc + 1])
+        sel = lambda t: f64(t[:, a:b][:, :, heads])
+        ref = kda_backward(sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(d["g"]), sel(d["beta"]), sel(ct["do"]),
+                           dht=f64(ct["dht"][doc:doc + 1, heads]))
+        tag = "varlen doc %d (%d tokens)" % (doc, b - a)
+        for n in ("dq", "dk", "dv", "dg", "dbeta"):
+            check_grad(tag, n, got[n][:, a:b][:, :, heads], ref[n])
+        check_grad(tag, "dh0", got["dh0"][doc:doc + 1, heads], ref["dh0"])

@@ -103,3 +103,17 @@ def test_prologue_rejects_fp32_prefill():
     d = inputs.make_prologue(1, 64, 1, 64, 64, "f32", seed=1)
     with pytest.raises(kda.KdaError):
         _gpu_chunk(d)
+
+
+def test_chunk_prologue_kimi_k3_heads_sampled():
+    """The fused prologue at the bench's prefill shape (B=1, T=32768, H=96,
+    dk=dv=128): two sampled heads against the oracle over the whole
+    sequence."""
+    d = inputs.make_prologue(1, 32768, 96, 128, 128, "bf16", seed=4004)
+    o, ht = _gpu_chunk(d)
+    heads = [7, 90]
+    sel = lambda t: f64(t[:, :, heads])
+    o_ref, h_ref = pro.kda_forward_prologue(sel(d["q_raw"]), sel(d["k_raw"]), sel(d["v"]), sel(d["f"]),
+                                            sel(d["b_raw"]), f64(d["A_log"][heads]), f64(d["dt_bias"][heads]))
+    assert_close("prologue K3 heads o", o[:, :, heads], o_ref, torch.bfloat16)
+    assert_close("prologue K3 heads ht", ht[:, heads], h_ref, torch.bfloat16)
