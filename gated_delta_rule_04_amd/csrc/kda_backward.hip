@@ -39,10 +39,10 @@
 // to stay inside the 160 KB of LDS per workgroup; everything that contracts
 // over the value axis accumulates in registers across the slices; the next
 // slice's global loads are in flight while the current one is computed.
-// Step 3 is the only recurrence: a short MFMA chain per chunk, with F^T
-// staged through LDS one chunk ahead and b kept in bf16.  The slot of chunk c of the sequence that starts at
-// token t0 and has index n is (t0 / 64) + n + c, so the per-chunk buffers
-// need no prefix sum over the sequences.
+// Step 3 is the only recurrence: a short MFMA chain per chunk, with F^T and
+// b (bf16) fetched two chunks ahead.  The slot of chunk c of the sequence
+// that starts at token t0 and has index n is (t0 / 64) + n + c, so the
+// per-chunk buffers need no prefix sum over the sequences.
 
 #include "kda_prefill_common.h"
 #include "kda_launch.h"
@@ -63,13 +63,11 @@ struct BwdCfg {
   static constexpr int NT = 64 * NW;
   static constexpr int NB = NT / DK;   // gating: token blocks per chunk
   static constexpr int TB = C / NB;    // gating: tokens per block
-  static constexpr int KT = DK / 16;   // key-channel tiles
   static constexpr int KHP = DK + 16;  // pitch of the [C][DK] operand tiles
   static constexpr int CTP = C + 16;   // pitch of the [C][C] tiles
   static constexpr int AP = C + 4;     // pitch of the fp32 A tile
   static constexpr int VSL = 32;       // local kernel: value columns per slice
   static constexpr int SP = VSL + 16;  // pitch of the slice tiles
-  static constexpr int NSL = DV / VSL;
   static constexpr int DVP = DV + 16;  // pitch of the [C][DV] dO tile (prep)
   static_assert(NB == 4 && TB == 16, "gating map");
 };
