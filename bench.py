@@ -72,6 +72,17 @@ def alg_backward(B, T, H, dk, dv, g_group, N=None, elem=2):
     return B * T * H * (per_in + per_out) + N * H * dk * dv * 8
 
 
+def pct(xs, p):
+    """p-th percentile of a list of timings (linear interpolation)."""
+    ys = sorted(xs)
+    if not ys:
+        return float("nan")
+    x = (len(ys) - 1) * p / 100.0
+    i = int(x)
+    j = min(i + 1, len(ys) - 1)
+    return ys[i] + (ys[j] - ys[i]) * (x - i)
+
+
 def sha256_files(paths):
     """sha256 of the concatenated contents of paths (in order)."""
     h = hashlib.sha256()
@@ -282,6 +293,9 @@ def main():
             "tokens_per_s": B * T / (pre_avg * 1e-3),
             "ms": pre_avg,
             "ms_min": min(pre_ms),
+            "ms_median": pct(pre_ms, 50),
+            "ms_p10": pct(pre_ms, 10),
+            "ms_p90": pct(pre_ms, 90),
             "alg_tflops": pre_tfs,
             "mfma_frac_alg": pre_tfs / PEAK_BF16_TFLOPS,
             "hbm_frac_alg": pre_gbs / PEAK_HBM_GBS,
@@ -290,6 +304,9 @@ def main():
             "tokens_per_s": N / (dec_avg * 1e-3),
             "ms_per_step": dec_avg,
             "ms_min": min(dec_ms),
+            "ms_median": pct(dec_ms, 50),
+            "ms_p10": pct(dec_ms, 10),
+            "ms_p90": pct(dec_ms, 90),
             "hbm_frac_alg": dec_gbs / PEAK_HBM_GBS,
         },
         "event_ms_per_step": mean(step_ms),
