@@ -15,9 +15,11 @@
 //
 // Design for MI355X: the step is HBM-bound (one read of x, one write of y).
 // A thread owns 8 channels (one 16-byte access per token in bf16) and a run of
-// 64 consecutive tokens, keeping the W-wide window in registers, so every
-// input is read once (plus W-1 history rows per run).  Adjacent threads own
-// adjacent channel groups, so a wavefront's accesses are contiguous.
+// 256 consecutive tokens, keeping the W-wide window in registers, so every
+// input is read once (plus W-1 history rows per run).  Inside a document the
+// run advances 8 tokens at a time with all 8 loads issued together; y is
+// written with non-temporal stores.  Adjacent threads own adjacent channel
+// groups, so a wavefront's accesses are contiguous.
 
 #include "kda_common.h"
 #include "kda_launch.h"
@@ -26,9 +28,10 @@ namespace kda {
 
 namespace {
 
-constexpr int kConvRun = 64;  // tokens per thread
+constexpr int kConvRun = 256;  // tokens per thread
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x8 load8(const bf16* p) {
   const bf16x8 b = *reinterpret_cast<const bf16x8*>(p);
@@ -45,7 +48,7 @@ __device__ __forceinline__ void store8(bf16* p, const f32x8& x) {
   bf16x8 b;
 #pragma unroll
   for (int i = 0; i < 8; ++i) b[i] = (bf16)x[i];  // RNE
-  *reinterpret_cast<bf16x8*>(p) = b;
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, b), reinterpret_cast<u32x4v*>(p));  // written once
 }
 __device__ __forceinline__ void store8(float* p, const f32x8& x) {
   *reinterpret_cast<f32x4*>(p) = __builtin_shufflevector(x, x, 0, 1, 2, 3);
@@ -117,7 +120,25 @@ __global__ __launch_bounds__(256) void short_conv_fwd_kernel(const T* __restrict
     const int p = t0 - (W - 1) + h;
     win[h] = p >= s ? load8(x + (size_t)p * C + ch) : history<T, W>(conv0, n, C, ch, p - s + W - 1);
   }
-  for (int t = t0; t < t1; ++t) {
+  int t = t0;
+  // Fast path: groups of 8 tokens inside the current sequence, all 8 loads
+  // issued before any arithmetic so that they are in flight together.
+  for (; t + 8 <= t1 && t + 8 <= e; t += 8) {
+    f32x8 xin[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xin[u] = load8(x + (size_t)(t + u) * C + ch);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      win[W - 1] = xin[u];
+      f32x8 acc = wg[0] * win[0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) acc += wg[w] * win[w];
+      store8(y + (size_t)(t + u) * C + ch, acc);
+#pragma unroll
+      for (int w = 0; w < W - 1; ++w) win[w] = win[w + 1];
+    }
+  }
+  for (; t < t1; ++t) {
     if (t >= e && n + 1 < num_seqs) {  // the next non-empty sequence starts here
       do {
         ++n;
