@@ -686,28 +686,15 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     }
     if (v0 + VSL < DV) load_slice(v0 + VSL);
     __syncthreads();
-    // R = V - Kt S
+    // R = V - Kt S and dU = Kh dSt + P^T dO (independent of each other)
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
-      f32x4 acc = zero4();
+      f32x4 acc = zero4(), du = zero4();
 #pragma unroll
       for (int s = 0; s < SK; ++s)
         acc = F::mma(ld_row<KHP>(ft.kt, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.S, 16 * ct, s, l16, kg), acc);
       st_acc<SP>(sl.R, 16 * tt, 16 * ct, Reg16<bf16>::rows(vr[jj], ident, -acc), ident, l16, kg);
-    }
-    if (v0 + VSL < DV) load_v(v0 + VSL);
-    __syncthreads();
-    // U = T R;  dU = Kh dSt + P^T dO
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
-      f32x4 u = zero4(), du = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        if (32 * s <= 16 * tt + 15)
-          u = F::mma(ld_row<CTP>(ft.t, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.R, 16 * ct, s, l16, kg), u);
-      st_acc<SP>(sl.U, 16 * tt, 16 * ct, u, ident, l16, kg);
 #pragma unroll
       for (int s = 0; s < SK; ++s)
         du = F::mma(ld_row<KHP>(ft.kh, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.dS, 16 * ct, s, l16, kg), du);
@@ -717,16 +704,21 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
           du = F::mma(ld_row<CTP>(ft.u2, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.dO, 16 * ct, s, l16, kg), du);
       st_acc<SP>(sl.dU, 16 * tt, 16 * ct, du, ident, l16, kg);
     }
+    if (v0 + VSL < DV) load_v(v0 + VSL);
     __syncthreads();
-    // dR = T^T dU: the value gradient
+    // U = T R and dR = T^T dU, the value gradient
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
-      f32x4 dr = zero4();
+      f32x4 u = zero4(), dr = zero4();
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 2; ++s) {
+        if (32 * s <= 16 * tt + 15)
+          u = F::mma(ld_row<CTP>(ft.t, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.R, 16 * ct, s, l16, kg), u);
         if (32 * s + 31 >= 16 * tt)
           dr = F::mma(ld_row<CTP>(ft.u1, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.dU, 16 * ct, s, l16, kg), dr);
+      }
+      st_acc<SP>(sl.U, 16 * tt, 16 * ct, u, ident, l16, kg);
       const f32x4 rt = Reg16<bf16>::prod(dr, ident);  // rows of four columns
       st_row4<SP>(sl.dR, 16 * tt + l16, 16 * ct + 4 * kg, rt);
       bstore4(rt, bdv, (16 * tt + l16) * rsv + (v0 + 16 * ct + 4 * kg) * 2, bf16());
