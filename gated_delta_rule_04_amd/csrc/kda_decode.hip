@@ -17,9 +17,10 @@
 // second pass.  Each thread owns 4 adjacent value columns (one 16-byte load
 // per row) and a strided set of rows; a wavefront's loads cover whole
 // contiguous rows, so every access is a fully coalesced 16-byte load/store.
-// The state is read with non-temporal loads and written with non-temporal
-// stores: it is streamed once per step and the pool is far larger than the
-// caches.  The two column reductions run
+// The state is read with non-temporal loads: it is streamed once per step and
+// the pool is far larger than the caches.  A bf16 pool is also written with
+// non-temporal stores; the fp32 state keeps ordinary stores, which measured
+// faster when the step runs between prefill calls.  The two column reductions run
 // through cross-lane shuffles and an LDS exchange between the 8 wavefronts.
 // An in-place read-modify-write stream of this shape runs at about 67% of the
 // 8 TB/s peak on MI355X (measured: read-only about 74%, write-only about 70%).
@@ -43,7 +44,7 @@ namespace kda {
 typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
 
 // Four consecutive state values (fp32: one 16-byte access; bf16: one 8-byte
-// access), streamed with non-temporal loads and stores.
+// access), streamed with non-temporal loads.
 __device__ __forceinline__ f32x4 load_state4(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 }
@@ -51,9 +52,7 @@ __device__ __forceinline__ f32x4 load_state4(const bf16* p) {
   const bf16x4 b = __builtin_bit_cast(bf16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p)));
   return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
 }
-__device__ __forceinline__ void store_state4(float* p, const f32x4& x) {
-  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
-}
+__device__ __forceinline__ void store_state4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ __forceinline__ void store_state4(bf16* p, const f32x4& x) {
   const bf16x4 b = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};  // RNE
   __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, b), reinterpret_cast<u32x2v*>(p));
