@@ -242,3 +242,28 @@ def test_packed_documents_workload_full_size():
         for n in ("dq", "dk", "dv", "dg", "dbeta"):
             check_grad(tag, n, got[n][:, a:b][:, :, heads], ref[n])
         check_grad(tag, "dh0", got["dh0"][doc:doc + 1, heads], ref["dh0"])
+
+
+def test_decay_g64_workload_full_size():
+    """The decay-g64 workload at full size (B=5, T=8192, H=12, dk=dv=128,
+    one log-decay per 64 channels): the last 512 tokens of two sequences on
+    two heads against the oracle run from the state that enters them."""
+    d = inputs.workload_prefill("mini1h_g64_bf16")
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    ct = inputs.make_cotangents(B, T, H, dk, dv, B, "bf16", seed=3004, final_state=True, state_std=1.0)
+    got = run_gpu(d, ct)
+    for n in NAMES:
+        assert torch.isfinite(got[n]).all(), n
+    W = 512
+    heads = [0, 11]
+    for b in (1, 4):
+        sel = lambda t: f64(t[b:b + 1, :, heads])
+        q, k, v, g, beta, do = (sel(x) for x in (d["q"], d["k"], d["v"], d["g"], d["beta"], ct["do"]))
+        _, h_mid = orc.kda_forward(q[:, :T - W], k[:, :T - W], v[:, :T - W], g[:, :T - W], beta[:, :T - W],
+                                   g_group=64)
+        w = slice(T - W, T)
+        ref = kda_backward(q[:, w], k[:, w], v[:, w], g[:, w], beta[:, w], do[:, w], h0=h_mid,
+                           dht=f64(ct["dht"][b:b + 1, heads]), g_group=64)
+        for n in ("dq", "dk", "dv", "dg", "dbeta"):
+            check_grad("g64 seq %d last 512" % b, n, got[n][b:b + 1, w][:, :, heads], ref[n])
