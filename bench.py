@@ -427,7 +427,39 @@ def main():
         "hbm_frac_alg": bwd_bytes / (bwd_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "workspace_bytes": wsb.numel(),
     }
-    del dob, dhtb, wsb, gout
+    # Training pair: the forward keeps its chunk states in the workspace and
+    # the backward reads them instead of recomputing them.
+    fo = fh = None
+
+    def fwd_save():
+        return kda.chunk_fwd_save(P["q"], P["k"], P["v"], P["g"], P["beta"], output_final_state=True, out=fo,
+                                  final_state=fh, workspace=wsb)[:2]
+
+    def bwd_saved():
+        return kda.chunk_bwd(P["q"], P["k"], P["v"], P["g"], P["beta"], dob, dht=dhtb, workspace=wsb, out=gout,
+                             states_saved=True)
+
+    for _ in range(args.warmup):
+        fo, fh = fwd_save()
+        gout = bwd_saved()
+    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        tev[i][0].record()
+        fo, fh = fwd_save()
+        tev[i][1].record()
+        gout = bwd_saved()
+        tev[i][2].record()
+    torch.cuda.synchronize()
+    fs_ms = [e[0].elapsed_time(e[1]) for e in tev]
+    bs_ms = [e[1].elapsed_time(e[2]) for e in tev]
+    line["chunk_bwd_bf16"]["training_pair"] = {
+        "entry_points": "kda_chunk_fwd_save, kda_chunk_bwd_saved",
+        "fwd_save_ms": mean(fs_ms),
+        "bwd_saved_ms": mean(bs_ms),
+        "bwd_saved_ms_min": min(bs_ms),
+        "fwd_plus_bwd_ms": mean(fs_ms) + mean(bs_ms),
+    }
+    del dob, dhtb, wsb, gout, fo, fh
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, dec)
     print(json.dumps(line), flush=True)

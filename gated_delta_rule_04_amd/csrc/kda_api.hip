@@ -272,11 +272,19 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
   return L.total;
 }
 
-kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                         const float* h0, const void* dout, const float* dht, void* dq, void* dk, void* dv,
-                         void* dg, void* dbeta, float* dh0, const int* cu_seqlens, int num_seqs, int B, int T,
-                         int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// kRecompute: the backward recomputes the forward's chunk states itself.
+// kSaved: the workspace already holds them (written by kda_chunk_fwd_save).
+// kForwardSave: the forward only (o, optional ht), keeping the chunk states.
+enum class BwdMode { kRecompute, kSaved, kForwardSave };
+
+kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const float* h0, void* o, float* ht, const void* dout, const float* dht, void* dq, void* dk,
+                          void* dv, void* dg, void* dbeta, float* dh0, const int* cu_seqlens, int num_seqs, int B,
+                          int T, int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                          size_t workspace_bytes, void* stream, BwdMode mode) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
   if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
   if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
@@ -295,8 +303,10 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
   long long slots;
   if (!bwd_layout(B, T, H, Dk, Dv, N, varlen, L, slots)) return KDA_ERR_SHAPE;
   const bool has_tokens = (long long)B * T > 0;
-  if (has_tokens && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
-    return KDA_ERR_NULL;
+  const bool fwd_only = mode == BwdMode::kForwardSave;
+  if (has_tokens && (!q || !k || !v || !g || !beta)) return KDA_ERR_NULL;
+  if (has_tokens && fwd_only && !o) return KDA_ERR_NULL;
+  if (has_tokens && !fwd_only && (!dout || !dq || !dk || !dv || !dg || !dbeta)) return KDA_ERR_NULL;
   if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_WORKSPACE;
 
@@ -309,8 +319,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     order = reinterpret_cast<int*>(ws + 0);
     if (kda::launch_varlen_order(cu_seqlens, N, T, order, s) != hipSuccess) return KDA_ERR_HIP;
   }
-  // 1. forward, keeping the state entering every chunk
-  if (has_tokens) {
+  // 1. forward, keeping the state entering every chunk (and o, ht when asked)
+  if (mode != BwdMode::kSaved && (has_tokens || (fwd_only && ht))) {
     kda::PrefillArgs a;
     a.q = q;
     a.k = k;
@@ -318,8 +328,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     a.g = g;
     a.beta = beta;
     a.h0 = h0;
-    a.o = nullptr;
-    a.ht = nullptr;
+    a.o = fwd_only ? o : nullptr;
+    a.ht = fwd_only ? ht : nullptr;
     a.cu_seqlens = cu_seqlens;
     a.order = order;
     a.num_units = (int)units;
@@ -329,6 +339,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     const int vs = kda::prefill_slice_width(true, Dk, Dv, units, device_cus());
     if (kda::launch_prefill(true, Dk, Dv, g_group, vs, a, s) != hipSuccess) return KDA_ERR_HIP;
   }
+  if (fwd_only) return KDA_OK;
   // 2.-4. transfer and offset per chunk, reverse state pass, local gradients
   kda::BwdArgs b;
   b.q = static_cast<const kda::bf16*>(q);
@@ -356,6 +367,37 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
   b.slots = has_tokens ? (int)slots : 0;
   if (kda::launch_chunk_bwd(Dk, Dv, g_group, b, s) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* h0, const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                         void* dg, void* dbeta, float* dh0, const int* cu_seqlens, int num_seqs, int B, int T,
+                         int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl(q, k, v, g, beta, h0, nullptr, nullptr, dout, dht, dq, dk, dv, dg, dbeta, dh0, cu_seqlens,
+                        num_seqs, B, T, H, Dk, Dv, g_group, dt, workspace, workspace_bytes, stream,
+                        BwdMode::kRecompute);
+}
+
+kda_status kda_chunk_fwd_save(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T,
+                              int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl(q, k, v, g, beta, h0, o, ht, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group, dt, workspace, workspace_bytes, stream,
+                        BwdMode::kForwardSave);
+}
+
+kda_status kda_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const float* h0, const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                               void* dg, void* dbeta, float* dh0, const int* cu_seqlens, int num_seqs, int B, int T,
+                               int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl(q, k, v, g, beta, h0, nullptr, nullptr, dout, dht, dq, dk, dv, dg, dbeta, dh0, cu_seqlens,
+                        num_seqs, B, T, H, Dk, Dv, g_group, dt, workspace, workspace_bytes, stream, BwdMode::kSaved);
 }
 
 }  // extern "C"

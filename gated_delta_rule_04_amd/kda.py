@@ -28,9 +28,9 @@ _STATUS = {
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
 # KDA_ABI_VERSION of include/kda.h that these bindings are written for.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
-EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_recurrent_step", "kda_recurrent_step_pool",
+EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_save", "kda_chunk_bwd_saved", "kda_recurrent_step", "kda_recurrent_step_pool",
             "kda_short_conv_fwd", "kda_short_conv_step", "kda_status_str", "kda_abi_version"]
 
 _lib = None
@@ -69,6 +69,10 @@ def lib():
     L.kda_chunk_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_bwd.restype = i
     L.kda_chunk_bwd.argtypes = [vp] * 14 + [vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    L.kda_chunk_bwd_saved.restype = i
+    L.kda_chunk_bwd_saved.argtypes = [vp] * 14 + [vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    L.kda_chunk_fwd_save.restype = i
+    L.kda_chunk_fwd_save.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
     L.kda_recurrent_step.restype = i
     L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.kda_recurrent_step_pool.restype = i
@@ -231,7 +235,48 @@ def bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, varlen, dtype):
                                                    KDA_BF16 if dtype == torch.bfloat16 else KDA_F32))
 
 
-def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, workspace=None, out=None):
+def chunk_fwd_save(q, k, v, g, beta, initial_state=None, output_final_state=False, cu_seqlens=None, out=None,
+                   final_state=None, workspace=None):
+    """chunk_fwd (bf16) that also keeps the chunk states for the backward in
+    a backward workspace.  Returns (o, ht, workspace); pass the workspace to
+    chunk_bwd(..., workspace=..., states_saved=True) with the same inputs."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
+        raise ValueError("g's last dim must divide Dk")
+    g_group = Dk // g.shape[-1]
+    dt = _dt(q)
+    for t in (k, v, g, beta):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, g, beta must share one dtype")
+    if initial_state is not None and initial_state.dtype != torch.float32:
+        raise TypeError("initial_state must be float32")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _check_dev(q, k, v, g, beta, initial_state, cu_seqlens)
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    ht = final_state
+    if output_final_state and ht is None:
+        ht = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _check_dev(o, ht)
+    need = bwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, q.dtype)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().kda_chunk_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                                  _ptr(ht), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, g_group, dt, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream())
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_save")
+    return o, ht, ws
+
+
+def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, workspace=None, out=None,
+              states_saved=False):
     """Gradients of <do, o> + <dht, ht> for chunk_fwd(q, k, v, g, beta,
     initial_state, cu_seqlens) (bf16 inputs).  Returns a dict with dq, dk,
     dv, dg, dbeta (bf16, shaped like the inputs) and dh0 (float32
@@ -266,12 +311,14 @@ def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=Non
     ws = workspace
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(do),
-                             _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
-                             _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(cu_seqlens), N, B, T, H, Dk, Dv,
-                             g_group, dt, _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    if states_saved and workspace is None:
+        raise ValueError("states_saved needs the workspace that chunk_fwd_save filled")
+    fn = lib().kda_chunk_bwd_saved if states_saved else lib().kda_chunk_bwd
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(do), _ptr(dht),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]),
+            _ptr(cu_seqlens), N, B, T, H, Dk, Dv, g_group, dt, _ptr(ws), ws.numel() * ws.element_size(), _stream())
     if st != 0:
-        raise KdaError(st, "kda_chunk_bwd")
+        raise KdaError(st, "kda_chunk_bwd_saved" if states_saved else "kda_chunk_bwd")
     return out
 
 

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
   KDA_OK = 0,
@@ -169,6 +169,25 @@ kda_status kda_recurrent_step_prologue(const void* q_raw, const void* k_raw, con
                                        const void* b_raw, const float* A_log, const float* dt_bias, float* state,
                                        void* o, int N, int H, int Dk, int Dv, int g_group, kda_dtype dt,
                                        void* stream);
+
+/* Training pair: kda_chunk_fwd_save is kda_chunk_fwd (o, optional ht) that
+ * also keeps, in the backward workspace, the state entering every 64-token
+ * chunk; kda_chunk_bwd_saved is kda_chunk_bwd without its own recomputation
+ * of those states.  The workspace (kda_chunk_bwd_workspace_bytes, 256-byte
+ * aligned) must be passed to both, and the backward must see exactly the
+ * forward's q, k, v, g, beta, h0, cu_seqlens and sizes; between the two
+ * calls the workspace must not be used otherwise.  Gradients are bitwise
+ * those of kda_chunk_bwd.  Arguments, dtypes (bf16 only) and errors as for
+ * kda_chunk_fwd and kda_chunk_bwd. */
+kda_status kda_chunk_fwd_save(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T,
+                              int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                              size_t workspace_bytes, void* stream);
+kda_status kda_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const float* h0, const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                               void* dg, void* dbeta, float* dh0, const int* cu_seqlens, int num_seqs, int B, int T,
+                               int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* One recurrent decode step for N sequences x H heads (the recurrence of the
  * miniKimiK3 card's KDA bullet: constant cost per token), state in place.

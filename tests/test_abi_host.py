@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 5 == kda.ABI_VERSION
+    assert L.kda_abi_version() == 6 == kda.ABI_VERSION
     for s in range(7):
         assert L.kda_status_str(s).decode().startswith(("KDA_OK", "KDA_ERR"))
     assert L.kda_status_str(99)
@@ -148,3 +148,19 @@ def test_prologue_validation():
     assert ps(A=None) == NULL
     assert ps(q=None) == NULL
     assert ps(N=0, q=None, A=None) == OK
+
+
+def test_saved_pair_validation():
+    L = kda.lib()
+    need = L.kda_chunk_bwd_workspace_bytes(1, 64, 1, 64, 64, 1, 0, 1)
+    fs = lambda o=P, dt=1, ws=P, wsb=need: L.kda_chunk_fwd_save(P, P, P, P, P, None, o, None, None, 1, 1, 64, 1, 64,
+                                                                 64, 1, dt, ws, wsb, None)
+    assert fs(dt=0) == UNSUPPORTED
+    assert fs(o=None) == NULL
+    assert fs(wsb=need - 1) == WORKSPACE
+    assert fs(ws=None) == WORKSPACE
+    bs = lambda do=P, dt=1, wsb=need: L.kda_chunk_bwd_saved(P, P, P, P, P, None, do, None, P, P, P, P, P, None, None,
+                                                            1, 1, 64, 1, 64, 64, 1, dt, P, wsb, None)
+    assert bs(dt=0) == UNSUPPORTED
+    assert bs(do=None) == NULL
+    assert bs(wsb=need - 1) == WORKSPACE

@@ -267,3 +267,24 @@ def test_decay_g64_workload_full_size():
                            dht=f64(ct["dht"][b:b + 1, heads]), g_group=64)
         for n in ("dq", "dk", "dv", "dg", "dbeta"):
             check_grad("g64 seq %d last 512" % b, n, got[n][b:b + 1, w][:, :, heads], ref[n])
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_saved_states_pair_is_bitwise_the_plain_paths(packed):
+    """kda_chunk_fwd_save returns the forward's o and ht bitwise, and
+    kda_chunk_bwd_saved on its workspace the gradients of kda_chunk_bwd
+    bitwise."""
+    cu = [0, 70, 70, 200, 333] if packed else None
+    d, ct = case(1 if packed else 2, 333 if packed else 201, 3, 128, 128, cu=cu, seed=97)
+    dev = lambda t: None if t is None else t.cuda()
+    q, k, v, g, beta = (dev(d[n]) for n in ("q", "k", "v", "g", "beta"))
+    h0, cs = dev(d["h0"]), dev(d["cu_seqlens"])
+    o1, h1 = kda.chunk_fwd(q, k, v, g, beta, initial_state=h0, output_final_state=True, cu_seqlens=cs)
+    o2, h2, ws = kda.chunk_fwd_save(q, k, v, g, beta, initial_state=h0, output_final_state=True, cu_seqlens=cs)
+    a = kda.chunk_bwd(q, k, v, g, beta, dev(ct["do"]), initial_state=h0, dht=dev(ct["dht"]), cu_seqlens=cs)
+    b = kda.chunk_bwd(q, k, v, g, beta, dev(ct["do"]), initial_state=h0, dht=dev(ct["dht"]), cu_seqlens=cs,
+                      workspace=ws, states_saved=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
