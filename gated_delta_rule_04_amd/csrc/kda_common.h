@@ -26,6 +26,18 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE (v_cvt_pk_bf16_f32)
 
+// Two floats as one packed bf16 pair, rounded to nearest even: one
+// v_cvt_pk_bf16_f32.  Wider vectors are converted pair by pair: a conversion
+// of four lanes at once is otherwise split into four half-empty conversions
+// and two permutes.
+__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& v) {
+  typedef unsigned u32x2p __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(bf16x4, u32x2p{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])});
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -45,10 +45,8 @@ __device__ __forceinline__ f32x8 load8(const float* p) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ void store8(bf16* p, const f32x8& x) {
-  bf16x8 b;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) b[i] = (bf16)x[i];  // RNE
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, b), reinterpret_cast<u32x4v*>(p));  // written once
+  const u32x4v b = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7])};  // RNE
+  __builtin_nontemporal_store(b, reinterpret_cast<u32x4v*>(p));  // written once
 }
 __device__ __forceinline__ void store8(float* p, const f32x8& x) {
   *reinterpret_cast<f32x4*>(p) = __builtin_shufflevector(x, x, 0, 1, 2, 3);

@@ -54,7 +54,7 @@ __device__ __forceinline__ f32x4 load_state4(const bf16* p) {
 }
 __device__ __forceinline__ void store_state4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ __forceinline__ void store_state4(bf16* p, const f32x4& x) {
-  const bf16x4 b = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};  // RNE
+  const bf16x4 b = to_bf16x4(x);  // RNE
   __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, b), reinterpret_cast<u32x2v*>(p));
 }
 

@@ -47,7 +47,7 @@ template <typename E>
 __device__ __forceinline__ void store4(E* p, const f32x4& v);
 template <>
 __device__ __forceinline__ void store4<bf16>(bf16* p, const f32x4& v) {
-  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *reinterpret_cast<bf16x4*>(p) = to_bf16x4(v);
 }
 template <>
 __device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
@@ -131,7 +131,7 @@ struct Row4<float> {
   typedef f32x4 type;
 };
 __device__ __forceinline__ void bstore4(const f32x4& v, rsrc_t r, int off, bf16) {
-  const bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  const bf16x4 b = to_bf16x4(v);
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), r, off, 0, 0);
 }
 __device__ __forceinline__ void bstore4(const f32x4& v, rsrc_t r, int off, float) {
@@ -232,7 +232,7 @@ struct Frag<bf16> {
   }
   // From accumulator tiles x (tile 2s) and y (tile 2s + 1).
   __device__ __forceinline__ static V acc2(const f32x4& x, const f32x4& y) {
-    return V{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3], (bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+    return __builtin_shufflevector(to_bf16x4(x), to_bf16x4(y), 0, 1, 2, 3, 4, 5, 6, 7);
   }
   __device__ __forceinline__ static f32x4 mma(V a, V b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -265,7 +265,7 @@ struct Reg16;
 template <>
 struct Reg16<bf16> {
   __device__ __forceinline__ static s16x4 cvt(const f32x4& x) {
-    return __builtin_bit_cast(s16x4, bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]});
+    return __builtin_bit_cast(s16x4, to_bf16x4(x));
   }
   __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt(At), cvt(B), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -277,7 +277,7 @@ struct Reg16<bf16> {
   // as its C operand.
   __device__ __forceinline__ static f32x4 rows(const bf16x4& r, const f32x4& ident, const f32x4& c) {
     const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-    const bf16x4 i4 = {(bf16)ident[0], (bf16)ident[1], (bf16)ident[2], (bf16)ident[3]};
+    const bf16x4 i4 = to_bf16x4(ident);
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(r, z, 0, 1, 2, 3, 4, 5, 6, 7),
                                                    __builtin_shufflevector(i4, z, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
   }
@@ -322,9 +322,15 @@ template <int N>
 __device__ __forceinline__ float acc_frag(const f32x4 (&acc)[N], int s, float) {
   return acc[s >> 2][s & 3];
 }
+// Rounding to nearest even is symmetric in sign, so the negated fragment is
+// the fragment with both sign bits of each packed pair flipped.
 template <int N>
 __device__ __forceinline__ bf16x8 acc_frag_neg(const f32x4 (&acc)[N], int s, bf16) {
-  return Frag<bf16>::acc2(-acc[2 * s], -acc[2 * s + 1]);
+  const f32x4 &x = acc[2 * s], &y = acc[2 * s + 1];
+  constexpr unsigned kSign2 = 0x80008000u;
+  const u32x4 p = {pk_bf16(x[0], x[1]) ^ kSign2, pk_bf16(x[2], x[3]) ^ kSign2, pk_bf16(y[0], y[1]) ^ kSign2,
+                   pk_bf16(y[2], y[3]) ^ kSign2};
+  return __builtin_bit_cast(bf16x8, p);
 }
 template <int N>
 __device__ __forceinline__ float acc_frag_neg(const f32x4 (&acc)[N], int s, float) {
