@@ -179,6 +179,38 @@ struct PrefillCfg {
 // which spreads the producer's column writes over all banks while the state
 // wavefronts' row reads (one 16-row block per instruction) stay conflict-free.
 __device__ __forceinline__ int kht_swizzle(int row) { return (5 * (row >> 4)) & 15; }
+// Cross-lane sums without LDS traffic (the LDS is the busiest unit of the
+// pipelined prefill; a __shfl_* is an LDS-crossbar ds_bpermute).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Sum over the N = 8 or 16 consecutive lanes of a (half) row, in every lane:
+// quad permutes [1,0,3,2] and [2,3,0,1], then row_half_mirror and row_mirror.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(N == 8 || N == 16, "row_sum");
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  if constexpr (N == 16) x += dpp_mov<0x140>(x);
+  return x;
+}
+// Over the four 16-lane rows of a wavefront, lane by lane: the exclusive
+// prefix of x over the rows before this lane's row, and the total of all
+// four (gfx950 v_permlane16_swap hands a lane the even and the odd row of its
+// row pair, v_permlane32_swap the lower and the upper half).
+__device__ __forceinline__ void rows4_scan(float x, int row, float& excl, float& total) {
+  const unsigned xb = __builtin_bit_cast(unsigned, x);
+  const auto s = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  const float even = __builtin_bit_cast(float, (unsigned)s[0]), odd = __builtin_bit_cast(float, (unsigned)s[1]);
+  const float pair = even + odd;
+  const unsigned pb = __builtin_bit_cast(unsigned, pair);
+  const auto r = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
+  const float lower = __builtin_bit_cast(float, (unsigned)r[0]), upper = __builtin_bit_cast(float, (unsigned)r[1]);
+  excl = ((row & 1) ? even : 0.f) + ((row & 2) ? lower : 0.f);
+  total = lower + upper;
+}
 // bf16 Kh rows: 4-element unit u of token row r is stored at unit u ^ ((r / 4) % 4).
 // Row reads (16 consecutive rows), transposing reads (4 rows x 4 units per
 // 16 lanes) and the producer's row writes then spread over all banks.

@@ -344,22 +344,32 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
             G[j][c] = acc[c];
           }
         }
+        if constexpr (RBW == 4) {  // the four row blocks are the wavefront's 16-lane rows
+          float tot[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) off[c] = acc[c];  // inclusive prefix over blocks
-#pragma unroll
-        for (int d = 1; d < RBW; d <<= 1) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float y = __shfl_up(off[c], d * CGN);
-            if (rbw >= d) off[c] += y;
+          for (int c = 0; c < 8; ++c) rows4_scan(acc[c], rbw, off[c], tot[c]);
+          if (rbw == RBW - 1) {
+            *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch]) = f32x4{tot[0], tot[1], tot[2], tot[3]};
+            *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch + 4]) = f32x4{tot[4], tot[5], tot[6], tot[7]};
           }
-        }
-        if (rbw == RBW - 1) {
-          *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch]) = f32x4{off[0], off[1], off[2], off[3]};
-          *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch + 4]) = f32x4{off[4], off[5], off[6], off[7]};
-        }
+        } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) off[c] -= acc[c];  // exclusive within the wavefront
+          for (int c = 0; c < 8; ++c) off[c] = acc[c];  // inclusive prefix over blocks
+#pragma unroll
+          for (int d = 1; d < RBW; d <<= 1) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const float y = __shfl_up(off[c], d * CGN);
+              if (rbw >= d) off[c] += y;
+            }
+          }
+          if (rbw == RBW - 1) {
+            *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch]) = f32x4{off[0], off[1], off[2], off[3]};
+            *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch + 4]) = f32x4{off[4], off[5], off[6], off[7]};
+          }
+#pragma unroll
+          for (int c = 0; c < 8; ++c) off[c] -= acc[c];  // exclusive within the wavefront
+        }
         if (tid < C) sm.beta[bG][tid] = PRO ? (tid < nvG ? sigmoid_f(to_f32(rbeta)) : 0.f) : to_f32(rbeta);
         if (cG + 1 < nchunks) load_gb(cG + 1);  // prefetch (g, beta registers are free)
       }
@@ -403,11 +413,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
               sq += elem(rq[j], c) * elem(rq[j], c);
               sk += elem(rk[j], c) * elem(rk[j], c);
             }
-#pragma unroll
-            for (int o = 1; o < CGN; o <<= 1) {
-              sq += __shfl_xor(sq, o);
-              sk += __shfl_xor(sk, o);
-            }
+            sq = row_sum<CGN>(sq);
+            sk = row_sum<CGN>(sk);
             iq[j] = __builtin_amdgcn_rsqf(sq + kNormEps);
             ik[j] = __builtin_amdgcn_rsqf(sk + kNormEps);
           }
