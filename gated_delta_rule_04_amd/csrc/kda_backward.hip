@@ -770,8 +770,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
       kf[j] = bload<bf16>(bk, (tb * TB + j) * rsk + ch * 2);
     }
   }
-  rs += __shfl_xor(rs, 16);
-  rs += __shfl_xor(rs, 32);
+  rs = rows4_sum(rs);
   if (kg == 0) sm.dgc[16 * w + l16] = rs;
   __syncthreads();  // slice tiles are free: the C x C gradient tiles take their place
 
@@ -799,8 +798,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
           const int r = 16 * I + 4 * kg + i;
           part += x[i] * (float)ft.x[r * CTP + swz(r, 16 * J + l16)];
         }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
+        part = rows4_sum(part);
         if (kg == 0) sm.dbt[I][16 * J + l16] = part;
         st_acc<CTP>(cc.dM, 16 * I, 16 * J, x * ft.beta[16 * J + l16], ident, l16, kg);
       }
@@ -837,9 +835,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     }
     f32x4 pr = dA * bm;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] += __shfl_xor(pr[i], o);
+    for (int i = 0; i < 4; ++i) pr[i] = row_sum<16>(pr[i]);
     if (l16 == 0) *reinterpret_cast<f32x4*>(&sm.dba[J][16 * I + 4 * kg]) = pr;
     const f32x4 br = *reinterpret_cast<const f32x4*>(&ft.beta[16 * I + 4 * kg]);
     st_acc<CTP>(cc.dB, 16 * I, 16 * J, dA * br, ident, l16, kg);
@@ -914,8 +910,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     if constexpr (GG == 1) {
       bstore_bf16(x, bdg, r * rsg + ch * 2);
     } else {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+      x = rows4_sum(row_sum<16>(x));
       if (lane == 0) bstore_bf16(x, bdg, r * rsg + (ch / GG) * 2);
     }
   }

@@ -211,6 +211,16 @@ __device__ __forceinline__ void rows4_scan(float x, int row, float& excl, float&
   excl = ((row & 1) ? even : 0.f) + ((row & 2) ? lower : 0.f);
   total = lower + upper;
 }
+// The total of x over the four 16-lane rows, lane by lane (the sum that
+// __shfl_xor by 16 and by 32 would form).
+__device__ __forceinline__ float rows4_sum(float x) {
+  const unsigned xb = __builtin_bit_cast(unsigned, x);
+  const auto s = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  const float pair = __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
+  const unsigned pb = __builtin_bit_cast(unsigned, pair);
+  const auto r = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
 // bf16 Kh rows: 4-element unit u of token row r is stored at unit u ^ ((r / 4) % 4).
 // Row reads (16 consecutive rows), transposing reads (4 rows x 4 units per
 // 16 lanes) and the producer's row writes then spread over all banks.
