@@ -152,10 +152,17 @@ def cpu_baseline(pre, dec, budget_s=12.0):
     B, T, H = pre["q"].shape[:3]
     N = dec["state"].shape[0]
     t_step = B * T * H / pre_headtok_s + N * H / dec_pairs_s
+    try:  # BLAS threads the oracle's numpy could use
+        import threadpoolctl
+        blas = [p.get("num_threads") for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    except Exception:
+        blas = []
     return {
         "value": (B * T + N) / t_step,
         "unit": "tokens/s",
         "cores": cores,
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "blas_threads": blas[0] if blas else None,
         "kind": "oracle",
         "sample": ("fp64 numpy oracle: prefill on %d of %d heads x %d tokens (%.1f s), decode step on %d of %d "
                    "sequences x %d heads x %d steps (%.1f s); step time scaled to all heads and sequences"
@@ -312,6 +319,24 @@ def main():
         "event_ms_per_step": mean(step_ms),
         "input_gen_s": t_gen,
     }
+    # The decode workload as stated: its consecutive steps from the initial
+    # state (carried), each step timed on its own (outside the timed region).
+    st_run = dec["state"].to(dev)
+    ev_run = [torch.cuda.Event(enable_timing=True) for _ in range(len(D) + 1)]
+    ev_run[0].record()
+    for i, s in enumerate(D):
+        kda.recurrent_step(s["q"], s["k"], s["v"], s["g"], s["beta"], st_run, out=od)
+        ev_run[i + 1].record()
+    torch.cuda.synchronize()
+    run_ms = [ev_run[i].elapsed_time(ev_run[i + 1]) for i in range(len(D))]
+    line["decode"]["consecutive_steps"] = {
+        "steps": len(D),
+        "ms_total": sum(run_ms),
+        "ms_median": pct(run_ms, 50),
+        "ms_p10": pct(run_ms, 10),
+        "ms_p90": pct(run_ms, 90),
+    }
+    del st_run
     # Serving form (outside the timed step above): the same decode inputs over a
     # bf16 state pool, sequences in shuffled slots of a larger pool.
     ns = N + N // 4
