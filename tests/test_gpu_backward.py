@@ -269,13 +269,13 @@ def test_decay_g64_workload_full_size():
             check_grad("g64 seq %d last 512" % b, n, got[n][b:b + 1, w][:, :, heads], ref[n])
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_saved_states_pair_is_bitwise_the_plain_paths(packed):
+@pytest.mark.parametrize("packed,gg,dk", [(False, 1, 128), (True, 1, 128), (False, 64, 128), (True, 1, 64)])
+def test_saved_states_pair_is_bitwise_the_plain_paths(packed, gg, dk):
     """kda_chunk_fwd_save returns the forward's o and ht bitwise, and
     kda_chunk_bwd_saved on its workspace the gradients of kda_chunk_bwd
     bitwise."""
     cu = [0, 70, 70, 200, 333] if packed else None
-    d, ct = case(1 if packed else 2, 333 if packed else 201, 3, 128, 128, cu=cu, seed=97)
+    d, ct = case(1 if packed else 2, 333 if packed else 201, 3, dk, 128, gg=gg, cu=cu, seed=97 + gg + dk)
     dev = lambda t: None if t is None else t.cuda()
     q, k, v, g, beta = (dev(d[n]) for n in ("q", "k", "v", "g", "beta"))
     h0, cs = dev(d["h0"]), dev(d["cu_seqlens"])
