@@ -1,0 +1,116 @@
+"""Seeded random shapes against the oracle: prefill (bf16, and fp32 at
+d_k = 64), decode steps and the backward, with random batch, length, head
+count, head sizes, decay groups, initial states and packed documents
+(including empty ones).  Each case prints its draw, so a failure names it.
+Tolerances are the ones of the other parity tests."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.kda_oracle as orc
+from gated_delta_rule_04_amd import inputs, kda
+from oracle.kda_backward import kda_backward
+from tests._parity import assert_close, f64, to_dev
+from tests.test_gpu_backward import NAMES, check_grad
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed, dks=(64, 128), max_t=260):
+    rng = np.random.default_rng(seed)
+    c = dict(dk=int(rng.choice(dks)), dv=int(rng.choice([64, 128])), gg=int(rng.choice([1, 64])),
+             H=int(rng.integers(1, 4)), h0=bool(rng.integers(0, 2)))
+    if c["gg"] > c["dk"]:
+        c["gg"] = 1
+    if rng.integers(0, 2):
+        lens = [int(x) for x in rng.integers(0, 150, int(rng.integers(1, 6)))]
+        if sum(lens) == 0:
+            lens[-1] = 1
+        c.update(B=1, cu=[0] + [int(x) for x in np.cumsum(lens)])
+        c["T"] = c["cu"][-1]
+    else:
+        c.update(B=int(rng.integers(1, 4)), T=int(rng.integers(1, max_t)), cu=None)
+    print("case seed %d: %s" % (seed, c), flush=True)
+    return c
+
+
+def _prefill(c, dtype, seed):
+    return inputs.make_prefill(c["B"], c["T"], c["H"], c["dk"], c["dv"], dtype, c["gg"], seed=seed, h0=c["h0"],
+                               cu_seqlens=c["cu"])
+
+
+def _oracle_fwd(d):
+    cu = None if d.get("cu_seqlens") is None else d["cu_seqlens"].numpy()
+    return orc.kda_forward(*(f64(d[n]) for n in ("q", "k", "v", "g", "beta")),
+                           h0=None if d.get("h0") is None else f64(d["h0"]), cu_seqlens=cu, g_group=d["g_group"])
+
+
+def _gpu_fwd(d):
+    dd = to_dev(d)
+    o, ht = kda.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], initial_state=dd.get("h0"),
+                          output_final_state=True, cu_seqlens=dd.get("cu_seqlens"))
+    torch.cuda.synchronize()
+    return o.cpu(), ht.cpu()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_prefill_bf16(seed):
+    c = _draw(500 + seed)
+    d = _prefill(c, "bf16", 500 + seed)
+    o, ht = _gpu_fwd(d)
+    o_ref, h_ref = _oracle_fwd(d)
+    assert_close("random bf16 %d o" % seed, o, o_ref, torch.bfloat16)
+    assert_close("random bf16 %d ht" % seed, ht, h_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_prefill_f32(seed):
+    c = _draw(600 + seed, dks=(64,))
+    d = _prefill(c, "f32", 600 + seed)
+    o, ht = _gpu_fwd(d)
+    o_ref, h_ref = _oracle_fwd(d)
+    assert_close("random f32 %d o" % seed, o, o_ref, torch.float32)
+    assert_close("random f32 %d ht" % seed, ht, h_ref, torch.float32)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_decode_steps(seed):
+    rng = np.random.default_rng(700 + seed)
+    N, H = int(rng.integers(1, 9)), int(rng.integers(1, 5))
+    dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    gg = int(rng.choice([1, 64]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    print("case seed %d: N %d H %d dk %d dv %d gg %d %s" % (seed, N, H, dk, dv, gg, dtype), flush=True)
+    r = inputs.make_decode(N, H, dk, dv, steps=3, dtype=dtype, g_group=gg, seed=700 + seed)
+    state = r["state"].cuda()
+    ref = f64(r["state"])
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    for i, st in enumerate(r["steps"]):
+        o = kda.recurrent_step(*(st[n].cuda() for n in ("q", "k", "v", "g", "beta")), state)
+        torch.cuda.synchronize()
+        ref, o_ref = orc.kda_decode_step(ref, *(f64(st[n]) for n in ("q", "k", "v", "g", "beta")), g_group=gg)
+        assert_close("random decode %d step %d o" % (seed, i), o.cpu(), o_ref, tdt)
+        assert_close("random decode %d step %d S" % (seed, i), state.cpu(), ref, tdt)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_backward(seed):
+    c = _draw(800 + seed, max_t=200)
+    d = _prefill(c, "bf16", 800 + seed)
+    N = c["B"] if c["cu"] is None else len(c["cu"]) - 1
+    ct = inputs.make_cotangents(c["B"], c["T"], c["H"], c["dk"], c["dv"], N, "bf16", seed=900 + seed,
+                                final_state=bool(seed % 2 == 0), state_std=1.0)
+    dev = lambda t: None if t is None else t.cuda()
+    got = kda.chunk_bwd(*(dev(d[n]) for n in ("q", "k", "v", "g", "beta")), dev(ct["do"]),
+                        initial_state=dev(d.get("h0")), dht=dev(ct.get("dht")), cu_seqlens=dev(d.get("cu_seqlens")))
+    torch.cuda.synchronize()
+    cu = d.get("cu_seqlens")
+    ref = kda_backward(*(f64(d[n]) for n in ("q", "k", "v", "g", "beta")), f64(ct["do"]),
+                       h0=None if d.get("h0") is None else f64(d["h0"]),
+                       dht=None if ct.get("dht") is None else f64(ct["dht"]),
+                       cu_seqlens=None if cu is None else cu.numpy(), g_group=d["g_group"])
+    for n in NAMES:
+        if n == "dh0" and d.get("h0") is None:
+            continue
+        check_grad("random bwd %d" % seed, n, got[n].cpu(), ref[n])
