@@ -31,9 +31,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 CSRC = os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc")
 # Sources of each measured kernel (the bf16 prefill kernel is the pipelined one).
+# what a kernel is built from: its sources and the build script (compile flags)
+BUILD_PY = os.path.join(os.path.dirname(CSRC), "build.py")
 PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("kda_common.h", "kda_prefill_common.h", "kda_prefill.hip",
-                                                "kda_prefill_pipe.hip")]
-DECODE_SRCS = [os.path.join(CSRC, f) for f in ("kda_common.h", "kda_decode.hip")]
+                                                "kda_prefill_pipe.hip")] + [BUILD_PY]
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("kda_common.h", "kda_decode.hip")] + [BUILD_PY]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 
 

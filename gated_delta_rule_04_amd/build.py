@@ -32,6 +32,17 @@ COMMON = [
 ]
 
 
+# Per-file scheduling.  LLVM's max-ILP machine scheduler (a compiler option,
+# so per translation unit) runs the pipelined prefill and the decode step
+# faster (1.72 -> 1.68 ms and 0.614 -> 0.597 ms at B1 T32768 H96 d128 and N256;
+# results bitwise unchanged) and the backward kernels slower (+5%), which keep
+# the default scheduler.
+SOURCE_FLAGS = {
+    "kda_prefill_pipe.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "kda_decode.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -45,7 +56,7 @@ def sources():
 
 def _compile(src, objdir, extra):
     obj = os.path.join(objdir, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc()] + COMMON + extra + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + SOURCE_FLAGS.get(os.path.basename(src), []) + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     noise = "is not a recognized feature for this target"
     out = "\n".join(l for l in r.stdout.splitlines() if noise not in l)
