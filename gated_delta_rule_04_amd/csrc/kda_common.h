@@ -41,17 +41,18 @@ __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNormEps = 1e-6f;  // guard of the prologue's L2 normalisation
 
-// Prologue activations (fp32).  softplus(x) = log(1 + e^x): x itself above
-// 15 and e^x below -15 (where the rounded forms are exact to fp32), else
-// through the hardware exp2 / log2.
-__device__ __forceinline__ float softplus_f(float x) {
-  if (x > 15.f) return x;
-  const float e = fast_exp2(x * kLog2e);
-  if (x < -15.f) return e;
-  return __builtin_amdgcn_logf(1.f + e) * kLn2;
+// Prologue activations (fp32).  The gate's softplus is taken in log2 units:
+// with xs = x log2(e), softplus(x) log2(e) = log2(1 + 2^xs), because the ln 2
+// of the natural log and the log2(e) of the change of base cancel.  That is
+// xs itself above 15 log2(e) and 2^xs log2(e) below -15 log2(e) (where the
+// rounded forms are exact to fp32), else the hardware exp2 and log2.  Both
+// transcendentals are issued unconditionally and the branch is a select.
+__device__ __forceinline__ float softplus_log2(float xs) {
+  const float e = fast_exp2(xs);
+  const float l = __builtin_amdgcn_logf(1.f + e);
+  return xs > 15.f * kLog2e ? xs : (xs < -15.f * kLog2e ? e * kLog2e : l);
 }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + fast_exp2(-x * kLog2e)); }
 

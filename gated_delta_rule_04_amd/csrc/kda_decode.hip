@@ -108,12 +108,13 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
   if (tid < DK) {
     s_q[tid] = to_f32(q[u * DK + tid]);
     s_k[tid] = to_f32(k[u * DK + tid]);
-    float gx = to_f32(g[u * (DK / GG) + tid / GG]);
+    const float gx = to_f32(g[u * (DK / GG) + tid / GG]);
+    float lg = kLog2e * gx;  // log2 of the decay
     if constexpr (PRO) {
       const int gi = (int)(u % H) * (DK / GG) + tid / GG;
-      gx = -fast_exp2(A_log[gi] * kLog2e) * softplus_f(gx + dt_bias[gi]);
+      lg = -fast_exp2(A_log[gi] * kLog2e) * softplus_log2((gx + dt_bias[gi]) * kLog2e);
     }
-    s_a[tid] = fast_exp2(kLog2e * gx);
+    s_a[tid] = fast_exp2(lg);
   }
   __syncthreads();
   if (wave == 0) {

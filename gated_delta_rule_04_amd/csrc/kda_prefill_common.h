@@ -119,6 +119,23 @@ template <typename V>
 __device__ __forceinline__ float elem(const V& v, int i) {
   return (float)v[i];
 }
+// Sum of squares of 8 elements (bf16: four v_dot2_f32_bf16, which take the
+// pairs straight from the loaded registers).
+__device__ __forceinline__ float sumsq8(const bf16x8& v) {
+  float s = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const bf16x2 x = {v[2 * p], v[2 * p + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
+  }
+  return s;
+}
+__device__ __forceinline__ float sumsq8(const f32x8& v) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s += v[c] * v[c];
+  return s;
+}
 // Four consecutive elements of a row (one 8- or 16-byte access).
 template <typename T>
 struct Row4;

@@ -153,17 +153,25 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     const int rsk = H * DK * (int)sizeof(T);         // token stride of q, k (bytes)
     const int rsg = H * (DK / GG) * (int)sizeof(T);  // token stride of g
     const int rsb = H * (int)sizeof(T);              // token stride of beta
-    // prologue: exp(A_log) and dt_bias of this thread's channels (or group)
+    // prologue: -exp(A_log) and dt_bias log2(e) of this thread's channels (or group)
     constexpr int NGC = PRO ? (GG == 1 ? 8 : 1) : 1;
-    float gA[NGC], gD[NGC];
+    float nA[NGC], gDs[NGC];
     if constexpr (PRO) {
 #pragma unroll
       for (int c = 0; c < NGC; ++c) {
         const int gi = h * (DK / GG) + (GG == 1 ? ch + c : ch / GG);
-        gA[c] = fast_exp2(args.A_log[gi] * kLog2e);
-        gD[c] = args.dt_bias[gi];
+        nA[c] = -fast_exp2(args.A_log[gi] * kLog2e);
+        gDs[c] = args.dt_bias[gi] * kLog2e;
       }
     }
+    // log2 of a decay from its gate: the gate itself, or under the prologue
+    // -exp(A_log) softplus(g + dt_bias)
+    auto lg_gate = [&](float x, int c) {
+      if constexpr (PRO)
+        return nA[c] * softplus_log2(fmaf(x, kLog2e, gDs[c]));
+      else
+        return x * kLog2e;
+    };
     auto chunk_rows = [&](int ck) { return min(C, len - ck * C); };
     auto chunk_row0 = [&](int ck) { return (size_t)(tok0 + ck * C) * H + h; };
     auto load_gb = [&](int ck) {  // g, beta
@@ -323,27 +331,35 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = 0.f;
         // rows past the end of the sequence stay inert under the prologue too:
-        // their (zero) gate logits must not become a decay
+        // their (zero) gate logits must not become a decay.  A full chunk
+        // (uniform test) skips the per-row mask.
         const int nvG = chunk_rows(cG);
+        auto gate_rows = [&](auto Full) {
+          constexpr bool FULL = decltype(Full)::value;
 #pragma unroll
-        for (int j = 0; j < RPB; ++j) {
-          const bool live = !PRO || rb * RPB + j < nvG;
-          float grow = 0.f;  // decay-group gate of row j
-          if constexpr (GG != 1) {
-            grow = to_f32(rgs[j]);
-            if constexpr (PRO) grow = live ? -gA[0] * softplus_f(grow + gD[0]) : 0.f;
-          }
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            float gx = grow;
-            if constexpr (GG == 1) {
-              gx = elem(rg[j], c);
-              if constexpr (PRO) gx = live ? -gA[c] * softplus_f(gx + gD[c]) : 0.f;
+          for (int j = 0; j < RPB; ++j) {
+            const bool live = FULL || rb * RPB + j < nvG;
+            float lrow = 0.f;  // decay-group gate of row j (log2 units)
+            if constexpr (GG != 1) {
+              lrow = lg_gate(to_f32(rgs[j]), 0);
+              if constexpr (!FULL) lrow = live ? lrow : 0.f;
             }
-            acc[c] += gx * kLog2e;
-            G[j][c] = acc[c];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              float lx = lrow;
+              if constexpr (GG == 1) {
+                lx = lg_gate(elem(rg[j], c), c);
+                if constexpr (!FULL) lx = live ? lx : 0.f;
+              }
+              acc[c] += lx;
+              G[j][c] = acc[c];
+            }
           }
-        }
+        };
+        if (!PRO || nvG == C)
+          gate_rows(IC<1>{});
+        else
+          gate_rows(IC<0>{});
         if constexpr (RBW == 4) {  // the four row blocks are the wavefront's 16-lane rows
           float tot[8];
 #pragma unroll
@@ -407,14 +423,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         if constexpr (PRO) {
 #pragma unroll
           for (int j = 0; j < RPB; ++j) {
-            float sq = 0.f, sk = 0.f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              sq += elem(rq[j], c) * elem(rq[j], c);
-              sk += elem(rk[j], c) * elem(rk[j], c);
-            }
-            sq = row_sum<CGN>(sq);
-            sk = row_sum<CGN>(sk);
+            const float sq = row_sum<CGN>(sumsq8(rq[j]));
+            const float sk = row_sum<CGN>(sumsq8(rk[j]));
             iq[j] = __builtin_amdgcn_rsqf(sq + kNormEps);
             ik[j] = __builtin_amdgcn_rsqf(sk + kNormEps);
           }
