@@ -24,7 +24,7 @@ Sources (the page text the method is defined on):
 * Mini-K3-1H-decay-g64 model card: decay granularity ("decay-g64") is an
   ablation axis -- one log-decay value shared by a group of 64 channels.
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
 
 * The gradient step is on 1/2 ||S^T k - v||^2 with step size beta; this gives
   exactly the matrix form above (a literal ||.||^2 would double the step).
