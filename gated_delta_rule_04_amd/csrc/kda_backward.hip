@@ -50,6 +50,9 @@
 #ifndef KDA_BWD_DH_WAVES
 #define KDA_BWD_DH_WAVES 4  // wavefronts (16-column tiles) per reverse-state-pass workgroup
 #endif
+#ifndef KDA_BWD_DH_STAGES
+#define KDA_BWD_DH_STAGES 2  // chunks of F^T and b in flight ahead of the reverse state pass
+#endif
 
 namespace kda {
 
@@ -451,12 +454,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
 // NWD = 4):
 // dS_in = F^T dS_out + b, chunk by chunk from the last.  NWD wavefronts, one
 // 16-column tile each.  F^T fragments are shared through LDS (double
-// buffered); the loads of chunk c - 2 are issued while chunk c is computed,
-// into two register stages that alternate (the loop is unrolled by two), so
-// each load has two iterations to land.  The slices of a head read F^T
+// buffered); F^T and b are fetched NST chunks ahead into register stages
+// used in turn (the loop is unrolled by NST).  The slices of a head read F^T
 // through the same XCD's L2.
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int NWD>
+template <int DK, int DV, int NWD, int NST>
 __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
   constexpr int KS = DK / 32, KT = DK / 16, NTD = 64 * NWD, NS = DV / (16 * NWD);
   constexpr int FU = DK * DK / 8;     // 16-byte fragment units of F^T per chunk
@@ -487,27 +489,33 @@ __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[mt][i] = d ? d[(size_t)(16 * mt + 4 * kg + i) * DV + 16 * ct + l16] : 0.f;
   }
-  auto load_f = [&](u32x4 (&dst)[FPT], int cc) {
+  auto load_f = [&](u32x4 (&dst)[FPT], int cc) __attribute__((always_inline)) {
     const u32x4* p = reinterpret_cast<const u32x4*>(A.fw + ((size_t)(slot0 + cc) * A.H + h) * DK * DK);
 #pragma unroll
     for (int j = 0; j < FPT; ++j) dst[j] = p[tid + NTD * j];
   };
-  auto load_b = [&](bf16x4 (&dst)[KT], int cc) {
+  auto load_b = [&](bf16x4 (&dst)[KT], int cc) __attribute__((always_inline)) {
     const bf16* p = A.bw + ((size_t)(slot0 + cc) * A.H + h) * DK * DV;
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
       dst[mt] = __builtin_bit_cast(bf16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
                                                p + ((size_t)(mt * (DV / 16) + ct) * 64 + lane) * 4)));
   };
-  auto put_f = [&](const u32x4 (&src)[FPT], int buf) {
+  auto put_f = [&](const u32x4 (&src)[FPT], int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < FPT; ++j) fbuf[buf][tid + NTD * j] = src[j];
   };
-  bf16x4 bc[KT];  // b of the chunk being computed
-  // one chunk: dS_out is kept, then dS_in = F^T dS_out + b; afterwards the
-  // next chunk's F^T goes to LDS from stage (fs, bs), which is then refilled
-  // with the chunk three below
-  auto step = [&](int cc, u32x4 (&fs)[FPT], bf16x4 (&bs)[KT]) {
+  // Register stages, used in turn: at iteration j (chunk cc = nch - 1 - j)
+  // stage u = j % NST holds b of chunk cc and F^T of chunk cc - 1.  Both are
+  // refilled in the same iteration (b with chunk cc - NST, F^T with chunk
+  // cc - 1 - NST), so each load has NST iterations to land.  The refills are
+  // unconditional (an index below zero rereads chunk 0): no copy between
+  // stages and no merge of loaded and unloaded values, either of which makes
+  // the compiler wait for the loads just issued.
+  u32x4 fs[NST][FPT];
+  bf16x4 bs[NST][KT];
+  auto step = [&](int cc, auto Uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(Uc)::value;
     __syncthreads();  // F^T of chunk cc is in fbuf[cc & 1]
     bf16* dh = A.dh + ((size_t)(slot0 + cc) * A.H + h) * DK * DV;
 #pragma unroll
@@ -519,42 +527,31 @@ __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
     const u32x4* fb = fbuf[cc & 1];
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt) {
-      f32x4 acc = {(float)bc[mt][0], (float)bc[mt][1], (float)bc[mt][2], (float)bc[mt][3]};
+      f32x4 acc = {(float)bs[u][mt][0], (float)bs[u][mt][1], (float)bs[u][mt][2], (float)bs[u][mt][3]};
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = F::mma(__builtin_bit_cast(FV, fb[(mt * KS + s) * 64 + lane]), SF[s], acc);
       dS[mt] = acc;
     }
-    if (cc >= 1) {
-      put_f(fs, (cc - 1) & 1);  // its buffer held chunk cc + 1, done before this iteration's barrier
-#pragma unroll
-      for (int mt = 0; mt < KT; ++mt) bc[mt] = bs[mt];
-      if (cc >= 3) {
-        load_f(fs, cc - 3);
-        load_b(bs, cc - 3);
-      }
-    }
+    load_b(bs[u], max(cc - NST, 0));
+    if (cc >= 1) put_f(fs[u], (cc - 1) & 1);  // its buffer held chunk cc + 1, done before this iteration's barrier
+    load_f(fs[u], max(cc - 1 - NST, 0));
   };
 
-  u32x4 fa[FPT], fb2[FPT];
-  bf16x4 ba[KT], bb[KT];
   if (nch > 0) {
-    load_f(fa, nch - 1);
-    load_b(bc, nch - 1);
-    put_f(fa, (nch - 1) & 1);
-    if (nch > 1) {
-      load_f(fa, nch - 2);
-      load_b(ba, nch - 2);
-    }
-    if (nch > 2) {
-      load_f(fb2, nch - 3);
-      load_b(bb, nch - 3);
-    }
+    load_f(fs[0], nch - 1);
+    put_f(fs[0], (nch - 1) & 1);
+    static_for<NST>([&](auto Uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(Uc)::value;
+      load_b(bs[u], max(nch - 1 - u, 0));
+      load_f(fs[u], max(nch - 2 - u, 0));
+    });
   }
-  // stage a holds chunk nch - 2, stage b chunk nch - 3; they alternate
-  for (int cc = nch - 1; cc >= 0; cc -= 2) {
-    step(cc, fa, ba);
-    if (cc >= 1) step(cc - 1, fb2, bb);
-  }
+  // whole groups of NST iterations, then the rest
+  int j0 = 0;
+  for (; j0 + NST <= nch; j0 += NST) static_for<NST>([&](auto Uc) __attribute__((always_inline)) { step(nch - 1 - j0 - decltype(Uc)::value, Uc); });
+  static_for<NST>([&](auto Uc) __attribute__((always_inline)) {
+    if (j0 + decltype(Uc)::value < nch) step(nch - 1 - j0 - decltype(Uc)::value, Uc);
+  });
   // dh0 (fp32); for an empty sequence it is dht
   if (A.dh0) {
     float* d0 = A.dh0 + ((size_t)n * A.H + h) * DK * DV;
@@ -941,7 +938,7 @@ static hipError_t launch_bwd_cfg(const BwdArgs& a, hipStream_t s) {
   if (units > 0) {
     constexpr int NWD = KDA_BWD_DH_WAVES;
     const int grid2 = (units + 7) / 8 * 8 * (DV / (16 * NWD));
-    hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, DV, NWD>), dim3(grid2), dim3(64 * NWD), 0, s, a);
+    hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, DV, NWD, KDA_BWD_DH_STAGES>), dim3(grid2), dim3(64 * NWD), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

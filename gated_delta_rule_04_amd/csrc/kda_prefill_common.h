@@ -22,6 +22,14 @@ template <int V>
 struct IC {
   static constexpr int value = V;
 };
+// fn(IC<0>{}), fn(IC<1>{}), ..., fn(IC<N - 1>{}), in order (compile-time indices).
+template <int N, int I = 0, class Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (I < N) {
+    fn(IC<I>{});
+    static_for<N, I + 1>(fn);
+  }
+}
 template <int N, class Fn>
 __device__ __forceinline__ void static_switch(int w, Fn&& fn) {
   if constexpr (N > 0) {
