@@ -11,6 +11,10 @@
 
 namespace {
 
+// The chunked kernels address a 64-token span of one tensor with 32-bit
+// byte offsets: 64 * H * max(Dk, Dv) * 4 bytes must fit in an int.
+constexpr int kMaxChunkedHeads = 65535;
+
 bool head_dims_ok(int Dk, int Dv, int g_group) {
   const bool d_ok = (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
   const bool g_ok = (g_group == 1 || g_group == 64) && Dk % g_group == 0;
@@ -72,7 +76,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
                           int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
                           void* stream, const float* A_log, const float* dt_bias) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
-  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
+  if (B < 0 || T < 0 || H <= 0 || H > kMaxChunkedHeads || num_seqs < 0) return KDA_ERR_SHAPE;
   if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
   const bool bf = dt == KDA_BF16;
   if (!kda::prefill_supported(bf, Dk, Dv)) return KDA_ERR_UNSUPPORTED;
@@ -286,7 +290,7 @@ kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const voi
                           int T, int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
                           size_t workspace_bytes, void* stream, BwdMode mode) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
-  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
+  if (B < 0 || T < 0 || H <= 0 || H > kMaxChunkedHeads || num_seqs < 0) return KDA_ERR_SHAPE;
   if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
   if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   const bool varlen = cu_seqlens != nullptr;

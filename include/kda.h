@@ -67,6 +67,9 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
  * bullet; chunk size 64 internally).  Computes o_t for every token and,
  * optionally, each sequence's final state.
  *
+ *   H      heads, 1 .. 65535 (a 64-token span of one tensor must stay below
+ *          2 GiB: the kernels address a chunk with 32-bit byte offsets);
+ *          more heads return KDA_ERR_SHAPE.
  *   q, k   [B, T, H, Dk]        dt
  *   v      [B, T, H, Dv]        dt
  *   g      [B, T, H, Dk/g_group] dt   log(alpha) <= 0
@@ -110,7 +113,8 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
  * internally, so o is not an input.
  *
  *   q, k, v, g, beta, h0, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group:
- *          as for kda_chunk_fwd (same layouts, same chunk-decay domain).
+ *          as for kda_chunk_fwd (same layouts, same chunk-decay domain, same
+ *          head limit).
  *   dout   [B, T, H, Dv]   bf16  cotangent of o
  *   dht    [N, H, Dk, Dv]  f32 or NULL (NULL = zero)  cotangent of ht
  *   dq, dk [B, T, H, Dk]   bf16  gradients (every token written)

@@ -66,6 +66,8 @@ def test_chunk_fwd_validation():
     assert fwd(cu=P, N=3, ws=P, wsb=need - 1) == WORKSPACE
     assert kda.lib().kda_chunk_fwd_workspace_bytes(1, 64, 1, 64, 64, 1, 0, 1) == 0
     assert fwd(B=2 ** 30, T=2 ** 30, N=2 ** 30) == SHAPE  # size overflow
+    assert fwd(H=65536) == SHAPE                      # a chunk span must fit 32-bit byte offsets
+    assert fwd(H=65535, B=0, T=0, N=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
 
 
 def test_chunk_fwd_nothing_to_do_is_ok_without_gpu():
@@ -117,6 +119,7 @@ def test_chunk_bwd_validation():
 
     assert bwd(dt=7) == DTYPE
     assert bwd(T=-1) == SHAPE
+    assert bwd(H=65536, wsb=0) == SHAPE
     assert bwd(Dk=96) == UNSUPPORTED
     assert bwd(dt=0) == UNSUPPORTED                   # the backward is bf16 only
     assert bwd(N=2, B=1) == SHAPE
