@@ -171,7 +171,30 @@ def round_bf16(x):
     return np.ldexp(np.round(m * 256.0) / 256.0, e)
 
 
-def kda_decode_step_pool(pool, slots, q, k, v, g, beta, g_group=1, state_bf16=False):
+def round_f16(x):
+    """Round float64 values to the nearest IEEE 754 binary16 value, ties to
+    even (numpy's float64 -> float16 conversion is that rounding, subnormals
+    and overflow to infinity included)."""
+    with np.errstate(over="ignore"):  # overflow to infinity is the defined result
+        return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def output_gate(o, z):
+    """The output gate on the mixer output: o * sigmoid(z), elementwise.
+
+    The Mini-K3-1H model cards list output gates among the operators the
+    family keeps, without a formula; this is the plain reading: an
+    elementwise logistic gate with one logit per (sequence, head, value
+    channel), the logits z coming from the layer's own gate projection.
+    """
+    return _f64(o) / (1.0 + np.exp(-_f64(z)))
+
+
+_STATE_ROUND = {"f32": lambda x: x, "bf16": round_bf16, "f16": round_f16}
+
+
+def kda_decode_step_pool(pool, slots, q, k, v, g, beta, g_group=1, state_bf16=False, state_dtype=None,
+                         o_gate=None):
     """One decode step over a pool of states (serving form).
 
     pool: [num_slots, H, dk, dv]; slots: [N] ints; q, k: [N, H, dk];
@@ -180,11 +203,15 @@ def kda_decode_step_pool(pool, slots, q, k, v, g, beta, g_group=1, state_bf16=Fa
     serving notes: decode concurrency is bounded by a pool of per-sequence
     KDA states whose dtype is a serving knob).  A slot outside [0, num_slots)
     marks the sequence inactive: its output row is zero and no state changes.
-    With state_bf16 the pool holds bfloat16 values: the step runs on them
-    exactly and the new state is rounded to the nearest bfloat16 (ties to
-    even); the output is the exact step's output.
+    state_dtype "f32" (default), "bf16" (also state_bf16=True) or "f16": the
+    pool holds values of that type, the step runs on them exactly and the new
+    state is rounded to the nearest value of the type (ties to even).
+    o_gate [N, H, dv] or None: the output gate's logits; an active sequence's
+    output is then output_gate(o, o_gate).  The output is the exact step's.
     Returns (new_pool, o [N, H, dv]).
     """
+    sdt = state_dtype or ("bf16" if state_bf16 else "f32")
+    rnd = _STATE_ROUND[sdt]
     pool = _f64(pool).copy()
     slots = np.asarray(slots)
     N, H = np.asarray(q).shape[:2]
@@ -197,6 +224,6 @@ def kda_decode_step_pool(pool, slots, q, k, v, g, beta, g_group=1, state_bf16=Fa
         S_new, o_n = kda_decode_step(pool[s][None], np.asarray(q)[n:n + 1], np.asarray(k)[n:n + 1],
                                      np.asarray(v)[n:n + 1], np.asarray(g)[n:n + 1], np.asarray(beta)[n:n + 1],
                                      g_group)
-        pool[s] = round_bf16(S_new[0]) if state_bf16 else S_new[0]
-        o[n] = o_n[0]
+        pool[s] = rnd(S_new[0])
+        o[n] = o_n[0] if o_gate is None else output_gate(o_n[0], np.asarray(o_gate)[n])
     return pool, o

@@ -1,5 +1,5 @@
-"""Pins of the oracle's serving-pool decode step and its bfloat16 rounding
-(CPU only).  The K3-Tiny-L13 card's serving notes bound decode concurrency by
+"""Pins of the oracle's serving-pool decode step, its bfloat16 and float16
+rounding and the output gate (CPU only).  The K3-Tiny-L13 card's serving notes bound decode concurrency by
 a pool of per-sequence KDA states whose dtype is a serving knob; the pool
 step is the plain decode step on the state in each sequence's slot."""
 
@@ -63,3 +63,55 @@ def test_pool_step_bf16_state_is_the_rounded_exact_step():
     assert np.array_equal(o, o_exact)                  # the output is the exact step's
     assert np.array_equal(new, orc.round_bf16(exact))  # the state is its bf16 rounding
     assert not np.array_equal(new, exact)
+
+
+def test_round_f16_matches_torch_on_float32_values():
+    # torch's float32 -> float16 conversion rounds to nearest, ties to even
+    x = np.random.default_rng(17).standard_normal(200000) * np.exp(np.random.default_rng(18).uniform(-20, 11, 200000))
+    x32 = x.astype(np.float32).astype(np.float64)
+    ref = torch.tensor(x32, dtype=torch.float32).half().double().numpy()
+    assert np.array_equal(orc.round_f16(x32), ref)
+
+
+def test_round_f16_ties_subnormals_and_overflow():
+    # float16 spacing is 2^-10 in [1, 2); the smallest subnormal is 2^-24; the
+    # largest finite value is 65504, and 65520 lies halfway to 2^16
+    x = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -24, 3 * 2.0 ** -26, 2.0 ** -26, 65504.0,
+                  65519.0, 65520.0, -(1 + 2.0 ** -11)])
+    want = np.array([1.0, 1 + 2.0 ** -9, 2.0 ** -24, 2.0 ** -24, 0.0, 65504.0, 65504.0, np.inf, -1.0])
+    assert np.array_equal(orc.round_f16(x), want)
+
+
+def test_output_gate_closed_forms():
+    o = np.random.default_rng(19).standard_normal(64)
+    assert np.array_equal(orc.output_gate(o, np.zeros(64)), o / 2)           # sigmoid(0) = 1/2
+    assert np.allclose(orc.output_gate(o, np.full(64, np.log(3.0))), 0.75 * o, rtol=1e-15, atol=0)
+    assert np.array_equal(orc.output_gate(o, np.full(64, 40.0)), o)           # 1 + e^-40 rounds to 1
+    assert np.all(np.abs(orc.output_gate(o, np.full(64, -40.0))) <= 1e-17 * np.abs(o))
+
+
+def test_pool_step_output_gate_scales_only_the_output():
+    x, S = _step_inputs(4, 2, 8, 8, seed=43)
+    pool = np.random.default_rng(5).standard_normal((5, 2, 8, 8)) * 0.1
+    slots = np.array([3, -1, 0, 4])
+    ref_pool, ref_o = orc.kda_decode_step_pool(pool, slots, x["q"], x["k"], x["v"], x["g"], x["beta"])
+    half_pool, half_o = orc.kda_decode_step_pool(pool, slots, x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                                 o_gate=np.zeros((4, 2, 8)))
+    assert np.array_equal(half_pool, ref_pool)   # the gate never reaches the state
+    assert np.array_equal(half_o, ref_o / 2)     # and inactive rows stay zero
+    z = np.full((4, 2, 8), np.log(3.0))
+    _, o3 = orc.kda_decode_step_pool(pool, slots, x["q"], x["k"], x["v"], x["g"], x["beta"], o_gate=z)
+    assert np.allclose(o3, 0.75 * ref_o, rtol=1e-15, atol=0)
+
+
+def test_pool_step_f16_state_is_the_rounded_exact_step():
+    x, S = _step_inputs(3, 2, 16, 8, seed=44)
+    pool = orc.round_f16(np.random.default_rng(6).standard_normal((3, 2, 16, 8)) * 0.05)
+    new, o = orc.kda_decode_step_pool(pool, np.array([1, 2, 0]), x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                      state_dtype="f16")
+    exact, o_exact = orc.kda_decode_step_pool(pool, np.array([1, 2, 0]), x["q"], x["k"], x["v"], x["g"], x["beta"])
+    assert np.array_equal(o, o_exact)
+    assert np.array_equal(new, orc.round_f16(exact))
+    assert not np.array_equal(new, exact)
+    # float16 keeps 3 more significant bits than bfloat16
+    assert np.abs(new - exact).max() < np.abs(orc.round_bf16(exact) - exact).max()
