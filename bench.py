@@ -417,6 +417,38 @@ def main():
         "alg_bytes_per_launch": pool_bytes,
         "hbm_frac_alg": pool_bytes / (pool_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
+
+    # The same pool step with the output gate (logits [N, H, dv]), and over a
+    # float16 state pool of the same bytes.
+    def time_pool(p, gate):
+        for i in range(args.warmup):
+            s = D[i % len(D)]
+            kda.recurrent_step_pool(s["q"], s["k"], s["v"], s["g"], s["beta"], p, slots, out=od, o_gate=gate)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            s = D[i % len(D)]
+            ev[i][0].record()
+            kda.recurrent_step_pool(s["q"], s["k"], s["v"], s["g"], s["beta"], p, slots, out=od, o_gate=gate)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return mean([e[0].elapsed_time(e[1]) for e in ev])
+
+    zg = torch.randn((N, H, dv), generator=torch.Generator().manual_seed(18)).to(torch.bfloat16).to(dev)
+    gated_ms = time_pool(pool, zg)
+    del pool
+    pool16 = torch.zeros((ns, H, dk, dv), dtype=torch.float16, device=dev)
+    pool16[slots.long()] = state.to(torch.float16)
+    f16_ms = time_pool(pool16, None)
+    del pool16
+    gate_bytes = N * H * dv * 2
+    line["decode_pool_bf16"]["with_output_gate"] = {
+        "ms_per_step": gated_ms,
+        "hbm_frac_alg": (pool_bytes + gate_bytes) / (gated_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    line["decode_pool_bf16"]["f16_state"] = {
+        "ms_per_step": f16_ms,
+        "hbm_frac_alg": pool_bytes / (f16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
     # Short causal convolution (outside the timed step): one K3 projection's
     # width over the prefill tokens, W = 4.
     Cc, Wc = H * dk, 4

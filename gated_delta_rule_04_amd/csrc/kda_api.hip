@@ -184,18 +184,20 @@ kda_status kda_recurrent_step_prologue(const void* q_raw, const void* k_raw, con
 }
 
 kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                                   void* state_pool, const int* slots, int num_slots, void* o, int N, int H,
-                                   int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt, void* stream) {
+                                   void* state_pool, const int* slots, int num_slots, void* o, const void* o_gate,
+                                   int N, int H, int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt,
+                                   void* stream) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
-  if (state_dt != KDA_F32 && state_dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (state_dt != KDA_F32 && state_dt != KDA_BF16 && state_dt != KDA_F16) return KDA_ERR_DTYPE;
   if (N < 0 || H <= 0 || num_slots < 0) return KDA_ERR_SHAPE;
   if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
   if (!prod_fits({N, H}, INT_MAX)) return KDA_ERR_SHAPE;
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || !g || !beta || !slots || !o) return KDA_ERR_NULL;
   if (num_slots > 0 && !state_pool) return KDA_ERR_NULL;
-  if (kda::launch_decode_pool(dt == KDA_BF16, state_dt == KDA_BF16, Dk, Dv, g_group, q, k, v, g, beta, state_pool,
-                              slots, num_slots, H, o, N * H, static_cast<hipStream_t>(stream)) != hipSuccess)
+  const int state_kind = state_dt == KDA_BF16 ? 1 : (state_dt == KDA_F16 ? 2 : 0);
+  if (kda::launch_decode_pool(dt == KDA_BF16, state_kind, Dk, Dv, g_group, q, k, v, g, beta, state_pool, slots,
+                              num_slots, H, o, o_gate, N * H, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_HIP;
   return KDA_OK;
 }

@@ -29,7 +29,10 @@
 // (the state pool that bounds concurrency in the K3-Tiny-L13 card's serving
 // notes, with the state dtype as a knob).  A slot outside the pool marks an
 // inactive sequence: its output row is zero and no state is touched.  A bf16
-// pool is widened to fp32 for the step and rounded to nearest even after it.
+// or fp16 pool is widened to fp32 for the step and rounded to nearest even
+// after it.  An optional output gate (the Mini-K3-1H cards list output gates
+// among the family's operators) scales the output by sigmoid(z), one logit
+// per value channel; it never reaches the state.
 //
 // Prologue form (PRO): q and k arrive raw and are L2-normalised here, g holds
 // the gate logits f (g = -exp(A_log) softplus(f + dt_bias)) and beta the
@@ -42,6 +45,8 @@
 namespace kda {
 
 typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Four consecutive state values (fp32: one 16-byte access; bf16: one 8-byte
 // access), streamed with non-temporal loads.
@@ -52,10 +57,18 @@ __device__ __forceinline__ f32x4 load_state4(const bf16* p) {
   const bf16x4 b = __builtin_bit_cast(bf16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p)));
   return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
 }
+__device__ __forceinline__ f32x4 load_state4(const f16* p) {
+  const f16x4 h = __builtin_bit_cast(f16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p)));
+  return __builtin_convertvector(h, f32x4);
+}
 __device__ __forceinline__ void store_state4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ __forceinline__ void store_state4(bf16* p, const f32x4& x) {
   const bf16x4 b = to_bf16x4(x);  // RNE
   __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, b), reinterpret_cast<u32x2v*>(p));
+}
+__device__ __forceinline__ void store_state4(f16* p, const f32x4& x) {
+  const f16x4 h = __builtin_convertvector(x, f16x4);  // RNE (the default rounding mode)
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, h), reinterpret_cast<u32x2v*>(p));
 }
 
 template <int DK, int DV, typename T, int GG, typename SE, bool PRO>
@@ -63,7 +76,8 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
                                                           const T* __restrict__ v, const T* __restrict__ g,
                                                           const T* __restrict__ beta, SE* __restrict__ state,
                                                           const int* __restrict__ slots, int num_slots, int H,
-                                                          T* __restrict__ o, const float* __restrict__ A_log,
+                                                          T* __restrict__ o, const T* __restrict__ o_gate,
+                                                          const float* __restrict__ A_log,
                                                           const float* __restrict__ dt_bias) {
   constexpr int NT = 512;
   constexpr int CG = DV / 4;         // column groups of 4 floats
@@ -196,7 +210,11 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
   const f32x4 uu = b * (vv - et);
 
   if (rg == 0) {
-    const f32x4 out = yt + s_qk * uu;
+    f32x4 out = yt + s_qk * uu;
+    if (o_gate) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) out[c] *= sigmoid_f(to_f32(o_gate[u * DV + 4 * cg + c]));
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[u * DV + 4 * cg + c] = from_f32<T>(out[c]);
   }
@@ -215,26 +233,27 @@ struct Prologue {
 
 template <int DK, int DV, typename T, int GG, typename SE>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                                  void* state, const int* slots, int num_slots, int H, void* o, int NH,
-                                  hipStream_t stream, Prologue pro) {
+                                  void* state, const int* slots, int num_slots, int H, void* o, const void* o_gate,
+                                  int NH, hipStream_t stream, Prologue pro) {
   if (pro.A_log)
     hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, GG, SE, true>), dim3(NH), dim3(512), 0, stream, (const T*)q,
                        (const T*)k, (const T*)v, (const T*)g, (const T*)beta, (SE*)state, slots, num_slots, H,
-                       (T*)o, pro.A_log, pro.dt_bias);
+                       (T*)o, (const T*)o_gate, pro.A_log, pro.dt_bias);
   else
     hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, GG, SE, false>), dim3(NH), dim3(512), 0, stream, (const T*)q,
                        (const T*)k, (const T*)v, (const T*)g, (const T*)beta, (SE*)state, slots, num_slots, H,
-                       (T*)o, nullptr, nullptr);
+                       (T*)o, (const T*)o_gate, nullptr, nullptr);
   return hipGetLastError();
 }
 
 template <typename T, int GG, typename SE>
 static hipError_t launch_decode_g(int Dk, int Dv, const void* q, const void* k, const void* v, const void* g,
                                   const void* beta, void* state, const int* slots, int num_slots, int H, void* o,
-                                  int NH, hipStream_t stream, Prologue pro) {
+                                  const void* o_gate, int NH, hipStream_t stream, Prologue pro) {
 #define KDA_DEC(DK_, DV_)      \
   if (Dk == DK_ && Dv == DV_) \
-    return launch_decode_t<DK_, DV_, T, GG, SE>(q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro);
+    return launch_decode_t<DK_, DV_, T, GG, SE>(q, k, v, g, beta, state, slots, num_slots, H, o, o_gate, NH, stream, \
+                                                pro);
   KDA_DEC(64, 64)
   KDA_DEC(64, 128)
   KDA_DEC(128, 64)
@@ -246,36 +265,44 @@ static hipError_t launch_decode_g(int Dk, int Dv, const void* q, const void* k, 
 template <typename SE>
 static hipError_t launch_decode_s(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k,
                                   const void* v, const void* g, const void* beta, void* state, const int* slots,
-                                  int num_slots, int H, void* o, int NH, hipStream_t stream, Prologue pro = {}) {
+                                  int num_slots, int H, void* o, const void* o_gate, int NH, hipStream_t stream,
+                                  Prologue pro = {}) {
   if (bf16_io)
-    return g_group == 1
-               ? launch_decode_g<bf16, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro)
-               : launch_decode_g<bf16, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro);
-  return g_group == 1
-             ? launch_decode_g<float, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro)
-             : launch_decode_g<float, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o, NH, stream, pro);
+    return g_group == 1 ? launch_decode_g<bf16, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o,
+                                                       o_gate, NH, stream, pro)
+                        : launch_decode_g<bf16, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o,
+                                                        o_gate, NH, stream, pro);
+  return g_group == 1 ? launch_decode_g<float, 1, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o,
+                                                      o_gate, NH, stream, pro)
+                      : launch_decode_g<float, 64, SE>(Dk, Dv, q, k, v, g, beta, state, slots, num_slots, H, o,
+                                                       o_gate, NH, stream, pro);
 }
 
 hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream) {
-  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, state, nullptr, 0, 1, o, NH, stream);
+  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, state, nullptr, 0, 1, o, nullptr, NH,
+                                stream);
 }
 
 hipError_t launch_decode_prologue(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k,
                                   const void* v, const void* g, const void* beta, float* state, void* o, int N, int H,
                                   const float* A_log, const float* dt_bias, hipStream_t stream) {
-  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, state, nullptr, 0, H, o, N * H, stream,
-                                Prologue{A_log, dt_bias});
+  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, state, nullptr, 0, H, o, nullptr, N * H,
+                                stream, Prologue{A_log, dt_bias});
 }
 
-hipError_t launch_decode_pool(bool bf16_io, bool bf16_state, int Dk, int Dv, int g_group, const void* q,
+hipError_t launch_decode_pool(bool bf16_io, int state_kind, int Dk, int Dv, int g_group, const void* q,
                               const void* k, const void* v, const void* g, const void* beta, void* pool,
-                              const int* slots, int num_slots, int H, void* o, int NH, hipStream_t stream) {
-  if (bf16_state)
-    return launch_decode_s<bf16>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, NH,
-                                 stream);
-  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, NH,
-                                stream);
+                              const int* slots, int num_slots, int H, void* o, const void* o_gate, int NH,
+                              hipStream_t stream) {
+  if (state_kind == 1)
+    return launch_decode_s<bf16>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, o_gate,
+                                 NH, stream);
+  if (state_kind == 2)
+    return launch_decode_s<f16>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, o_gate,
+                                NH, stream);
+  return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, o_gate,
+                                NH, stream);
 }
 
 }  // namespace kda

@@ -22,13 +22,13 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libkda.so")
 
-KDA_F32, KDA_BF16 = 0, 1
+KDA_F32, KDA_BF16, KDA_F16 = 0, 1, 2
 _STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
 # KDA_ABI_VERSION of include/kda.h that these bindings are written for.
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_save", "kda_chunk_bwd_saved", "kda_recurrent_step", "kda_recurrent_step_pool",
             "kda_short_conv_fwd", "kda_short_conv_step", "kda_status_str", "kda_abi_version"]
@@ -76,7 +76,7 @@ def lib():
     L.kda_recurrent_step.restype = i
     L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.kda_recurrent_step_pool.restype = i
-    L.kda_recurrent_step_pool.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, vp]
+    L.kda_recurrent_step_pool.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, vp]
     L.kda_short_conv_fwd.restype = i
     L.kda_short_conv_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.kda_short_conv_step.restype = i
@@ -341,27 +341,31 @@ def recurrent_step(q, k, v, g, beta, state, out=None):
     return o
 
 
-def recurrent_step_pool(q, k, v, g, beta, state_pool, slots, out=None):
+def recurrent_step_pool(q, k, v, g, beta, state_pool, slots, out=None, o_gate=None):
     """One KDA decode step over a state pool: sequence n updates
-    state_pool[slots[n]] in place ([num_slots, H, Dk, Dv], float32 or
-    bfloat16).  A slot outside [0, num_slots) marks the sequence inactive:
-    its output row is zero and no state is touched."""
+    state_pool[slots[n]] in place ([num_slots, H, Dk, Dv], float32, bfloat16
+    or float16).  A slot outside [0, num_slots) marks the sequence inactive:
+    its output row is zero and no state is touched.  o_gate [N, H, Dv] (q's
+    dtype): logits z of the output gate, o <- o * sigmoid(z)."""
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     if g.shape[-1] <= 0 or Dk % g.shape[-1]:
         raise ValueError("g's last dim must divide Dk")
     g_group = Dk // g.shape[-1]
     dt = _dt(q)
-    sdt = _dt(state_pool)
+    sdt = KDA_F16 if state_pool.dtype == torch.float16 else _dt(state_pool)
     if slots.dtype != torch.int32 or slots.shape != (N,):
         raise TypeError("slots must be int32 of shape [N]")
     if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, Dk, Dv):
         raise ValueError("state_pool must be [num_slots, H, Dk, Dv]")
-    _check_dev(q, k, v, g, beta, state_pool, slots)
+    if o_gate is not None and (o_gate.dtype != q.dtype or tuple(o_gate.shape) != (N, H, Dv)
+                               or not o_gate.is_contiguous()):
+        raise ValueError("o_gate must be a contiguous [N, H, Dv] tensor of q's dtype")
+    _check_dev(q, k, v, g, beta, state_pool, slots, o_gate)
     o = out if out is not None else torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
     st = lib().kda_recurrent_step_pool(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
-                                       _ptr(slots), state_pool.shape[0], _ptr(o), N, H, Dk, Dv, g_group, dt, sdt,
-                                       _stream())
+                                       _ptr(slots), state_pool.shape[0], _ptr(o), _ptr(o_gate), N, H, Dk, Dv,
+                                       g_group, dt, sdt, _stream())
     if st != 0:
         raise KdaError(st, "kda_recurrent_step_pool")
     return o

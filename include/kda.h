@@ -17,8 +17,9 @@
  *   never allocates, frees or keeps a pointer after the call returns.
  * - Tensors are dense, contiguous, row-major with the shapes given below
  *   (token-major [B, T, H, D]; states [N, H, Dk, Dv] with Dv contiguous).
- * - Element type of q, k, v, g, beta and o is `dt` (KDA_F32 or KDA_BF16);
- *   states (h0, ht, state) are always float32.  bf16 is bfloat16 with
+ * - Element type of q, k, v, g, beta and o is `dt` (KDA_F32 or KDA_BF16;
+ *   KDA_F16 there is KDA_ERR_DTYPE); states (h0, ht, state) are float32,
+ *   except a serving pool's, whose type is a knob.  bf16 is bfloat16 with
  *   round-to-nearest-even on output.
  * - Supported head sizes: Dk, Dv in {64, 128}.  g_group in {1, 64} is the
  *   number of consecutive key channels that share one log-decay value
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 typedef enum {
   KDA_OK = 0,
@@ -54,7 +55,7 @@ typedef enum {
   KDA_ERR_HIP = 6          /* a HIP launch failed                                 */
 } kda_status;
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_F16 = 2 } kda_dtype;  /* KDA_F16: pool state only */
 
 /* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 when no
  * workspace is needed: without cu_seqlens).  num_seqs is the number of
@@ -213,6 +214,11 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
  * writes pool slot slots[n]; the step itself is the one of kda_recurrent_step.
  *
  *   q, k, v, g, beta, o   as for kda_recurrent_step ([N, H, ...], dt);
+ *   o_gate [N, H, Dv] dt, or NULL: logits z of the output gate.  The
+ *          Mini-K3-1H model cards list output gates among the family's
+ *          operators without a formula; it is read as the elementwise
+ *          logistic gate o <- o * sigmoid(z) on the step's output.  It
+ *          never reaches the state; an inactive sequence's row stays zero.
  *   state_pool  [num_slots, H, Dk, Dv] of state_dt, updated in place for the
  *          slots named by active sequences; every other slot is untouched.
  *   slots  device int32 [N]: the pool slot of each sequence.  A value outside
@@ -220,15 +226,17 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
  *          as zeros and no state is read or written.  Two active sequences
  *          must not name the same slot (their updates would race).
  *   num_slots  pool size (>= 0; state_pool may be NULL when it is 0).
- *   state_dt   KDA_F32 or KDA_BF16.  A bf16 state is widened to fp32 for
- *          the step and rounded to nearest even when written back.
+ *   state_dt   KDA_F32, KDA_BF16 or KDA_F16.  A bf16 or fp16 state is
+ *          widened to fp32 for the step and rounded to nearest even when
+ *          written back (fp16: IEEE binary16, overflow to infinity).
  * N = 0 is a no-op.  Errors: KDA_ERR_NULL (q, k, v, g, beta, slots or o NULL,
  * or state_pool NULL with num_slots > 0), KDA_ERR_SHAPE, KDA_ERR_DTYPE (dt
  * or state_dt), KDA_ERR_UNSUPPORTED, KDA_ERR_HIP as elsewhere.
  */
 kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                                   void* state_pool, const int* slots, int num_slots, void* o, int N, int H,
-                                   int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt, void* stream);
+                                   void* state_pool, const int* slots, int num_slots, void* o, const void* o_gate,
+                                   int N, int H, int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt,
+                                   void* stream);
 
 /* Short causal depthwise convolution along the token axis, with document
  * reset.  The miniKimiK3 card ("Limitations") says order information reaches

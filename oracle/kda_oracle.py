@@ -35,6 +35,9 @@ Readings where the pages are silent:
   g = log(alpha) <= 0 and beta arrive ready to use.
 * With cu_seqlens each document starts from h0[doc] (zeros if absent) and
   returns its own final state; a zero-length document returns h0[doc].
+* The serving pool's output gate (the Mini-K3-1H cards list output gates
+  without a formula) is the elementwise logistic gate o * sigmoid(z) on the
+  step's output; it never reaches the state.
 
 Layouts follow the library: q, k [B, T, H, dk]; v [B, T, H, dv];
 g [B, T, H, dk // g_group]; beta [B, T, H]; state [N, H, dk, dv].

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 6 == kda.ABI_VERSION
+    assert L.kda_abi_version() == 7 == kda.ABI_VERSION
     for s in range(7):
         assert L.kda_status_str(s).decode().startswith(("KDA_OK", "KDA_ERR"))
     assert L.kda_status_str(99)
@@ -94,9 +94,10 @@ def test_recurrent_step_validation():
 def test_recurrent_step_pool_validation():
     L = kda.lib()
     step = lambda q=P, pool=P, slots=P, ns=4, N=1, H=1, Dk=64, Dv=64, gg=1, dt=1, sdt=1: L.kda_recurrent_step_pool(
-        q, P, P, P, P, pool, slots, ns, P, N, H, Dk, Dv, gg, dt, sdt, None)
-    assert step(dt=2) == DTYPE
+        q, P, P, P, P, pool, slots, ns, P, None, N, H, Dk, Dv, gg, dt, sdt, None)
+    assert step(dt=2) == DTYPE                        # float16 is a pool state type only
     assert step(sdt=5) == DTYPE
+    assert step(sdt=2, N=0, q=None, pool=None, slots=None) == OK  # a float16 pool is accepted
     assert step(N=-1) == SHAPE
     assert step(H=0) == SHAPE
     assert step(ns=-1) == SHAPE

@@ -1,5 +1,6 @@
 """Serving-pool decode step on the GPU (through the C-ABI) against the CPU
-oracle: slot indirection, inactive sequences, and a bfloat16 state pool."""
+oracle: slot indirection, inactive sequences, bfloat16 and float16 state
+pools, and the output gate."""
 
 import numpy as np
 import pytest
@@ -98,3 +99,53 @@ def test_k3_pool_bf16_state_sampled():
         assert_close("k3 pool o step %d" % s, o.cpu()[seqs][:, heads], o_ref, torch.bfloat16)
     got = pool.cpu()[torch.from_numpy(perm[seqs]).long()][:, heads]
     assert_close("k3 pool state", got, S, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dk,dv,io", [(64, 64, "bf16"), (128, 128, "bf16"), (128, 64, "f32")])
+def test_pool_f16_state_steps(dk, dv, io):
+    N, H, steps = 5, 3, 12
+    r = inputs.make_decode(N, H, dk, dv, steps=steps, dtype=io, g_group=1, seed=340 + dk + dv)
+    ns = N + 2
+    slots = np.array([6, 2, 0, 3, 5], dtype=np.int32)
+    pool0 = torch.from_numpy(orc.round_f16(np.random.default_rng(14).standard_normal((ns, H, dk, dv)) * 0.02))
+    pool = pool0.to(torch.float16).cuda()
+    ref_pool = f64(pool0)
+    sl = torch.from_numpy(slots).cuda()
+    tol = torch.bfloat16 if io == "bf16" else torch.float16
+    for s, st in enumerate(r["steps"]):
+        d = _dev(st)
+        o = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, sl)
+        ref_pool, ref_o = orc.kda_decode_step_pool(ref_pool, slots, f64(st["q"]), f64(st["k"]), f64(st["v"]),
+                                                   f64(st["g"]), f64(st["beta"]), state_dtype="f16")
+        torch.cuda.synchronize()
+        assert_close("o step %d" % s, o.cpu(), ref_o, torch.bfloat16)
+    assert_close("f16 pool", pool.cpu()[slots], ref_pool[slots], tol)
+    untouched = [s for s in range(ns) if s not in slots]
+    assert torch.equal(pool.cpu()[untouched], pool0.to(torch.float16)[untouched])
+
+
+@pytest.mark.parametrize("sdt", [torch.float32, torch.bfloat16])
+def test_pool_output_gate(sdt):
+    N, H, dk, dv, ns = 6, 2, 128, 128, 8
+    r = inputs.make_decode(N, H, dk, dv, steps=1, dtype="bf16", g_group=1, seed=350)
+    st = r["steps"][0]
+    d = _dev(st)
+    z = torch.from_numpy(np.random.default_rng(15).standard_normal((N, H, dv)) * 2).to(torch.bfloat16)
+    slots = np.array([7, -1, 0, 3, ns, 5], dtype=np.int32)
+    sl = torch.from_numpy(slots).cuda()
+    base = torch.from_numpy(np.random.default_rng(16).standard_normal((ns, H, dk, dv)) * 0.02).to(sdt)
+    pool_g, pool_n, pool_0 = base.cuda(), base.cuda(), base.cuda()
+    o_g = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool_g, sl, o_gate=z.cuda())
+    o_n = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool_n, sl)
+    o_0 = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool_0, sl,
+                                  o_gate=torch.zeros((N, H, dv), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(pool_g, pool_n) and torch.equal(pool_0, pool_n)  # the gate never reaches the state
+    assert torch.equal(o_0, o_n / 2)                                     # sigmoid(0) = 1/2, exact in bf16
+    ref_pool, ref_o = orc.kda_decode_step_pool(f64(base), slots, f64(st["q"]), f64(st["k"]), f64(st["v"]),
+                                               f64(st["g"]), f64(st["beta"]),
+                                               state_dtype="bf16" if sdt == torch.bfloat16 else "f32",
+                                               o_gate=f64(z))
+    active = [n for n in range(N) if 0 <= slots[n] < ns]
+    assert_close("gated o", o_g.cpu()[active], ref_o[active], torch.bfloat16)
+    assert torch.all(o_g.cpu()[[n for n in range(N) if n not in active]] == 0)
