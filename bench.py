@@ -343,6 +343,7 @@ def main():
         },
         "prefill": {
             "tokens_per_s": B * T / (pre_avg * 1e-3),
+            "head_tokens_per_s": B * T * H / (pre_avg * 1e-3),
             "ms": pre_avg,
             "ms_min": min(pre_ms),
             "ms_median": pct(pre_ms, 50),
@@ -354,6 +355,7 @@ def main():
         },
         "decode": {
             "tokens_per_s": N / (dec_avg * 1e-3),
+            "head_tokens_per_s": N * H / (dec_avg * 1e-3),
             "ms_per_step": dec_avg,
             "ms_min": min(dec_ms),
             "ms_median": pct(dec_ms, 50),
