@@ -124,13 +124,14 @@ def test_pool_f16_state_steps(dk, dv, io):
     assert torch.equal(pool.cpu()[untouched], pool0.to(torch.float16)[untouched])
 
 
-@pytest.mark.parametrize("sdt", [torch.float32, torch.bfloat16])
-def test_pool_output_gate(sdt):
+@pytest.mark.parametrize("sdt,io", [(torch.float32, "bf16"), (torch.bfloat16, "bf16"), (torch.float32, "f32")])
+def test_pool_output_gate(sdt, io):
     N, H, dk, dv, ns = 6, 2, 128, 128, 8
-    r = inputs.make_decode(N, H, dk, dv, steps=1, dtype="bf16", g_group=1, seed=350)
+    r = inputs.make_decode(N, H, dk, dv, steps=1, dtype=io, g_group=1, seed=350)
     st = r["steps"][0]
     d = _dev(st)
-    z = torch.from_numpy(np.random.default_rng(15).standard_normal((N, H, dv)) * 2).to(torch.bfloat16)
+    zt = torch.bfloat16 if io == "bf16" else torch.float32
+    z = torch.from_numpy(np.random.default_rng(15).standard_normal((N, H, dv)) * 2).to(zt)
     slots = np.array([7, -1, 0, 3, ns, 5], dtype=np.int32)
     sl = torch.from_numpy(slots).cuda()
     base = torch.from_numpy(np.random.default_rng(16).standard_normal((ns, H, dk, dv)) * 0.02).to(sdt)
@@ -138,14 +139,14 @@ def test_pool_output_gate(sdt):
     o_g = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool_g, sl, o_gate=z.cuda())
     o_n = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool_n, sl)
     o_0 = kda.recurrent_step_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], pool_0, sl,
-                                  o_gate=torch.zeros((N, H, dv), dtype=torch.bfloat16, device="cuda"))
+                                  o_gate=torch.zeros((N, H, dv), dtype=zt, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(pool_g, pool_n) and torch.equal(pool_0, pool_n)  # the gate never reaches the state
-    assert torch.equal(o_0, o_n / 2)                                     # sigmoid(0) = 1/2, exact in bf16
+    assert torch.equal(o_0, o_n / 2)                                     # sigmoid(0) = 1/2, exact halving
     ref_pool, ref_o = orc.kda_decode_step_pool(f64(base), slots, f64(st["q"]), f64(st["k"]), f64(st["v"]),
                                                f64(st["g"]), f64(st["beta"]),
                                                state_dtype="bf16" if sdt == torch.bfloat16 else "f32",
                                                o_gate=f64(z))
     active = [n for n in range(N) if 0 <= slots[n] < ns]
-    assert_close("gated o", o_g.cpu()[active], ref_o[active], torch.bfloat16)
+    assert_close("gated o", o_g.cpu()[active], ref_o[active], torch.bfloat16 if io == "bf16" else torch.float32)
     assert torch.all(o_g.cpu()[[n for n in range(N) if n not in active]] == 0)
