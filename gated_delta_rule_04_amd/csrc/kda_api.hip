@@ -183,10 +183,13 @@ kda_status kda_recurrent_step_prologue(const void* q_raw, const void* k_raw, con
   return KDA_OK;
 }
 
-kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                                   void* state_pool, const int* slots, int num_slots, void* o, const void* o_gate,
-                                   int N, int H, int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt,
-                                   void* stream) {
+}  // extern "C"
+
+namespace {
+kda_status step_pool_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const float* A_log, const float* dt_bias, void* state_pool, const int* slots,
+                          int num_slots, void* o, const void* o_gate, int N, int H, int Dk, int Dv, int g_group,
+                          kda_dtype dt, kda_dtype state_dt, void* stream) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
   if (state_dt != KDA_F32 && state_dt != KDA_BF16 && state_dt != KDA_F16) return KDA_ERR_DTYPE;
   if (N < 0 || H <= 0 || num_slots < 0) return KDA_ERR_SHAPE;
@@ -197,9 +200,32 @@ kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, 
   if (num_slots > 0 && !state_pool) return KDA_ERR_NULL;
   const int state_kind = state_dt == KDA_BF16 ? 1 : (state_dt == KDA_F16 ? 2 : 0);
   if (kda::launch_decode_pool(dt == KDA_BF16, state_kind, Dk, Dv, g_group, q, k, v, g, beta, state_pool, slots,
-                              num_slots, H, o, o_gate, N * H, static_cast<hipStream_t>(stream)) != hipSuccess)
+                              num_slots, H, o, o_gate, N * H, A_log, dt_bias,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_HIP;
   return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                   void* state_pool, const int* slots, int num_slots, void* o, const void* o_gate,
+                                   int N, int H, int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt,
+                                   void* stream) {
+  return step_pool_impl(q, k, v, g, beta, nullptr, nullptr, state_pool, slots, num_slots, o, o_gate, N, H, Dk, Dv,
+                        g_group, dt, state_dt, stream);
+}
+
+kda_status kda_recurrent_step_pool_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
+                                            const void* b_raw, const float* A_log, const float* dt_bias,
+                                            void* state_pool, const int* slots, int num_slots, void* o,
+                                            const void* o_gate, int N, int H, int Dk, int Dv, int g_group,
+                                            kda_dtype dt, kda_dtype state_dt, void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (N > 0 && H > 0 && (!A_log || !dt_bias)) return KDA_ERR_NULL;
+  return step_pool_impl(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, state_pool, slots, num_slots, o, o_gate, N, H,
+                        Dk, Dv, g_group, dt, state_dt, stream);
 }
 
 static bool conv_dims_ok(int C, int W) { return C > 0 && C % 8 == 0 && W >= 1 && W <= 8; }

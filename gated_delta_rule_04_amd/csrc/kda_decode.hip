@@ -294,15 +294,16 @@ hipError_t launch_decode_prologue(bool bf16_io, int Dk, int Dv, int g_group, con
 hipError_t launch_decode_pool(bool bf16_io, int state_kind, int Dk, int Dv, int g_group, const void* q,
                               const void* k, const void* v, const void* g, const void* beta, void* pool,
                               const int* slots, int num_slots, int H, void* o, const void* o_gate, int NH,
-                              hipStream_t stream) {
+                              const float* A_log, const float* dt_bias, hipStream_t stream) {
+  const Prologue pro{A_log, dt_bias};
   if (state_kind == 1)
     return launch_decode_s<bf16>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, o_gate,
-                                 NH, stream);
+                                 NH, stream, pro);
   if (state_kind == 2)
     return launch_decode_s<f16>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, o_gate,
-                                NH, stream);
+                                NH, stream, pro);
   return launch_decode_s<float>(bf16_io, Dk, Dv, g_group, q, k, v, g, beta, pool, slots, num_slots, H, o, o_gate,
-                                NH, stream);
+                                NH, stream, pro);
 }
 
 }  // namespace kda

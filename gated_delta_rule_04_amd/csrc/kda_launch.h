@@ -64,11 +64,12 @@ hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* 
 hipError_t launch_decode_prologue(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k,
                                   const void* v, const void* g, const void* beta, float* state, void* o, int N, int H,
                                   const float* A_log, const float* dt_bias, hipStream_t stream);
-// state_kind: 0 fp32, 1 bf16, 2 fp16 pool; o_gate NULL or the output gate's logits [N, H, Dv]
+// state_kind: 0 fp32, 1 bf16, 2 fp16 pool; o_gate NULL or the output gate's logits [N, H, Dv];
+// A_log NULL for prepared inputs, else the prologue's gate parameters (raw q, k, f, b)
 hipError_t launch_decode_pool(bool bf16_io, int state_kind, int Dk, int Dv, int g_group, const void* q,
                               const void* k, const void* v, const void* g, const void* beta, void* pool,
                               const int* slots, int num_slots, int H, void* o, const void* o_gate, int NH,
-                              hipStream_t stream);
+                              const float* A_log, const float* dt_bias, hipStream_t stream);
 hipError_t launch_short_conv_fwd(bool bf16_io, const void* x, const void* weight, const void* conv0, void* y,
                                  void* conv_final, const int* cu, int num_seqs, int B, int T, int C, int W,
                                  hipStream_t s);

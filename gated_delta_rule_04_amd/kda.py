@@ -28,9 +28,9 @@ _STATUS = {
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
 # KDA_ABI_VERSION of include/kda.h that these bindings are written for.
-ABI_VERSION = 7
+ABI_VERSION = 8
 
-EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_save", "kda_chunk_bwd_saved", "kda_recurrent_step", "kda_recurrent_step_pool",
+EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_save", "kda_chunk_bwd_saved", "kda_recurrent_step", "kda_recurrent_step_pool", "kda_recurrent_step_pool_prologue",
             "kda_short_conv_fwd", "kda_short_conv_step", "kda_status_str", "kda_abi_version"]
 
 _lib = None
@@ -77,6 +77,8 @@ def lib():
     L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.kda_recurrent_step_pool.restype = i
     L.kda_recurrent_step_pool.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, vp]
+    L.kda_recurrent_step_pool_prologue.restype = i
+    L.kda_recurrent_step_pool_prologue.argtypes = [vp] * 9 + [i, vp, vp, i, i, i, i, i, i, i, vp]
     L.kda_short_conv_fwd.restype = i
     L.kda_short_conv_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.kda_short_conv_step.restype = i
@@ -368,6 +370,39 @@ def recurrent_step_pool(q, k, v, g, beta, state_pool, slots, out=None, o_gate=No
                                        g_group, dt, sdt, _stream())
     if st != 0:
         raise KdaError(st, "kda_recurrent_step_pool")
+    return o
+
+
+def recurrent_step_pool_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, state_pool, slots, out=None,
+                                 o_gate=None):
+    """recurrent_step_pool on raw projections: the fused prologue (q, k L2
+    norm; g = -exp(A_log) softplus(f + dt_bias); beta = sigmoid(b_raw)) and
+    one decode step over a state pool, with the optional output gate."""
+    N, H, Dk = q_raw.shape
+    Dv = v.shape[-1]
+    if f.shape[-1] <= 0 or Dk % f.shape[-1]:
+        raise ValueError("f's last dim must divide Dk")
+    g_group = Dk // f.shape[-1]
+    dt = _dt(q_raw)
+    for t in (k_raw, v, f, b_raw):
+        if t.dtype != q_raw.dtype:
+            raise TypeError("q_raw, k_raw, v, f, b_raw must share one dtype")
+    _gate_params(A_log, dt_bias, H, f.shape[-1])
+    sdt = KDA_F16 if state_pool.dtype == torch.float16 else _dt(state_pool)
+    if slots.dtype != torch.int32 or slots.shape != (N,):
+        raise TypeError("slots must be int32 of shape [N]")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, Dk, Dv):
+        raise ValueError("state_pool must be [num_slots, H, Dk, Dv]")
+    if o_gate is not None and (o_gate.dtype != q_raw.dtype or tuple(o_gate.shape) != (N, H, Dv)):
+        raise ValueError("o_gate must be an [N, H, Dv] tensor of q_raw's dtype")
+    o = out if out is not None else torch.empty((N, H, Dv), dtype=q_raw.dtype, device=q_raw.device)
+    _check_dev(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, state_pool, slots, o, o_gate)
+    st = lib().kda_recurrent_step_pool_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(f), _ptr(b_raw),
+                                                _ptr(A_log), _ptr(dt_bias), _ptr(state_pool), _ptr(slots),
+                                                state_pool.shape[0], _ptr(o), _ptr(o_gate), N, H, Dk, Dv, g_group,
+                                                dt, sdt, _stream())
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_step_pool_prologue")
     return o
 
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 
 typedef enum {
   KDA_OK = 0,
@@ -237,6 +237,24 @@ kda_status kda_recurrent_step_pool(const void* q, const void* k, const void* v, 
                                    void* state_pool, const int* slots, int num_slots, void* o, const void* o_gate,
                                    int N, int H, int Dk, int Dv, int g_group, kda_dtype dt, kda_dtype state_dt,
                                    void* stream);
+
+/* The serving-pool decode step with the fused gate and normalisation
+ * prologue: kda_recurrent_step_pool on raw projections, as
+ * kda_recurrent_step_prologue is kda_recurrent_step on raw projections.
+ *
+ *   q_raw, k_raw, v, f, b_raw, A_log, dt_bias   as for
+ *          kda_recurrent_step_prologue ([N, H, ...] dt; A_log and dt_bias
+ *          f32 [H, Dk/g_group]);
+ *   state_pool, slots, num_slots, o, o_gate, state_dt   as for
+ *          kda_recurrent_step_pool.
+ * N = 0 is a no-op.  Errors as for kda_recurrent_step_pool, plus
+ * KDA_ERR_NULL for a NULL A_log or dt_bias when N > 0.
+ */
+kda_status kda_recurrent_step_pool_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
+                                            const void* b_raw, const float* A_log, const float* dt_bias,
+                                            void* state_pool, const int* slots, int num_slots, void* o,
+                                            const void* o_gate, int N, int H, int Dk, int Dv, int g_group,
+                                            kda_dtype dt, kda_dtype state_dt, void* stream);
 
 /* Short causal depthwise convolution along the token axis, with document
  * reset.  The miniKimiK3 card ("Limitations") says order information reaches

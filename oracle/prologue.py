@@ -29,12 +29,12 @@ the prepared inputs.
 
 import numpy as np
 
-from .kda_oracle import kda_decode_step, kda_forward
+from .kda_oracle import kda_decode_step, kda_decode_step_pool, kda_forward
 
 EPS = 1e-6
 
 __all__ = ["EPS", "l2_normalize", "softplus", "sigmoid", "gate", "prepare", "kda_forward_prologue",
-           "kda_decode_step_prologue"]
+           "kda_decode_step_prologue", "kda_decode_step_pool_prologue"]
 
 
 def l2_normalize(x, eps=EPS):
@@ -77,3 +77,12 @@ def kda_decode_step_prologue(state, q_raw, k_raw, v, f, b_raw, A_log, dt_bias, g
     """The prologue followed by one decode step ([N, H, ...] inputs)."""
     q, k, g, beta = prepare(q_raw, k_raw, f, b_raw, A_log, dt_bias)
     return kda_decode_step(state, q, k, v, g, beta, g_group=g_group)
+
+
+def kda_decode_step_pool_prologue(pool, slots, q_raw, k_raw, v, f, b_raw, A_log, dt_bias, g_group=1,
+                                  state_dtype=None, o_gate=None):
+    """The prologue followed by one serving-pool decode step (see
+    kda_decode_step_pool for the slots, the state dtype and the output gate)."""
+    q, k, g, beta = prepare(q_raw, k_raw, f, b_raw, A_log, dt_bias)
+    return kda_decode_step_pool(pool, slots, q, k, v, g, beta, g_group=g_group, state_dtype=state_dtype,
+                                o_gate=o_gate)

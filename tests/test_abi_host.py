@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 7 == kda.ABI_VERSION
+    assert L.kda_abi_version() == 8 == kda.ABI_VERSION
     for s in range(7):
         assert L.kda_status_str(s).decode().startswith(("KDA_OK", "KDA_ERR"))
     assert L.kda_status_str(99)
@@ -107,6 +107,19 @@ def test_recurrent_step_pool_validation():
     assert step(slots=None) == NULL
     assert step(pool=None) == NULL                    # a pool is required when num_slots > 0
     assert step(N=0, q=None, pool=None, slots=None) == OK
+
+
+def test_recurrent_step_pool_prologue_validation():
+    L = kda.lib()
+    step = lambda q=P, A=P, pool=P, slots=P, ns=4, N=1, H=1, dt=1, sdt=1: L.kda_recurrent_step_pool_prologue(
+        q, P, P, P, P, A, P, pool, slots, ns, P, None, N, H, 64, 64, 1, dt, sdt, None)
+    assert step(dt=2) == DTYPE
+    assert step(sdt=5) == DTYPE
+    assert step(A=None) == NULL
+    assert step(q=None) == NULL
+    assert step(pool=None) == NULL
+    assert step(H=0) == SHAPE
+    assert step(N=0, q=None, A=None, pool=None, slots=None) == OK
 
 
 def test_chunk_bwd_validation():

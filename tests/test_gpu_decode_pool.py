@@ -150,3 +150,40 @@ def test_pool_output_gate(sdt, io):
     active = [n for n in range(N) if 0 <= slots[n] < ns]
     assert_close("gated o", o_g.cpu()[active], ref_o[active], torch.bfloat16 if io == "bf16" else torch.float32)
     assert torch.all(o_g.cpu()[[n for n in range(N) if n not in active]] == 0)
+
+
+@pytest.mark.parametrize("sdt", [torch.float32, torch.bfloat16])
+def test_pool_prologue(sdt):
+    """Raw projections into a pool: identity slots with an fp32 pool are
+    bitwise the plain prologue step; permuted and inactive slots, a bf16 pool
+    and the output gate against the oracle."""
+    import oracle.prologue as pro
+    N, H, dk, dv, ns = 5, 3, 128, 64, 7
+    d = inputs.make_prologue(1, N, H, dk, dv, "bf16", g_group=1, seed=60)
+    q, k, v, f, b = (d[n][0] for n in ("q_raw", "k_raw", "v", "f", "b_raw"))
+    dev = lambda t: t.cuda()
+    A, D = dev(d["A_log"]), dev(d["dt_bias"])
+    base = torch.from_numpy(np.random.default_rng(17).standard_normal((ns, H, dk, dv)) * 0.02).to(sdt)
+    if sdt == torch.float32:
+        a, p = base[:N].clone().cuda(), base[:N].clone().cuda()
+        o1 = kda.recurrent_step_prologue(dev(q), dev(k), dev(v), dev(f), dev(b), A, D, a)
+        o2 = kda.recurrent_step_pool_prologue(dev(q), dev(k), dev(v), dev(f), dev(b), A, D, p,
+                                              torch.arange(N, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(a, p)
+    slots = np.array([6, -1, 2, 0, 4], dtype=np.int32)
+    z = torch.from_numpy(np.random.default_rng(18).standard_normal((N, H, dv))).to(torch.bfloat16)
+    pool = base.cuda()
+    o = kda.recurrent_step_pool_prologue(dev(q), dev(k), dev(v), dev(f), dev(b), A, D, pool,
+                                         torch.from_numpy(slots).cuda(), o_gate=z.cuda())
+    torch.cuda.synchronize()
+    ref_pool, ref_o = pro.kda_decode_step_pool_prologue(
+        f64(base), slots, f64(q), f64(k), f64(v), f64(f), f64(b), f64(d["A_log"]), f64(d["dt_bias"]),
+        state_dtype="bf16" if sdt == torch.bfloat16 else "f32", o_gate=f64(z))
+    active = [n for n in range(N) if 0 <= slots[n] < ns]
+    assert_close("pool prologue o", o.cpu()[active], ref_o[active], torch.bfloat16)
+    assert torch.all(o.cpu()[1] == 0)
+    used = sorted(int(slots[n]) for n in active)
+    assert_close("pool prologue state", pool.cpu()[used], ref_pool[used], torch.bfloat16)
+    untouched = [s for s in range(ns) if s not in used]
+    assert torch.equal(pool.cpu()[untouched], base[untouched])

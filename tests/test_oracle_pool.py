@@ -115,3 +115,23 @@ def test_pool_step_f16_state_is_the_rounded_exact_step():
     assert not np.array_equal(new, exact)
     # float16 keeps 3 more significant bits than bfloat16
     assert np.abs(new - exact).max() < np.abs(orc.round_bf16(exact) - exact).max()
+
+
+def test_pool_prologue_step_is_the_prologue_step_in_each_slot():
+    import oracle.prologue as pro
+    rng = np.random.default_rng(45)
+    N, H, dk, dv = 4, 2, 8, 8
+    q, k = rng.standard_normal((N, H, dk)) * 3, rng.standard_normal((N, H, dk))
+    v, f, b = rng.standard_normal((N, H, dv)), rng.standard_normal((N, H, dk)), rng.standard_normal((N, H))
+    A_log, dt_bias = 0.3 * rng.standard_normal((H, dk)), -2 + 0.3 * rng.standard_normal((H, dk))
+    pool = rng.standard_normal((5, H, dk, dv)) * 0.1
+    slots = np.array([2, -1, 4, 0])
+    new, o = pro.kda_decode_step_pool_prologue(pool, slots, q, k, v, f, b, A_log, dt_bias)
+    for n, s in enumerate(slots):
+        if s < 0:
+            assert np.all(o[n] == 0)
+            continue
+        S1, o1 = pro.kda_decode_step_prologue(pool[s][None], q[n:n + 1], k[n:n + 1], v[n:n + 1], f[n:n + 1],
+                                              b[n:n + 1], A_log, dt_bias)
+        assert np.array_equal(new[s], S1[0]) and np.array_equal(o[n], o1[0])
+    assert np.array_equal(new[[1, 3]], pool[[1, 3]])
