@@ -109,6 +109,56 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(t, shape, name):
+    """Raise ValueError unless tensor t (if given) has exactly this shape.  The
+    kernels size every access from q's sizes, so a smaller tensor would be
+    read or written out of bounds on the device."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _prefill_shapes(q, k, v, g, beta, g_name="g"):
+    """Sizes (B, T, H, Dk, Dv, g_group) of a prefill call, after checking that
+    k, v, g and beta agree with q."""
+    if q.dim() != 4 or v.dim() != 4 or g.dim() != 4:
+        raise ValueError("q, k, v and %s must be 4-d [B, T, H, D]" % g_name)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
+        raise ValueError("%s's last dim must divide Dk" % g_name)
+    _expect(k, (B, T, H, Dk), "k")
+    _expect(v, (B, T, H, Dv), "v")
+    _expect(g, (B, T, H, g.shape[-1]), g_name)
+    _expect(beta, (B, T, H), "beta")
+    return B, T, H, Dk, Dv, Dk // g.shape[-1]
+
+
+def _decode_shapes(q, k, v, g, beta, g_name="g"):
+    """Sizes (N, H, Dk, Dv, g_group) of a decode call, after checking that
+    k, v, g and beta agree with q."""
+    if q.dim() != 3 or v.dim() != 3 or g.dim() != 3:
+        raise ValueError("q, k, v and %s must be 3-d [N, H, D]" % g_name)
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
+        raise ValueError("%s's last dim must divide Dk" % g_name)
+    _expect(k, (N, H, Dk), "k")
+    _expect(v, (N, H, Dv), "v")
+    _expect(g, (N, H, g.shape[-1]), g_name)
+    _expect(beta, (N, H), "beta")
+    return N, H, Dk, Dv, Dk // g.shape[-1]
+
+
+def _num_seqs(B, cu_seqlens):
+    if cu_seqlens is None:
+        return B
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise TypeError("cu_seqlens must be a 1-d int32 tensor [num_seqs + 1]")
+    if B != 1:
+        raise ValueError("packed documents (cu_seqlens) need B == 1")
+    return cu_seqlens.numel() - 1
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -121,23 +171,21 @@ def workspace_bytes(B, T, H, Dk, Dv, num_seqs, varlen, dtype):
 def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=False, cu_seqlens=None, out=None,
               final_state=None, workspace=None):
     """Chunked KDA prefill.  Returns (o, ht) -- ht is None unless requested."""
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
-        raise ValueError("g's last dim must divide Dk")
-    g_group = Dk // g.shape[-1]
+    B, T, H, Dk, Dv, g_group = _prefill_shapes(q, k, v, g, beta)
     dt = _dt(q)
     for t in (k, v, g, beta):
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, g, beta must share one dtype")
     if initial_state is not None and initial_state.dtype != torch.float32:
         raise TypeError("initial_state must be float32")
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
+    N = _num_seqs(B, cu_seqlens)
+    _expect(initial_state, (N, H, Dk, Dv), "initial_state")
+    _expect(out, (B, T, H, Dv), "out")
+    _expect(final_state, (N, H, Dk, Dv), "final_state")
+    if out is not None and out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
+    if final_state is not None and final_state.dtype != torch.float32:
+        raise TypeError("final_state must be float32")
     _check_dev(q, k, v, g, beta, initial_state, cu_seqlens)
     o = out if out is not None else torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
     ht = final_state
@@ -169,11 +217,7 @@ def chunk_fwd_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, initial_state=
     """Chunked prefill with the fused prologue (bf16): q, k L2-normalised per
     token, g = -exp(A_log) softplus(f + dt_bias), beta = sigmoid(b_raw), all
     inside the kernel.  Returns (o, ht)."""
-    B, T, H, Dk = q_raw.shape
-    Dv = v.shape[-1]
-    if f.shape[-1] <= 0 or Dk % f.shape[-1]:
-        raise ValueError("f's last dim must divide Dk")
-    g_group = Dk // f.shape[-1]
+    B, T, H, Dk, Dv, g_group = _prefill_shapes(q_raw, k_raw, v, f, b_raw, g_name="f")
     dt = _dt(q_raw)
     for t in (k_raw, v, f, b_raw):
         if t.dtype != q_raw.dtype:
@@ -181,12 +225,14 @@ def chunk_fwd_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, initial_state=
     _gate_params(A_log, dt_bias, H, f.shape[-1])
     if initial_state is not None and initial_state.dtype != torch.float32:
         raise TypeError("initial_state must be float32")
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
+    N = _num_seqs(B, cu_seqlens)
+    _expect(initial_state, (N, H, Dk, Dv), "initial_state")
+    _expect(out, (B, T, H, Dv), "out")
+    _expect(final_state, (N, H, Dk, Dv), "final_state")
+    if out is not None and out.dtype != q_raw.dtype:
+        raise TypeError("out must have q_raw's dtype")
+    if final_state is not None and final_state.dtype != torch.float32:
+        raise TypeError("final_state must be float32")
     _check_dev(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, initial_state, cu_seqlens)
     o = out if out is not None else torch.empty((B, T, H, Dv), dtype=q_raw.dtype, device=q_raw.device)
     ht = final_state
@@ -209,11 +255,7 @@ def chunk_fwd_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, initial_state=
 def recurrent_step_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, state, out=None):
     """One decode step with the fused prologue; state [N, H, Dk, Dv] float32
     updated in place.  Returns o [N, H, Dv]."""
-    N, H, Dk = q_raw.shape
-    Dv = v.shape[-1]
-    if f.shape[-1] <= 0 or Dk % f.shape[-1]:
-        raise ValueError("f's last dim must divide Dk")
-    g_group = Dk // f.shape[-1]
+    N, H, Dk, Dv, g_group = _decode_shapes(q_raw, k_raw, v, f, b_raw, g_name="f")
     dt = _dt(q_raw)
     for t in (k_raw, v, f, b_raw):
         if t.dtype != q_raw.dtype:
@@ -221,6 +263,10 @@ def recurrent_step_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, state, ou
     _gate_params(A_log, dt_bias, H, f.shape[-1])
     if state.dtype != torch.float32:
         raise TypeError("state must be float32")
+    _expect(state, (N, H, Dk, Dv), "state")
+    _expect(out, (N, H, Dv), "out")
+    if out is not None and out.dtype != q_raw.dtype:
+        raise TypeError("out must have q_raw's dtype")
     o = out if out is not None else torch.empty((N, H, Dv), dtype=q_raw.dtype, device=q_raw.device)
     _check_dev(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, state, o)
     st = lib().kda_recurrent_step_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(f), _ptr(b_raw), _ptr(A_log),
@@ -242,23 +288,21 @@ def chunk_fwd_save(q, k, v, g, beta, initial_state=None, output_final_state=Fals
     """chunk_fwd (bf16) that also keeps the chunk states for the backward in
     a backward workspace.  Returns (o, ht, workspace); pass the workspace to
     chunk_bwd(..., workspace=..., states_saved=True) with the same inputs."""
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
-        raise ValueError("g's last dim must divide Dk")
-    g_group = Dk // g.shape[-1]
+    B, T, H, Dk, Dv, g_group = _prefill_shapes(q, k, v, g, beta)
     dt = _dt(q)
     for t in (k, v, g, beta):
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, g, beta must share one dtype")
     if initial_state is not None and initial_state.dtype != torch.float32:
         raise TypeError("initial_state must be float32")
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
+    N = _num_seqs(B, cu_seqlens)
+    _expect(initial_state, (N, H, Dk, Dv), "initial_state")
+    _expect(out, (B, T, H, Dv), "out")
+    _expect(final_state, (N, H, Dk, Dv), "final_state")
+    if out is not None and out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
+    if final_state is not None and final_state.dtype != torch.float32:
+        raise TypeError("final_state must be float32")
     _check_dev(q, k, v, g, beta, initial_state, cu_seqlens)
     o = out if out is not None else torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
     ht = final_state
@@ -283,11 +327,7 @@ def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=Non
     initial_state, cu_seqlens) (bf16 inputs).  Returns a dict with dq, dk,
     dv, dg, dbeta (bf16, shaped like the inputs) and dh0 (float32
     [N, H, Dk, Dv]).  `out` may hold preallocated tensors under those names."""
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
-        raise ValueError("g's last dim must divide Dk")
-    g_group = Dk // g.shape[-1]
+    B, T, H, Dk, Dv, g_group = _prefill_shapes(q, k, v, g, beta)
     dt = _dt(q)
     for t in (k, v, g, beta, do):
         if t.dtype != q.dtype:
@@ -295,14 +335,20 @@ def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=Non
     for t in (initial_state, dht):
         if t is not None and t.dtype != torch.float32:
             raise TypeError("initial_state and dht must be float32")
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
-    _check_dev(q, k, v, g, beta, do, initial_state, dht, cu_seqlens)
+    N = _num_seqs(B, cu_seqlens)
+    _expect(do, (B, T, H, Dv), "do")
+    _expect(initial_state, (N, H, Dk, Dv), "initial_state")
+    _expect(dht, (N, H, Dk, Dv), "dht")
     out = dict(out or {})
+    for name, like in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta)):
+        t = out.get(name)
+        _expect(t, like.shape, name)
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("%s must have q's dtype" % name)
+    _expect(out.get("dh0"), (N, H, Dk, Dv), "dh0")
+    if out.get("dh0") is not None and out["dh0"].dtype != torch.float32:
+        raise TypeError("dh0 must be float32")
+    _check_dev(q, k, v, g, beta, do, initial_state, dht, cu_seqlens)
     for name, like in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta)):
         if out.get(name) is None:
             out[name] = torch.empty_like(like)
@@ -326,14 +372,17 @@ def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=Non
 
 def recurrent_step(q, k, v, g, beta, state, out=None):
     """One KDA decode step; `state` [N, H, Dk, Dv] float32 is updated in place."""
-    N, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
-        raise ValueError("g's last dim must divide Dk")
-    g_group = Dk // g.shape[-1]
+    N, H, Dk, Dv, g_group = _decode_shapes(q, k, v, g, beta)
     dt = _dt(q)
+    for t in (k, v, g, beta):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, g, beta must share one dtype")
     if state.dtype != torch.float32:
         raise TypeError("state must be float32")
+    _expect(state, (N, H, Dk, Dv), "state")
+    _expect(out, (N, H, Dv), "out")
+    if out is not None and out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
     _check_dev(q, k, v, g, beta, state)
     o = out if out is not None else torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
     st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H, Dk,
@@ -349,12 +398,14 @@ def recurrent_step_pool(q, k, v, g, beta, state_pool, slots, out=None, o_gate=No
     or float16).  A slot outside [0, num_slots) marks the sequence inactive:
     its output row is zero and no state is touched.  o_gate [N, H, Dv] (q's
     dtype): logits z of the output gate, o <- o * sigmoid(z)."""
-    N, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if g.shape[-1] <= 0 or Dk % g.shape[-1]:
-        raise ValueError("g's last dim must divide Dk")
-    g_group = Dk // g.shape[-1]
+    N, H, Dk, Dv, g_group = _decode_shapes(q, k, v, g, beta)
     dt = _dt(q)
+    for t in (k, v, g, beta):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, g, beta must share one dtype")
+    _expect(out, (N, H, Dv), "out")
+    if out is not None and out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
     sdt = KDA_F16 if state_pool.dtype == torch.float16 else _dt(state_pool)
     if slots.dtype != torch.int32 or slots.shape != (N,):
         raise TypeError("slots must be int32 of shape [N]")
@@ -378,16 +429,15 @@ def recurrent_step_pool_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, stat
     """recurrent_step_pool on raw projections: the fused prologue (q, k L2
     norm; g = -exp(A_log) softplus(f + dt_bias); beta = sigmoid(b_raw)) and
     one decode step over a state pool, with the optional output gate."""
-    N, H, Dk = q_raw.shape
-    Dv = v.shape[-1]
-    if f.shape[-1] <= 0 or Dk % f.shape[-1]:
-        raise ValueError("f's last dim must divide Dk")
-    g_group = Dk // f.shape[-1]
+    N, H, Dk, Dv, g_group = _decode_shapes(q_raw, k_raw, v, f, b_raw, g_name="f")
     dt = _dt(q_raw)
     for t in (k_raw, v, f, b_raw):
         if t.dtype != q_raw.dtype:
             raise TypeError("q_raw, k_raw, v, f, b_raw must share one dtype")
     _gate_params(A_log, dt_bias, H, f.shape[-1])
+    _expect(out, (N, H, Dv), "out")
+    if out is not None and out.dtype != q_raw.dtype:
+        raise TypeError("out must have q_raw's dtype")
     sdt = KDA_F16 if state_pool.dtype == torch.float16 else _dt(state_pool)
     if slots.dtype != torch.int32 or slots.shape != (N,):
         raise TypeError("slots must be int32 of shape [N]")
@@ -410,20 +460,20 @@ def short_conv_fwd(x, weight, conv0=None, output_final_state=False, cu_seqlens=N
     """Short causal depthwise convolution along tokens with document reset.
     x [B, T, C]; weight [C, W]; conv0 / conv_final [N, W-1, C] (same dtype).
     Returns (y, conv_final) -- conv_final is None unless requested."""
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be [B, T, C] and weight [C, W]")
     B, T, C = x.shape
     W = weight.shape[-1]
     dt = _dt(x)
     for t in (weight, conv0, conv_final, out):
         if t is not None and t.dtype != x.dtype:
             raise TypeError("x, weight, conv states and y must share one dtype")
-    if weight.shape != (C, W):
+    if weight.dim() != 2 or weight.shape[0] != C:
         raise ValueError("weight must be [C, W]")
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
+    N = _num_seqs(B, cu_seqlens)
+    _expect(conv0, (N, max(W - 1, 0), C), "conv0")
+    _expect(conv_final, (N, max(W - 1, 0), C), "conv_final")
+    _expect(out, (B, T, C), "out")
     y = out if out is not None else torch.empty_like(x)
     cf = conv_final
     if output_final_state and cf is None:
@@ -439,9 +489,17 @@ def short_conv_fwd(x, weight, conv0=None, output_final_state=False, cu_seqlens=N
 def short_conv_step(x, weight, conv_state, out=None):
     """One decode step of the short convolution: x [N, C]; conv_state
     [N, W-1, C] updated in place.  Returns y [N, C]."""
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError("x must be [N, C] and weight [C, W]")
     N, C = x.shape
     W = weight.shape[-1]
     dt = _dt(x)
+    for t in (weight, conv_state, out):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError("x, weight, conv_state and y must share one dtype")
+    _expect(weight, (C, W), "weight")
+    _expect(conv_state, (N, max(W - 1, 0), C), "conv_state")
+    _expect(out, (N, C), "out")
     y = out if out is not None else torch.empty_like(x)
     _check_dev(x, weight, conv_state, y)
     st = lib().kda_short_conv_step(_ptr(x), _ptr(weight), _ptr(conv_state), _ptr(y), N, C, W, dt, _stream())
