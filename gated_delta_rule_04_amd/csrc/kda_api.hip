@@ -273,7 +273,7 @@ kda_status kda_short_conv_step(const void* x, const void* weight, void* conv_sta
 
 namespace {
 struct BwdLayout {
-  size_t order, hs, fw, bw, dh, total;
+  size_t order, hs, fw, bw, dh, gw, total;
 };
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Slots cover every 64-token chunk of every sequence: chunk c of sequence n
@@ -289,7 +289,8 @@ bool bwd_layout(int B, int T, int H, int Dk, int Dv, int N, bool varlen, BwdLayo
   L.fw = L.hs + align256(sh * Dk * Dv * 2);
   L.bw = L.fw + align256(sh * Dk * Dk * 2);
   L.dh = L.bw + align256(sh * Dk * Dv * 2);
-  L.total = L.dh + align256(sh * Dk * Dv * 2);
+  L.gw = L.dh + align256(sh * Dk * Dv * 2);
+  L.total = L.gw + align256(sh * Dk * 4);
   return true;
 }
 }  // namespace
@@ -393,6 +394,7 @@ kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const voi
   b.fw = reinterpret_cast<kda::bf16*>(ws + L.fw);
   b.bw = reinterpret_cast<kda::bf16*>(ws + L.bw);
   b.dh = reinterpret_cast<kda::bf16*>(ws + L.dh);
+  b.gw = reinterpret_cast<float*>(ws + L.gw);
   b.N = N;
   b.H = H;
   b.T = T;

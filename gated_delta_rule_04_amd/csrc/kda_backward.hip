@@ -424,8 +424,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
   __syncthreads();  // dO complete
 
   const size_t uh = (size_t)slot * A.H + h;
-  // F tile (r, w) = Diag(gam)(I - Kh^T W): stored as A-operand fragments of
-  // F^T, [row tile w][slab][lane][8]: elements 0..3 from tile r = 2s, 4..7 from r = 2s + 1.
+  // F = Diag(gam)(I - Kh^T W) = Diag(gam) - M.  The decay part is kept apart
+  // (gam, fp32) and applied exactly by the reverse pass; only -M, a
+  // correction that is small where the chain is long and undamped, is rounded
+  // to bf16.  Rounding F whole would round its near-1 diagonal in every chunk.
+  // Tile (r, w) of -M is stored as A-operand fragments of -M^T,
+  // [row tile w][slab][lane][8]: elements 0..3 from tile r = 2s, 4..7 from r = 2s + 1.
+  if (tid < DK) A.gw[uh * DK + tid] = sm.ft.gam[tid];
   bf16* fw = A.fw + uh * DK * DK;
 #pragma unroll
   for (int r = 0; r < DK / 16; ++r) {
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
     const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.ft.gam[16 * r + 4 * kg]);
     f32x4 f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = gm[i] * ((16 * r + 4 * kg + i == 16 * w + l16 ? 1.f : 0.f) - acc[i]);
+    for (int i = 0; i < 4; ++i) f[i] = -gm[i] * acc[i];
     store4<bf16>(fw + ((size_t)(w * KS + r / 2) * 64 + lane) * 8 + 4 * (r & 1), f);
   }
   // b = Z^T dO, bf16 accumulator tiles [row tile w][column tile][lane][4]
@@ -452,7 +457,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
 // ---------------------------------------------------------------------------
 // Step 3: the reverse state pass, per (sequence, head, 16*NWD-column slice;
 // NWD = 4):
-// dS_in = F^T dS_out + b, chunk by chunk from the last.  NWD wavefronts, one
+// dS_in = F^T dS_out + b = Diag(gam) dS_out - M^T dS_out + b, chunk by chunk
+// from the last; the decay term in fp32, the correction on bf16 MFMA.  NWD wavefronts, one
 // 16-column tile each.  F^T fragments are shared through LDS (double
 // buffered); F^T and b are fetched NST chunks ahead into register stages
 // used in turn (the loop is unrolled by NST).  The slices of a head read F^T
@@ -465,6 +471,7 @@ __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
   constexpr int FPT = FU / NTD;       // per thread
   static_assert(FPT * NTD == FU && NS * 16 * NWD == DV, "dh geometry");
   __shared__ u32x4 fbuf[2][FU];
+  __shared__ float gbuf[2][DK];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the NS slices of a (sequence, head) share an XCD (and its L2)
@@ -489,10 +496,11 @@ __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[mt][i] = d ? d[(size_t)(16 * mt + 4 * kg + i) * DV + 16 * ct + l16] : 0.f;
   }
-  auto load_f = [&](u32x4 (&dst)[FPT], int cc) __attribute__((always_inline)) {
+  auto load_f = [&](u32x4 (&dst)[FPT], float& gdst, int cc) __attribute__((always_inline)) {
     const u32x4* p = reinterpret_cast<const u32x4*>(A.fw + ((size_t)(slot0 + cc) * A.H + h) * DK * DK);
 #pragma unroll
     for (int j = 0; j < FPT; ++j) dst[j] = p[tid + NTD * j];
+    gdst = tid < DK ? A.gw[((size_t)(slot0 + cc) * A.H + h) * DK + tid] : 0.f;
   };
   auto load_b = [&](bf16x4 (&dst)[KT], int cc) __attribute__((always_inline)) {
     const bf16* p = A.bw + ((size_t)(slot0 + cc) * A.H + h) * DK * DV;
@@ -501,9 +509,10 @@ __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
       dst[mt] = __builtin_bit_cast(bf16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
                                                p + ((size_t)(mt * (DV / 16) + ct) * 64 + lane) * 4)));
   };
-  auto put_f = [&](const u32x4 (&src)[FPT], int buf) __attribute__((always_inline)) {
+  auto put_f = [&](const u32x4 (&src)[FPT], float gsrc, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < FPT; ++j) fbuf[buf][tid + NTD * j] = src[j];
+    if (tid < DK) gbuf[buf][tid] = gsrc;
   };
   // Register stages, used in turn: at iteration j (chunk cc = nch - 1 - j)
   // stage u = j % NST holds b of chunk cc and F^T of chunk cc - 1.  Both are
@@ -513,6 +522,7 @@ __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
   // stages and no merge of loaded and unloaded values, either of which makes
   // the compiler wait for the loads just issued.
   u32x4 fs[NST][FPT];
+  float gs[NST];
   bf16x4 bs[NST][KT];
   auto step = [&](int cc, auto Uc) __attribute__((always_inline)) {
     constexpr int u = decltype(Uc)::value;
@@ -525,25 +535,29 @@ __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) SF[s] = F::acc2(dS[2 * s], dS[2 * s + 1]);
     const u32x4* fb = fbuf[cc & 1];
+    const float* gb = gbuf[cc & 1];
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt) {
-      f32x4 acc = {(float)bs[u][mt][0], (float)bs[u][mt][1], (float)bs[u][mt][2], (float)bs[u][mt][3]};
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(&gb[16 * mt + 4 * kg]);
+      f32x4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = (float)bs[u][mt][i] + gm[i] * dS[mt][i];
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = F::mma(__builtin_bit_cast(FV, fb[(mt * KS + s) * 64 + lane]), SF[s], acc);
       dS[mt] = acc;
     }
     load_b(bs[u], max(cc - NST, 0));
-    if (cc >= 1) put_f(fs[u], (cc - 1) & 1);  // its buffer held chunk cc + 1, done before this iteration's barrier
-    load_f(fs[u], max(cc - 1 - NST, 0));
+    if (cc >= 1) put_f(fs[u], gs[u], (cc - 1) & 1);  // its buffer held chunk cc + 1, done before this iteration's barrier
+    load_f(fs[u], gs[u], max(cc - 1 - NST, 0));
   };
 
   if (nch > 0) {
-    load_f(fs[0], nch - 1);
-    put_f(fs[0], (nch - 1) & 1);
+    load_f(fs[0], gs[0], nch - 1);
+    put_f(fs[0], gs[0], (nch - 1) & 1);
     static_for<NST>([&](auto Uc) __attribute__((always_inline)) {
       constexpr int u = decltype(Uc)::value;
       load_b(bs[u], max(nch - 1 - u, 0));
-      load_f(fs[u], max(nch - 2 - u, 0));
+      load_f(fs[u], gs[u], max(nch - 2 - u, 0));
     });
   }
   // whole groups of NST iterations, then the rest

@@ -52,7 +52,8 @@ struct BwdArgs {
   const int* cu_seqlens;
   const int* order;
   const bf16* hs;   // [slot][H][DK][DV]: state entering each chunk
-  bf16* fw;         // [slot][H]: F^T as MFMA A-operand fragments (DK x DK)
+  bf16* fw;         // [slot][H]: -M^T as MFMA A-operand fragments (DK x DK), F = Diag(gam) - M
+  float* gw;        // [slot][H][DK]: gam = e^{G_C} of each chunk
   bf16* bw;         // [slot][H]: b in accumulator tiles (DK x DV)
   bf16* dh;         // [slot][H][DK][DV]: cotangent of the state leaving each chunk
   int N, H, T, slots;

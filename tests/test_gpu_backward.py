@@ -194,26 +194,38 @@ def test_forward_unchanged_by_state_keeping():
     assert errors(o.cpu(), o_ref)[1] <= 5e-3 and errors(ht.cpu(), h_ref)[1] <= 5e-3
 
 
-def test_kimi_k3_heads_last_window():
-    """At the bench's prefill shape (B=1, T=32768, H=96, dk=dv=128): the
-    gradients of the last 512 tokens of two sampled heads against the oracle
-    run on that window from the state that enters it (the forward oracle,
-    streamed) and the same dht; plus finiteness of every gradient."""
+@pytest.mark.parametrize("decay", ["slow", "none"])
+def test_long_reverse_chain(decay):
+    """T = 4096 (64 chunks) with slow (alpha ~ 0.998) or no decay and small
+    writes (beta / 10): the state cotangent then crosses every chunk of the
+    reverse state pass almost undamped, so a wrong F^T or b stage anywhere in
+    the chain shows in the early tokens' gradients and in dh0.  Every token
+    of two heads, and dh0, against the oracle."""
+    d, ct = case(1, 4096, 2, 128, 128, seed=4096 + len(decay), decay=decay)
+    d["beta"] = (d["beta"].float() * 0.1).to(torch.bfloat16)
+    compare("T4096 decay=%s beta/10" % decay, d, ct)
+
+
+def test_kimi_k3_heads_full_chain():
+    """At the bench's prefill shape (B=1, T=32768, H=96, dk=dv=128): every
+    gradient of two heads over all 32,768 tokens, and their dh0, against the
+    oracle run over the whole sequence (so the first tokens' gradients
+    depend on the reverse pass through all 512 chunks); plus finiteness of
+    every gradient of every head."""
     B, T, H, dk, dv = 1, 32768, 96, 128, 128
     d, ct = case(B, T, H, dk, dv, seed=2024, h0=False)
     got = run_gpu(d, ct)
     for n in NAMES:
         assert torch.isfinite(got[n]).all(), n
     heads = [5, 77]
-    W = 512
     sel = lambda t: f64(t[:, :, heads])
-    q, k, v, g, beta, do = (sel(x) for x in (d["q"], d["k"], d["v"], d["g"], d["beta"], ct["do"]))
-    _, h_mid = orc.kda_forward(q[:, :T - W], k[:, :T - W], v[:, :T - W], g[:, :T - W], beta[:, :T - W])
-    w = slice(T - W, T)
-    ref = kda_backward(q[:, w], k[:, w], v[:, w], g[:, w], beta[:, w], do[:, w], h0=h_mid,
+    ref = kda_backward(*(sel(d[n]) for n in ("q", "k", "v", "g", "beta")), sel(ct["do"]),
                        dht=f64(ct["dht"][:, heads]))
     for n in ("dq", "dk", "dv", "dg", "dbeta"):
-        check_grad("K3 heads last 512", n, got[n][:, w][:, :, heads], ref[n])
+        check_grad("K3 heads all tokens", n, got[n][:, :, heads], ref[n])
+        first = slice(0, 512)
+        check_grad("K3 heads first 512", n, got[n][:, first][:, :, heads], ref[n][:, first])
+    check_grad("K3 heads", "dh0", got["dh0"][:, heads], ref["dh0"])
 
 
 def test_packed_documents_workload_full_size():
@@ -246,8 +258,8 @@ def test_packed_documents_workload_full_size():
 
 def test_decay_g64_workload_full_size():
     """The decay-g64 workload at full size (B=5, T=8192, H=12, dk=dv=128,
-    one log-decay per 64 channels): the last 512 tokens of two sequences on
-    two heads against the oracle run from the state that enters them."""
+    one log-decay per 64 channels): every token of two sequences on two
+    heads, and their dh0, against the oracle."""
     d = inputs.workload_prefill("mini1h_g64_bf16")
     B, T, H, dk = d["q"].shape
     dv = d["v"].shape[-1]
@@ -255,18 +267,14 @@ def test_decay_g64_workload_full_size():
     got = run_gpu(d, ct)
     for n in NAMES:
         assert torch.isfinite(got[n]).all(), n
-    W = 512
     heads = [0, 11]
     for b in (1, 4):
         sel = lambda t: f64(t[b:b + 1, :, heads])
-        q, k, v, g, beta, do = (sel(x) for x in (d["q"], d["k"], d["v"], d["g"], d["beta"], ct["do"]))
-        _, h_mid = orc.kda_forward(q[:, :T - W], k[:, :T - W], v[:, :T - W], g[:, :T - W], beta[:, :T - W],
-                                   g_group=64)
-        w = slice(T - W, T)
-        ref = kda_backward(q[:, w], k[:, w], v[:, w], g[:, w], beta[:, w], do[:, w], h0=h_mid,
+        ref = kda_backward(*(sel(d[n]) for n in ("q", "k", "v", "g", "beta")), sel(ct["do"]),
                            dht=f64(ct["dht"][b:b + 1, heads]), g_group=64)
         for n in ("dq", "dk", "dv", "dg", "dbeta"):
-            check_grad("g64 seq %d last 512" % b, n, got[n][b:b + 1, w][:, :, heads], ref[n])
+            check_grad("g64 seq %d all tokens" % b, n, got[n][b:b + 1][:, :, heads], ref[n])
+        check_grad("g64 seq %d" % b, "dh0", got["dh0"][b:b + 1, heads], ref["dh0"])
 
 
 @pytest.mark.parametrize("packed,gg,dk", [(False, 1, 128), (True, 1, 128), (False, 64, 128), (True, 1, 64)])

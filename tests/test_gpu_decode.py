@@ -33,8 +33,10 @@ def test_k3_decode_64_steps_sampled():
     64 steps, state carried); oracle on sampled (sequence, head) pairs."""
     r = inputs.workload_decode("k3_decode_bf16")
     state = r["state"].cuda()
-    seqs = np.array([0, 77, 255])
-    heads = np.array([0, 50, 95])
+    # sequences from both ends and the middle; heads on every residue mod 8
+    # and from both ends of the head range
+    seqs = np.array([0, 1, 127, 128, 254, 255])
+    heads = np.array([0, 9, 18, 27, 36, 45, 54, 63, 95])
     S = f64(r["state"][seqs][:, heads])
     for s, st in enumerate(r["steps"]):
         dev = {n: st[n].cuda() for n in st}
