@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda.h"
 #include "kda_common.h"
 #include "kda_launch.h"
@@ -70,13 +72,48 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// Allocation-free prefill: the packed-document order table (one int per
+// document) lives in a file-scope device array instead of a caller workspace.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device, with that device current, and
+// only that address is ever passed to a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+static __device__ __align__(256) int scratch[KDA_NOALLOC_MAX_SEQS];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch` for work on `stream` (the stream's device,
+// or the current device for the NULL stream); nullptr if HIP fails.
+int* scratch_for(hipStream_t stream) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (e != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = static_cast<int*>(p);
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
 namespace {
 kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                           const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B, int T,
                           int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
-                          void* stream, const float* A_log, const float* dt_bias) {
+                          void* stream, const float* A_log, const float* dt_bias, bool noalloc = false) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
   if (B < 0 || T < 0 || H <= 0 || H > kMaxChunkedHeads || num_seqs < 0) return KDA_ERR_SHAPE;
+  if (noalloc && cu_seqlens && num_seqs > KDA_NOALLOC_MAX_SEQS) return KDA_ERR_WORKSPACE;
   if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
   const bool bf = dt == KDA_BF16;
   if (!kda::prefill_supported(bf, Dk, Dv)) return KDA_ERR_UNSUPPORTED;
@@ -95,7 +132,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
   const bool has_tokens = (long long)B * T > 0;
   if (has_tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
   const size_t need = kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, N, varlen, dt);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (!noalloc && need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const long long units = (long long)N * H;
@@ -104,7 +141,8 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
 
   int* order = nullptr;
   if (varlen) {
-    order = static_cast<int*>(workspace);
+    order = noalloc ? scratch_for(s) : static_cast<int*>(workspace);
+    if (!order) return KDA_ERR_HIP;
     if (kda::launch_varlen_order(cu_seqlens, N, T, order, s) != hipSuccess) return KDA_ERR_HIP;
   }
   kda::PrefillArgs a;
@@ -150,6 +188,13 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
   if (H > 0 && (!A_log || !dt_bias)) return KDA_ERR_NULL;
   return chunk_fwd_impl(q_raw, k_raw, v, f, b_raw, h0, o, ht, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group, dt,
                         workspace, workspace_bytes, stream, A_log, dt_bias);
+}
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                 const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B,
+                                 int T, int H, int Dk, int Dv, int g_group, kda_dtype dt, void* stream) {
+  return chunk_fwd_impl(q, k, v, g, beta, h0, o, ht, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group, dt, nullptr, 0,
+                        stream, nullptr, nullptr, /*noalloc=*/true);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,

@@ -28,9 +28,9 @@ _STATUS = {
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
 # KDA_ABI_VERSION of include/kda.h that these bindings are written for.
-ABI_VERSION = 8
+ABI_VERSION = 9
 
-EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_save", "kda_chunk_bwd_saved", "kda_recurrent_step", "kda_recurrent_step_pool", "kda_recurrent_step_pool_prologue",
+EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_save", "kda_chunk_bwd_saved", "kda_recurrent_step", "kda_recurrent_step_pool", "kda_recurrent_step_pool_prologue",
             "kda_short_conv_fwd", "kda_short_conv_step", "kda_status_str", "kda_abi_version"]
 
 _lib = None
@@ -61,6 +61,8 @@ def lib():
     L.kda_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_fwd.restype = i
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    L.kda_chunk_fwd_noalloc.restype = i
+    L.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
     L.kda_chunk_fwd_prologue.restype = i
     L.kda_chunk_fwd_prologue.argtypes = [vp] * 11 + [i, i, i, i, i, i, i, i, vp, sz, vp]
     L.kda_recurrent_step_prologue.restype = i

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 8
+#define KDA_ABI_VERSION 9
 
 typedef enum {
   KDA_OK = 0,
@@ -99,6 +99,35 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B,
                          int T, int H, int Dk, int Dv, int g_group, kda_dtype dt, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Largest num_seqs kda_chunk_fwd_noalloc accepts with cu_seqlens. */
+#define KDA_NOALLOC_MAX_SEQS 65536
+
+/* kda_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as kda_chunk_fwd, minus the workspace.
+ * The packed-document order table that kda_chunk_fwd keeps in the caller's
+ * workspace (one int per document) lives instead in a static device array
+ * of the library, 256 KiB, one copy per GPU, held until the process ends;
+ * its device address is looked up on the first call on a device.  The call
+ * itself allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ *   cu_seqlens  as for kda_chunk_fwd; with cu_seqlens, num_seqs must be at
+ *          most KDA_NOALLOC_MAX_SEQS, else KDA_ERR_WORKSPACE (checked on the
+ *          host, nothing launched).  Without cu_seqlens no table is used.
+ *   stream the table of the stream's device is used (the current device's
+ *          for the NULL stream).
+ *
+ * Every call on one GPU shares that GPU's table, and each packed call
+ * rewrites all of its num_seqs entries before reading them (nothing needs
+ * to start at zero).  Packed calls that overlap on one GPU -- on different
+ * streams, or from different threads without ordering -- race on the
+ * table; the caller serialises them.  KDA_ERR_HIP if the table's address
+ * cannot be obtained or a launch fails.
+ */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                 const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B,
+                                 int T, int H, int Dk, int Dv, int g_group, kda_dtype dt, void* stream);
 
 /* Bytes of device workspace kda_chunk_bwd needs for these sizes: the
  * per-chunk states and cotangents of the backward pass (64-token chunks of

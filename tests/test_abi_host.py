@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 8 == kda.ABI_VERSION
+    assert L.kda_abi_version() == 9 == kda.ABI_VERSION
     for s in range(7):
         assert L.kda_status_str(s).decode().startswith(("KDA_OK", "KDA_ERR"))
     assert L.kda_status_str(99)
@@ -68,6 +68,29 @@ def test_chunk_fwd_validation():
     assert fwd(B=2 ** 30, T=2 ** 30, N=2 ** 30) == SHAPE  # size overflow
     assert fwd(H=65536) == SHAPE                      # a chunk span must fit 32-bit byte offsets
     assert fwd(H=65535, B=0, T=0, N=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+
+
+def fwd_noalloc(q=P, k=P, v=P, g=P, beta=P, h0=None, o=P, ht=None, cu=None, N=1, B=1, T=64, H=1, Dk=64, Dv=64,
+                gg=1, dt=1):
+    return kda.lib().kda_chunk_fwd_noalloc(q, k, v, g, beta, h0, o, ht, cu, N, B, T, H, Dk, Dv, gg, dt, None)
+
+
+def test_chunk_fwd_noalloc_validation():
+    # the checks of kda_chunk_fwd, minus the workspace, all before any HIP call
+    assert fwd_noalloc(dt=7) == DTYPE
+    assert fwd_noalloc(T=-1) == SHAPE
+    assert fwd_noalloc(Dk=96) == UNSUPPORTED
+    assert fwd_noalloc(cu=P, B=2, N=2) == SHAPE
+    assert fwd_noalloc(cu=P, N=3, q=None) == NULL
+    # the static order table holds KDA_NOALLOC_MAX_SEQS documents
+    text = open(HEADER).read()
+    limit = int(re.search(r"#define KDA_NOALLOC_MAX_SEQS (\d+)", text).group(1))
+    assert limit == 65536
+    assert fwd_noalloc(cu=P, N=limit + 1, T=limit + 1) == WORKSPACE
+    assert fwd_noalloc(cu=P, N=2 ** 31 - 1) == WORKSPACE
+    # nothing to launch: no device state is touched
+    assert fwd_noalloc(cu=P, N=0, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+    assert fwd_noalloc(N=0, B=0, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
 
 
 def test_chunk_fwd_nothing_to_do_is_ok_without_gpu():
