@@ -184,7 +184,6 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
-  if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (H > 0 && (!A_log || !dt_bias)) return KDA_ERR_NULL;
   return chunk_fwd_impl(q_raw, k_raw, v, f, b_raw, h0, o, ht, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group, dt,
                         workspace, workspace_bytes, stream, A_log, dt_bias);

@@ -22,11 +22,11 @@ struct PrefillArgs {
   int num_units;          // N * H
   int H;
   int T;                  // batch mode: tokens per sequence; varlen: total tokens
-  // Optional (bf16 path): the state entering every chunk, rounded to the
-  // operand type, row-major [slot][H][Dk][Dv]; chunk c of the sequence with
-  // first token t0 and index n uses slot (t0 / 64) + n + c.  NULL: not kept.
+  // Optional (bf16 path): the state entering every 64-token chunk, rounded
+  // to the operand type, row-major [slot][H][Dk][Dv]; chunk c of the sequence
+  // with first token t0 and index n uses slot (t0 / 64) + n + c.  NULL: not kept.
   void* hs = nullptr;
-  // Optional (bf16 path): the fused gate and normalisation prologue.  When
+  // Optional: the fused gate and normalisation prologue.  When
   // A_log is set, q and k are raw (L2-normalised per token in the kernel),
   // g holds the gate logits f (g = -exp(A_log) softplus(f + dt_bias)) and
   // beta the logits b (beta = sigmoid(b)); A_log, dt_bias: [H][Dk / g_group].
@@ -78,7 +78,8 @@ hipError_t launch_short_conv_step(bool bf16_io, const void* x, const void* weigh
                                   int C, int W, hipStream_t s);
 hipError_t launch_prefill(bool bf16_io, int Dk, int Dv, int g_group, int VS, const PrefillArgs& a,
                           hipStream_t stream);
-hipError_t launch_prefill_pipe(int Dk, int Dv, int g_group, int VS, const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_pipe(bool bf16_io, int Dk, int Dv, int g_group, int VS, const PrefillArgs& a,
+                               hipStream_t stream);
 hipError_t launch_varlen_order(const int* cu, int N, int T, int* order, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 int prefill_slice_width(bool bf16_io, int Dk, int Dv, long long units, int num_cus);

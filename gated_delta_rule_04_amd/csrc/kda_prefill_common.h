@@ -164,14 +164,17 @@ __device__ __forceinline__ void bstore4(const f32x4& v, rsrc_t r, int off, float
 }
 
 // ---------------------------------------------------------------------------
-// Launch geometry and LDS layout.
+// Launch geometry of the chunked prefill.  A workgroup owns one (sequence,
+// head, value slice) and walks that sequence in chunks of CL tokens, each
+// made of CL / 16 sub-blocks of 16 tokens.
 // ---------------------------------------------------------------------------
-template <int DK_, int DV_, int VS_, typename T_, int GG_>
+template <int DK_, int DV_, int VS_, typename T_, int GG_, int CL_>
 struct PrefillCfg {
   typedef T_ T;  // input/output element type
   typedef T_ E;  // MFMA operand type (bf16 path: bf16; f32 path: float)
   static constexpr int DK = DK_, DV = DV_, VS = VS_, GG = GG_;
-  static constexpr int C = 64;                   // chunk length
+  static constexpr int CL = CL_;                 // tokens per chunk (one pipeline step)
+  static constexpr int NSB = CL / 16;            // 16-token sub-blocks per chunk
   static constexpr int NPW = DK / 16;            // producer wavefronts (8 or 4)
   static constexpr int NA = 64 * NPW;            // producer threads
   static constexpr int RT = VS / 16;             // value-column tiles per slice
@@ -180,30 +183,29 @@ struct PrefillCfg {
   static constexpr int NT = NA + 64 * NBW;       // threads per workgroup
   static constexpr int PADE = 8 / sizeof(E);     // 8-byte row skew: pitch = 2 (mod 32) dwords
   static constexpr int KP = DK + PADE;           // pitch of [*][DK] operand tiles
-  // bf16: Kh^T fragments come from the token-major Kh tile through transposing
-  // LDS reads (gfx950 ds_read_b64_tr_b16); Kh rows are then 16 elements longer
-  // and XOR-permuted, and no separate Kh^T tile exists.  fp32 keeps Kh^T.
+  // bf16: the state update's (K e^{G_end - G})^T fragments come from the
+  // token-major tile through transposing LDS reads (gfx950
+  // ds_read_b64_tr_b16); its rows are then 16 elements longer and
+  // XOR-permuted.  fp32 reads that tile's columns directly.
   static constexpr bool TR = sizeof(E) == 2;
-  static constexpr int KHP = TR ? DK + 16 : KP;  // pitch of the Kh tile
-  static constexpr int CP = C + PADE;            // pitch of [*][C] operand tiles
-  static constexpr int AP = C + 4;               // pitch of the fp32 A tile
+  static constexpr int KEP = TR ? DK + 16 : KP;  // pitch of the KE tile
   static constexpr int CGN = DK / 8;             // gating: groups of 8 key channels
   static constexpr int NRB = NA / CGN;           // gating: row blocks
-  static constexpr int RPB = C / NRB;            // gating: rows per block
+  static constexpr int RPB = CL / NRB;           // gating: rows per block
   static constexpr int RBW = 64 / CGN;           // gating: row blocks per wavefront
+  static constexpr int RPW = RBW * RPB;          // gating: rows per wavefront
+  static constexpr int WPB = 16 / RPW;           // gating: wavefronts per sub-block
   static constexpr int KT = DK / 16;             // key-channel tiles
   static constexpr int NS = DV / VS;             // slices per head
   static_assert(DK == 64 || DK == 128, "DK");
+  static_assert(CL == 32 || CL == 64, "CL");
   static_assert(VS % 16 == 0 && DV % VS == 0 && RT % TPW == 0, "VS");
-  static_assert(NRB * CGN == NA && RPB * NRB == C && RBW * CGN == 64, "gating map");
-  static_assert(RPB == 2 || RPB == 4, "a thread's Kh^T run stays inside one 4-token group");
-  static_assert(NPW == 4 || NPW == 8, "producer wavefronts");
+  static_assert(NRB * CGN == NA && RPB * NRB == CL && RBW * CGN == 64, "gating map");
+  static_assert(RPW <= 16 && WPB * RPW == 16, "a sub-block is whole wavefronts of gating rows");
+  static_assert(NSB <= NPW && NSB % 2 == 0, "one producer wavefront per sub-block transform");
+  static_assert(RBW == 4 || WPB == 1, "cross-wavefront prefixes use the four-row-block scan");
 };
 
-// Kh^T is stored with its 4-token groups XOR-permuted per 16 key channels,
-// which spreads the producer's column writes over all banks while the state
-// wavefronts' row reads (one 16-row block per instruction) stay conflict-free.
-__device__ __forceinline__ int kht_swizzle(int row) { return (5 * (row >> 4)) & 15; }
 // Cross-lane sums without LDS traffic (the LDS is the busiest unit of the
 // pipelined prefill; a __shfl_* is an LDS-crossbar ds_bpermute).
 template <int CTRL>

@@ -1,52 +1,132 @@
-// KDA chunked prefill for bf16 inputs, gfx950: the producer work is
-// software-pipelined across chunks.
+// KDA chunked prefill, gfx950 (CDNA4): one fused, software-pipelined kernel
+// for bf16 and fp32 inputs.
 //
-// Same block algebra as the single-stage kernel (kda_prefill.hip): per chunk
-// of C = 64 tokens the gated operands Qt = Q e^G, Kt = K e^G, Kh = K e^-G, the
-// blocks A = strictly_lower(Diag(b) Kt Kh^T) and P = lower_incl_diag(Qt Kh^T),
-// the UT transform Tm = (I + A)^-1 Diag(b), and the state pass R = V - Kt S,
-// U = Tm R, O = Qt S + P U, S <- Diag(e^{G_C}) (S + Kh^T U).  It is derived
-// from the recurrence S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t
-// v_t^T, o_t = S_t^T q_t of the miniKimiK3 card's Kimi Delta Attention bullet
-// ("Architecture" section) and is exact up to rounding.
+// The chunked parallel form of the miniKimiK3 card's Kimi Delta Attention
+// bullet ("Architecture" section).  The pages state that KDA trains through a
+// chunked parallel form but give no algebra; the form below is derived from
+// the recurrence S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
+// o_t = S_t^T q_t, and is exact up to rounding.  Per head and sub-block of 16
+// tokens, with S the state entering the sub-block, G_r the cumulative
+// log-decay from the sub-block's start to token r and M = G_end / 2 the
+// midpoint of the sub-block's decay (per key channel):
 //
-// Only the state pass is a recurrence; gating and the transform of a chunk
-// depend on its own inputs alone.  Here they run ahead of the state pass, so
-// that the VALU-bound gating of one chunk overlaps the MFMA- and
-// latency-bound transform of the next and the state pass of the one after.
-// Each iteration i has two stages between workgroup barriers:
+//   gated operands  QB = Q e^{G-M},  KB = K e^{G-M},  KD = K e^{M-G},
+//                   KE = K e^{G_end - G + M'}   (M': the next sub-block's M,
+//                                                0 after a chunk's last one)
+//   transform       N = strictly_lower(Diag(b) KB KD^T),  P = lower_incl(QB KD^T),
+//                   T = (I + N)^-1 Diag(b)                        (16 x 16, MFMA)
+//   state pass      with S' = Diag(e^M) S carried instead of S:
+//                   R = V - KB S';  U = T R;  O = QB S' + P U;
+//                   S' <- Diag(e^{G_end - M + M'}) S' + KE^T U    (MFMA)
 //
-//   stage | state wavefronts           | producers: transform | producers: gating
-//   ------+----------------------------+----------------------+-------------------
-//     P   | chunk i:   U = Tm R,       | chunk i+1: A, P,     | chunk i+2: decay
-//         |   O += P U, o, S update    |   diagonal inverses  |   block sums, beta
-//     Q   | chunk i+1: R = V - Kt S,   | chunk i+1: blocks    | chunk i+2: Qt, Kt,
-//         |   O = Qt S                 |   below the diagonal |   Kh, e^{G_C}
+// Every exponent is referenced inside one 16-token sub-block and to the
+// midpoint of its decay, so QB, KB and KD lie within e^{+-D/2} of q and k,
+// D the sub-block's decay: they stay in the float range while a channel's
+// log-decay summed over the sub-block is above about -140, whatever the
+// decay over longer spans.  Between chunks S' is S; a chunk's first
+// sub-block starts with S' = Diag(e^M) S.
 //
-// The gated operands, Tm, P, beta and e^{G_C} are double-buffered in LDS by
-// chunk parity.  Kh^T fragments come from the token-major Kh tile through
-// gfx950 transposing LDS reads, and A keeps only its six blocks below the
-// diagonal, which is what makes the two buffers fit in 160 KB at d_k = 128.
-// Global loads are issued one full iteration before their use.
+// Design for MI355X.  A workgroup owns one (sequence, head, value slice) and
+// walks that sequence in chunks of CL tokens (CL / 16 sub-blocks); nothing
+// goes through HBM between the steps, so q, k, v, g, beta are read once and o
+// written once.  Wavefronts are specialised:
+//   - producers (one per 16 key channels) gate each chunk two steps ahead of
+//     the state pass and build each sub-block's T and P one step ahead;
+//   - state wavefronts (one per 16 value columns of the slice, at most four)
+//     keep their columns of the fp32 state in MFMA accumulators and run the
+//     sub-blocks in order, at raised issue priority (they carry the
+//     recurrence).
+// Each pipeline iteration i has two stages between LDS-only barriers:
+//
+//   stage | state wavefronts              | producers
+//   ------+--------------------------------+-------------------------------------
+//     P   | chunk i: second half of its    | chunk i+1: T, P of every sub-block
+//         |   sub-blocks                   | chunk i+2: decay sums, beta
+//     Q   | chunk i+1: first half of its   | chunk i+2: QB, KB, KE, KD, factors
+//         |   sub-blocks                   |
+//
+// QB, KB, KE, V, T, P, beta and the state factors are double-buffered in LDS
+// by chunk parity; KD is read only by the transform one stage after it is
+// written and has one buffer.  The producers issue every global load (q, k,
+// v, g, beta) one iteration before its use, so the loads stay in flight
+// across the barriers and the state wavefronts, whose only global accesses
+// are the o stores, never wait on memory.  The slices of one head are placed on
+// the same XCD so that their shared q/k/g reads hit that XCD's L2.
+//
+// Numerics: S, N and all accumulators are fp32; MFMA operands (gated q/k, T,
+// P, U and a copy of S') are rounded to the input type.  U = T R is taken in
+// fp32 from the bf16 T, so R is not rounded.
 
 #include "kda_prefill_common.h"
 #include "kda_launch.h"
 
 namespace kda {
 
+template <typename E>
+struct Tile16;  // one 16 x 16 tile in accumulator form, one lane's share
+template <>
+struct Tile16<bf16> {
+  typedef bf16x4 type;
+  __device__ __forceinline__ static type pack(const f32x4& v) { return to_bf16x4(v); }
+  __device__ __forceinline__ static f32x4 unpack(const type& v) {
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+};
+template <>
+struct Tile16<float> {
+  typedef f32x4 type;
+  __device__ __forceinline__ static type pack(const f32x4& v) { return v; }
+  __device__ __forceinline__ static f32x4 unpack(const type& v) { return v; }
+};
+
 template <class Cfg>
 struct PipeSmem {
   typedef typename Cfg::E E;
-  E q[2][Cfg::C][Cfg::KP];    // Qt = Q e^G          (token-major), by chunk parity
-  E k[2][Cfg::C][Cfg::KP];    // Kt = K e^G          (token-major)
-  E kh[2][Cfg::C][Cfg::KHP];  // Kh = K e^-G         (token-major, swizzled)
-  E t[2][Cfg::C][Cfg::CP];    // Tm = (I + A)^-1 Diag(b), row-major
-  E p[2][Cfg::C][Cfg::CP];    // P, row-major
-  alignas(16) float a[6][16][20];   // blocks A_IJ, I > J (fp32), block I(I-1)/2 + J
-  alignas(16) float xd[4][16][20];  // diagonal blocks of X = (I + A)^-1, row-major (fp32)
-  alignas(16) float beta[2][Cfg::C];
-  alignas(16) float gam[2][Cfg::DK];         // e^{G_C}
-  alignas(16) float gsum[Cfg::NPW][Cfg::DK];  // per-wavefront log2-decay totals
+  typedef typename Tile16<E>::type TT;
+  E q[2][Cfg::CL][Cfg::KP];    // QB = Q e^{G-M}          (token-major), by chunk parity
+  E k[2][Cfg::CL][Cfg::KP];    // KB = K e^{G-M}          (token-major)
+  E ke[2][Cfg::CL][Cfg::KEP];  // KE = K e^{G_end-G+M'}   (token-major; bf16: swizzled)
+  E kd[Cfg::CL][Cfg::KP];      // KD = K e^{M-G}          (token-major), transform only
+  E v[2][Cfg::CL][Cfg::VS + Cfg::PADE];  // V rows of the slice (loaded by the producers)
+  TT t[2][Cfg::NSB][64];       // T^T of each sub-block, accumulator form
+  TT p[2][Cfg::NSB][64];       // P^T of each sub-block, accumulator form
+  alignas(16) float beta[2][Cfg::CL];
+  alignas(16) float phi[2][Cfg::NSB][Cfg::DK];  // e^{G_end - M + M'} of each sub-block
+  alignas(16) float psi[2][Cfg::DK];            // e^M of the chunk's first sub-block
+  alignas(16) float gsum[Cfg::NPW][Cfg::DK];    // per-wavefront log2-decay totals
+};
+
+// 16x16 products whose first operand comes from LDS in accumulator form
+// (lane l: M[4(l/16) + i][l % 16] of the matrix whose transpose is A), as
+// Reg16<E>::prod(At, B) = A * B.  bf16: the stored operand is bf16 already.
+template <typename E>
+struct RegLds;
+template <>
+struct RegLds<bf16> {
+  // A * B with A^T stored in bf16 and B an fp32 accumulator tile, B split
+  // into bf16 parts hi + lo (lo = B - hi, rounded): two 16x16x16 steps whose
+  // sum is within about 2^-16 of A * B, so B is not rounded to bf16.
+  __device__ __forceinline__ static f32x4 prod_f32(const bf16x4& At, const f32x4& B) {
+    const bf16x4 hi = to_bf16x4(B);
+    const f32x4 lo = B - f32x4{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};
+    const s16x4 a = __builtin_bit_cast(s16x4, At);
+    const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, hi),
+                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, Reg16<bf16>::cvt(lo), c, 0, 0, 0);
+  }
+  // A * B with A^T an fp32 accumulator tile (rounded to bf16) and B stored
+  // in bf16 in accumulator form: one 16x16x16 bf16 step.
+  __device__ __forceinline__ static f32x4 prod(const f32x4& At, const bf16x4& B) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Reg16<bf16>::cvt(At), __builtin_bit_cast(s16x4, B),
+                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+};
+template <>
+struct RegLds<float> {
+  __device__ __forceinline__ static f32x4 prod_f32(const f32x4& At, const f32x4& B) {
+    return Reg16<float>::prod(At, B);
+  }
+  __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) { return Reg16<float>::prod(At, B); }
 };
 
 template <class Cfg, bool PRO>
@@ -55,13 +135,12 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
   typedef typename Cfg::E E;
   typedef Frag<E> F;
   typedef typename F::V FV;
-  static_assert(Cfg::TR, "bf16 path");
-  constexpr int DK = Cfg::DK, DV = Cfg::DV, VS = Cfg::VS, GG = Cfg::GG, C = Cfg::C, KP = Cfg::KP;
-  constexpr int KHP = Cfg::KHP, CP = Cfg::CP;
+  typedef Tile16<E> TL;
+  constexpr int DK = Cfg::DK, DV = Cfg::DV, VS = Cfg::VS, GG = Cfg::GG, CL = Cfg::CL, KP = Cfg::KP;
+  constexpr int KEP = Cfg::KEP, NSB = Cfg::NSB, HSB = NSB / 2;
   constexpr int NS = Cfg::NS, TPW = Cfg::TPW, KT = Cfg::KT, RPB = Cfg::RPB, NPW = Cfg::NPW;
-  constexpr int SLAB = F::SLAB;
-  constexpr int SK = DK / SLAB;  // slabs over key channels
-  constexpr int SC = C / SLAB;   // slabs over the chunk's tokens
+  constexpr int WPB = Cfg::WPB;
+  constexpr int SK = DK / F::SLAB;  // slabs over key channels
 
   __shared__ PipeSmem<Cfg> sm;
 
@@ -93,9 +172,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     len = args.T;
   }
   const int col0 = slice * VS;  // first value column of this slice
-  // chunk c of this sequence keeps its entering state in slot hs_slot0 + c
+  // 64-token chunk c of this sequence keeps its entering state in slot hs_slot0 + c
   const int hs_slot0 = (tok0 >> 6) + seq;
-  const int nchunks = (len + C - 1) / C;
+  const int nchunks = (len + CL - 1) / CL;
 
   const T* __restrict__ gq = static_cast<const T*>(args.q);
   const T* __restrict__ gk = static_cast<const T*>(args.k);
@@ -109,27 +188,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
 #pragma unroll
   for (int i = 0; i < 4; ++i) ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
 
-  // ---- upper 16x16 tiles of Tm and P are zero and never written again ----
-  for (int idx = tid; idx < 2 * C * C; idx += Cfg::NT) {
-    const int b = idx / (C * C), r = (idx / C) % C, c = idx % C;
-    if ((c >> 4) > (r >> 4)) {
-      sm.t[b][r][c] = from_f32<E>(0.f);
-      sm.p[b][r][c] = from_f32<E>(0.f);
-    }
-  }
-
-  // Fragments of the 16-row block blk of a token-major Qt or Kt tile.
+  // Fragments of the 16-row block blk of a token-major operand tile.
   auto ld_rows = [&](FV (&fr)[SK], const E (*tile)[KP], int blk) {
     const E* row = &tile[0][0] + opaque(l16 * KP) + 16 * blk * KP;
 #pragma unroll
     for (int s = 0; s < SK; ++s) fr[s] = F::ld(row, s, kg);
-  };
-  // Same for a Kh tile (its units are XOR-permuted by row / 4).
-  auto ld_kh_rows = [&](FV (&fr)[SK], int b, int blk) {
-    const E* row = &sm.kh[b][0][0] + opaque(l16 * KHP) + 16 * blk * KHP;
-    const int kgx = kg ^ kh_swizzle(l16);
-#pragma unroll
-    for (int s = 0; s < SK; ++s) fr[s] = F::ld(row, s, kgx);
   };
   auto mma_rows = [&](const FV (&a)[SK], const FV (&b)[SK]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -146,7 +209,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     const int cg = tid % CGN, rb = tid / CGN;
     const int ch = 8 * cg;                 // first key channel of this thread
     const int rbw = lane / CGN;            // row block within the wavefront
+    const int sbw = wave / WPB;            // sub-block of this wavefront's rows
     V8 rq[RPB], rk[RPB], rg[GG == 1 ? RPB : 1];
+    // V rows of the slice, in 8-element units spread over the producers
+    constexpr int VU = CL * VS / 8, NVL = (VU + Cfg::NA - 1) / Cfg::NA;
+    V8 rv[NVL];
     T rgs[GG == 1 ? 1 : RPB], rbeta;
     // Rows past the end of the sequence read as zero through the per-chunk
     // buffer bounds.
@@ -172,13 +239,19 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       else
         return x * kLog2e;
     };
-    auto chunk_rows = [&](int ck) { return min(C, len - ck * C); };
-    auto chunk_row0 = [&](int ck) { return (size_t)(tok0 + ck * C) * H + h; };
+    auto chunk_rows = [&](int ck) { return min(CL, len - ck * CL); };
+    auto chunk_row0 = [&](int ck) { return (size_t)(tok0 + ck * CL) * H + h; };
+    // bytes of a chunk's nv rows at a token stride (0 for no rows: nothing is read)
+    auto span = [&](int nv, int stride, int row_bytes) { return nv > 0 ? (nv - 1) * stride + row_bytes : 0; };
+    // Every prefetch is issued, in the same order, in every iteration (the
+    // last chunk again past the end), and only inside the loop (an extra
+    // leading iteration issues the first chunk's), so the compiler can count
+    // the loads in flight and wait only for the ones a stage uses.
     auto load_gb = [&](int ck) {  // g, beta
       const int nv = chunk_rows(ck);
       const size_t row0 = chunk_row0(ck);
-      const rsrc_t bg = make_rsrc(gg + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * (int)sizeof(T));
-      const rsrc_t bb = make_rsrc(gb + row0, (nv - 1) * rsb + (int)sizeof(T));
+      const rsrc_t bg = make_rsrc(gg + row0 * (DK / GG), span(nv, rsg, (DK / GG) * (int)sizeof(T)));
+      const rsrc_t bb = make_rsrc(gb + row0, span(nv, rsb, (int)sizeof(T)));
 #pragma unroll
       for (int j = 0; j < RPB; ++j) {
         const int r = rb * RPB + j;
@@ -187,46 +260,39 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         else
           rgs[j] = bload<T>(bg, r * rsg + (ch / GG) * (int)sizeof(T));
       }
-      if (tid < C) rbeta = bload<T>(bb, tid * rsb);
+      rbeta = bload<T>(bb, (tid % CL) * rsb);  // threads tid < CL use theirs
     };
-    auto load_qk = [&](int ck) {
-      const rsrc_t bq = make_rsrc(gq + chunk_row0(ck) * DK, (chunk_rows(ck) - 1) * rsk + DK * (int)sizeof(T));
-      const rsrc_t bk = make_rsrc(gk + chunk_row0(ck) * DK, (chunk_rows(ck) - 1) * rsk + DK * (int)sizeof(T));
+    const int rsv = H * DV * (int)sizeof(T);         // token stride of v (bytes)
+    auto load_qk = [&](int ck) {  // q, k and the slice's V rows
+      const int nv = chunk_rows(ck);
+      const rsrc_t bq = make_rsrc(gq + chunk_row0(ck) * DK, span(nv, rsk, DK * (int)sizeof(T)));
+      const rsrc_t bk = make_rsrc(gk + chunk_row0(ck) * DK, span(nv, rsk, DK * (int)sizeof(T)));
+      const rsrc_t bv = make_rsrc(gv + chunk_row0(ck) * DV + col0, span(nv, rsv, VS * (int)sizeof(T)));
 #pragma unroll
       for (int j = 0; j < RPB; ++j) rq[j] = Vec8<T>::load(bq, (rb * RPB + j) * rsk + ch * (int)sizeof(T));
 #pragma unroll
       for (int j = 0; j < RPB; ++j) rk[j] = Vec8<T>::load(bk, (rb * RPB + j) * rsk + ch * (int)sizeof(T));
+#pragma unroll
+      for (int j = 0; j < NVL; ++j) {
+        const int u = tid + Cfg::NA * j;
+        if (VU % Cfg::NA == 0 || u < VU)
+          rv[j] = Vec8<T>::load(bv, (u / (VS / 8)) * rsv + 8 * (u % (VS / 8)) * (int)sizeof(T));
+      }
     };
-    float G[RPB][8];  // cumulative log2-decay of this thread's rows (block-local)
-    float off[8];     // log2-decay of the chunk before this thread's block
-    f32x4 Xdiag;      // X_ww = (I + A_ww)^-1 of this wave's block, accumulator form
+    float G[RPB][8];  // cumulative log2-decay of this thread's rows (thread-local)
+    float off[8];     // log2-decay of the rows of this wavefront before this thread's block
+    float tot[8];     // log2-decay over this wavefront's rows
 
-    // ---- transform jobs for the chunk in buffer b.  Operands are ordered for
-    // the transposed product, so a lane ends with four consecutive columns of
-    // one row of the block. ----
-    // A_IJ below the diagonal (I > J), fp32; khJ = fragments of Kh block J
-    auto a_tile = [&](int b, int I, int J, const FV (&khJ)[SK]) {
-      FV kt[SK];
-      ld_rows(kt, sm.k[b], I);
-      const f32x4 d = mma_rows(khJ, kt) * sm.beta[b][opaque(l16) + 16 * I];
-      *reinterpret_cast<f32x4*>(&sm.a[I * (I - 1) / 2 + J][0][0] + opaque(20 * l16 + 4 * kg)) = d;
-    };
-    // P_IJ below the diagonal (I > J)
-    auto p_tile = [&](int b, int I, int J, const FV (&khJ)[SK]) {
-      FV qt[SK];
-      ld_rows(qt, sm.q[b], I);
-      store4<E>(&sm.p[b][0][0] + opaque(l16 * CP + 4 * kg) + 16 * I * CP + 16 * J, mma_rows(khJ, qt));
-    };
-    // Diagonal block I: N = A_II and N^T (registers only), P_II, and the
-    // inverse X_II = (I + N)^-1 kept in registers for the forward substitution;
-    // X_II (row-major, fp32) and Tm_II = X_II Diag(b_I) go to LDS.
+    // ---- transform of sub-block I of the chunk in buffer b: N = A_II and
+    // N^T (registers only), P^T, X = (I + N)^-1; T^T = (X Diag(b))^T and P^T
+    // go to LDS in accumulator form (lane order). ----
     auto diag_job = [&](int b, int I) {
-      FV kt[SK], kh[SK], qt[SK];
-      ld_rows(kt, sm.k[b], I);
-      ld_kh_rows(kh, b, I);
-      ld_rows(qt, sm.q[b], I);
-      f32x4 N = mma_rows(kt, kh), Nt = mma_rows(kh, kt);
-      f32x4 Pt = mma_rows(kh, qt);
+      FV kb[SK], kd[SK], qb[SK];
+      ld_rows(kb, sm.k[b], I);
+      ld_rows(kd, sm.kd, I);
+      ld_rows(qb, sm.q[b], I);
+      f32x4 N = mma_rows(kb, kd), Nt = mma_rows(kd, kb);
+      f32x4 Pt = mma_rows(kd, qb);  // lane: P[16I + l16][16I + 4kg + i]
       const float bl = sm.beta[b][opaque(l16) + 16 * I];
       const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[b][opaque(4 * kg) + 16 * I]);
 #pragma unroll
@@ -236,97 +302,27 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         Nt[i] = r < l16 ? Nt[i] * bl : 0.f;
         Pt[i] = r <= l16 ? Pt[i] : 0.f;       // lower including the diagonal
       }
-      const int pt = opaque(l16 * CP + 4 * kg) + 16 * I * CP + 16 * I;
-      store4<E>(&sm.p[b][0][0] + pt, Pt);
-      Xdiag = unit_lower_inverse16<E>(N, Nt, ident);
-      *reinterpret_cast<f32x4*>(&sm.xd[I][0][0] + opaque(20 * l16 + 4 * kg)) = Reg16<E>::prod(Xdiag, ident);
-      store4<E>(&sm.t[b][0][0] + pt, Reg16<E>::prod(Xdiag * bl, ident));
-    };
-    // Blocks below the diagonal in block column J, top to bottom; each needs
-    // only this column's blocks above it (registers) and the diagonal blocks:
-    // X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ.
-    auto solve_column = [&](int b, auto Jc) {
-      constexpr int J = decltype(Jc)::value;
-      const float bj = sm.beta[b][opaque(l16) + 16 * J];
-      const int ao = opaque(20 * l16 + 4 * kg), to = opaque(l16 * CP + 4 * kg);
-      f32x4 Xc[4 - J];  // X_KJ, K = J .. 3, accumulator form
-      Xc[0] = Xdiag;
-#pragma unroll
-      for (int d = 1; d < 4 - J; ++d) {
-        const int I = J + d;
-        f32x4 M = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < d; ++e) {
-          // (A_{I,J+e})^T in accumulator form: lane holds A[16I + l16][16(J+e) + 4kg + i]
-          const f32x4 At = *reinterpret_cast<const f32x4*>(&sm.a[I * (I - 1) / 2 + J + e][0][0] + ao);
-          M += Reg16<E>::prod(At, Xc[e]);
-        }
-        const f32x4 XIt = *reinterpret_cast<const f32x4*>(&sm.xd[I][0][0] + ao);
-        Xc[d] = -Reg16<E>::prod(XIt, M);
-        store4<E>(&sm.t[b][0][0] + to + 16 * I * CP + 16 * J, Reg16<E>::prod(Xc[d] * bj, ident));
-      }
+      const f32x4 X = unit_lower_inverse16<E>(N, Nt, ident);
+      // T^T in accumulator form: lane holds T[l16][4kg + i] = X[l16][4kg + i] b_{4kg + i}
+      const f32x4 Tt = Reg16<E>::prod(X, ident) * br;
+      sm.t[b][I][lane] = TL::pack(Tt);
+      sm.p[b][I][lane] = TL::pack(Pt);
     };
 
-    if (nchunks > 0) {
-      load_gb(0);
-      load_qk(0);
-    }
+    const int last = max(nchunks - 1, 0);
 
-    for (int i = -2; i < nchunks; ++i) {
+    for (int i = -3; i < nchunks; ++i) {
       const int cT = i + 1, cG = i + 2;  // chunks under transform and gating
       const int bT = cT & 1, bG = cG & 1;
       lds_barrier();  // ---------------------------------------------------- P
       if (cT >= 0 && cT < nchunks) {
-        // A and P: 10 + 10 tiles and four diagonal inverses over the producers
         static_switch<NPW>(wave, [&](auto Wc) {
           constexpr int W = decltype(Wc)::value;
-          if constexpr (W < 4) diag_job(bT, W);
-          FV kh0[SK];
-          if constexpr (NPW == 8) {
-            if constexpr (W == 4) {
-              ld_kh_rows(kh0, bT, 0);
-              a_tile(bT, 1, 0, kh0);
-              p_tile(bT, 1, 0, kh0);
-              a_tile(bT, 3, 0, kh0);
-            } else if constexpr (W == 5) {
-              ld_kh_rows(kh0, bT, 0);
-              p_tile(bT, 3, 0, kh0);
-              a_tile(bT, 2, 0, kh0);
-              p_tile(bT, 2, 0, kh0);
-            } else if constexpr (W == 6) {
-              ld_kh_rows(kh0, bT, 1);
-              a_tile(bT, 2, 1, kh0);
-              p_tile(bT, 2, 1, kh0);
-              a_tile(bT, 3, 1, kh0);
-            } else if constexpr (W == 7) {
-              ld_kh_rows(kh0, bT, 1);
-              p_tile(bT, 3, 1, kh0);
-              ld_kh_rows(kh0, bT, 2);
-              a_tile(bT, 3, 2, kh0);
-              p_tile(bT, 3, 2, kh0);
-            }
-          } else {  // four producers: the A blocks now, the P blocks with the solve
-            if constexpr (W == 0) {
-              ld_kh_rows(kh0, bT, 0);
-              a_tile(bT, 1, 0, kh0);
-              a_tile(bT, 2, 0, kh0);
-            } else if constexpr (W == 1) {
-              ld_kh_rows(kh0, bT, 1);
-              a_tile(bT, 2, 1, kh0);
-              ld_kh_rows(kh0, bT, 0);
-              a_tile(bT, 3, 0, kh0);
-            } else if constexpr (W == 2) {
-              ld_kh_rows(kh0, bT, 1);
-              a_tile(bT, 3, 1, kh0);
-            } else if constexpr (W == 3) {
-              ld_kh_rows(kh0, bT, 2);
-              a_tile(bT, 3, 2, kh0);
-            }
-          }
+          if constexpr (W < NSB) diag_job(bT, W);
         });
       }
-      if (cG < nchunks) {
-        // block-local cumulative decay; prefix over this wavefront's blocks
+      if (cG >= 0 && cG < nchunks) {
+        // thread-local cumulative decay; prefix over this wavefront's blocks
         float acc[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = 0.f;
@@ -356,19 +352,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
             }
           }
         };
-        if (!PRO || nvG == C)
+        if (!PRO || nvG == CL)
           gate_rows(IC<1>{});
         else
           gate_rows(IC<0>{});
         if constexpr (RBW == 4) {  // the four row blocks are the wavefront's 16-lane rows
-          float tot[8];
 #pragma unroll
           for (int c = 0; c < 8; ++c) rows4_scan(acc[c], rbw, off[c], tot[c]);
-          if (rbw == RBW - 1) {
-            *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch]) = f32x4{tot[0], tot[1], tot[2], tot[3]};
-            *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch + 4]) = f32x4{tot[4], tot[5], tot[6], tot[7]};
-          }
-        } else {
+        } else {  // one wavefront is one sub-block: its total is the sub-block's
 #pragma unroll
           for (int c = 0; c < 8; ++c) off[c] = acc[c];  // inclusive prefix over blocks
 #pragma unroll
@@ -379,40 +370,51 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
               if (rbw >= d) off[c] += y;
             }
           }
-          if (rbw == RBW - 1) {
-            *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch]) = f32x4{off[0], off[1], off[2], off[3]};
-            *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch + 4]) = f32x4{off[4], off[5], off[6], off[7]};
-          }
 #pragma unroll
-          for (int c = 0; c < 8; ++c) off[c] -= acc[c];  // exclusive within the wavefront
+          for (int c = 0; c < 8; ++c) {
+            tot[c] = __shfl(off[c], (RBW - 1) * CGN + cg);
+            off[c] -= acc[c];  // exclusive within the wavefront
+          }
         }
-        if (tid < C) sm.beta[bG][tid] = PRO ? (tid < nvG ? sigmoid_f(to_f32(rbeta)) : 0.f) : to_f32(rbeta);
-        if (cG + 1 < nchunks) load_gb(cG + 1);  // prefetch (g, beta registers are free)
+        if (rbw == RBW - 1) {  // this wavefront's total, for the other wavefronts
+          *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch]) = f32x4{tot[0], tot[1], tot[2], tot[3]};
+          *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch + 4]) = f32x4{tot[4], tot[5], tot[6], tot[7]};
+        }
+        if (tid < CL) sm.beta[bG][tid] = PRO ? (tid < nvG ? sigmoid_f(to_f32(rbeta)) : 0.f) : to_f32(rbeta);
       }
+      load_gb(min(cG + 1, last));  // prefetch (g, beta registers are free)
       lds_barrier();  // ---------------------------------------------------- Q
-      if (cT >= 0 && cT < nchunks) {
-        static_switch<NPW>(wave, [&](auto Wc) {
-          constexpr int W = decltype(Wc)::value;
-          if constexpr (W < 3) solve_column(bT, IC<W>{});
-          if constexpr (NPW == 4 && W > 0) {  // P blocks below the diagonal, against the solve's load
-            FV khj[SK];
+      if (cG >= 0 && cG < nchunks) {
+        // decay before this wavefront's rows within the sub-block, the
+        // sub-block's total and the next sub-block's total (log2 units): the
+        // other wavefronts' totals
+        float pre[8], gend[8], gnext[8];
 #pragma unroll
-            for (int J = 0; J < W; ++J) {
-              ld_kh_rows(khj, bT, J);
-              p_tile(bT, W, J, khj);
-            }
-          }
-        });
-      }
-      if (cG < nchunks) {
-        // decay before this thread's block: earlier wavefronts' totals
-        for (int w = 0; w < wave; ++w) {  // uniform trip count
+        for (int c = 0; c < 8; ++c) {
+          pre[c] = 0.f;
+          gend[c] = tot[c];
+          gnext[c] = 0.f;
+        }
+        const int wend = (sbw + 1 < NSB ? sbw + 2 : sbw + 1) * WPB;  // uniform
+#pragma unroll
+        for (int u = 0; u < 2 * WPB; ++u) {
+          const int w = sbw * WPB + u;
+          if (w == wave || w >= wend) continue;  // uniform
           const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch]);
           const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch + 4]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            off[c] += a[c];
-            off[c + 4] += b[c];
+            if (u < WPB) {
+              gend[c] += a[c];
+              gend[c + 4] += b[c];
+              if (w < wave) {
+                pre[c] += a[c];
+                pre[c + 4] += b[c];
+              }
+            } else {
+              gnext[c] += a[c];
+              gnext[c + 4] += b[c];
+            }
           }
         }
         // prologue: inverse L2 norms of this thread's q and k rows (a row's
@@ -429,42 +431,69 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
             ik[j] = __builtin_amdgcn_rsqf(sk + kNormEps);
           }
         }
-        // gated operands Qt, Kt, Kh (token-major)
-        float eL[8];  // e^G of this thread's last row
+        // Four channels at a time: the references M of this sub-block and M'
+        // of the next one in the chunk (0 after the chunk's last sub-block);
+        // KE = KD e^{G_end - M} e^{M'} (two factors that each stay in range
+        // inside the decay domain; a product that underflows there is below
+        // e^-87 of what it is added to); the sub-block's state factor
+        // e^{G_end - M + M'}; then the gated operands QB, KB, KE, KD
+        // (token-major) of this thread's rows.
+        const bool writer = wave % WPB == 0 && rbw == 0;  // one per (sub-block, channel group)
 #pragma unroll
-        for (int j = 0; j < RPB; ++j) {
-          const int r = rb * RPB + j;
-          float e[8], n[8];
+        for (int c4 = 0; c4 < 8; c4 += 4) {
+          float mid[4], fe1[4], fe2[4];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float Gc = off[c] + G[j][c];
-            e[c] = fast_exp2(Gc);
-            n[c] = fast_exp2(-Gc);
-            if (j == RPB - 1) eL[c] = e[c];
-          }
-          float qo[8], ko[8], ho[8];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float kx = elem(rk[j], c) * ik[j];
-            qo[c] = elem(rq[j], c) * iq[j] * e[c];
-            ko[c] = kx * e[c];
-            ho[c] = kx * n[c];
+          for (int c = 0; c < 4; ++c) {
+            mid[c] = 0.5f * gend[c4 + c];
+            fe1[c] = fast_exp2(gend[c4 + c] - mid[c]);
+            fe2[c] = fast_exp2(0.5f * gnext[c4 + c]);
           }
 #pragma unroll
-          for (int c = 0; c < 8; c += 4) {
-            store4<E>(&sm.q[bG][r][ch + c], f32x4{qo[c], qo[c + 1], qo[c + 2], qo[c + 3]});
-            store4<E>(&sm.k[bG][r][ch + c], f32x4{ko[c], ko[c + 1], ko[c + 2], ko[c + 3]});
-            store4<E>(&sm.kh[bG][r][4 * (((ch + c) >> 2) ^ kh_swizzle(r))],
-                      f32x4{ho[c], ho[c + 1], ho[c + 2], ho[c + 3]});
+          for (int j = 0; j < RPB; ++j) {
+            const int r = rb * RPB + j;
+            float qo[4], ko[4], eo[4], dd[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float Gc = pre[c4 + c] + off[c4 + c] + G[j][c4 + c];
+              const float el = fast_exp2(Gc - mid[c]), er = fast_exp2(mid[c] - Gc);
+              const float kx = elem(rk[j], c4 + c) * ik[j];
+              qo[c] = elem(rq[j], c4 + c) * iq[j] * el;
+              ko[c] = kx * el;
+              dd[c] = kx * er;
+              eo[c] = (dd[c] * fe1[c]) * fe2[c];
+            }
+            store4<E>(&sm.q[bG][r][ch + c4], f32x4{qo[0], qo[1], qo[2], qo[3]});
+            store4<E>(&sm.k[bG][r][ch + c4], f32x4{ko[0], ko[1], ko[2], ko[3]});
+            store4<E>(&sm.kd[r][ch + c4], f32x4{dd[0], dd[1], dd[2], dd[3]});
+            if constexpr (Cfg::TR)
+              store4<E>(&sm.ke[bG][r][4 * (((ch + c4) >> 2) ^ kh_swizzle(r))], f32x4{eo[0], eo[1], eo[2], eo[3]});
+            else
+              store4<E>(&sm.ke[bG][r][ch + c4], f32x4{eo[0], eo[1], eo[2], eo[3]});
+          }
+          if (writer) {  // the state factors of the sub-block (and e^M of a chunk's first)
+            *reinterpret_cast<f32x4*>(&sm.phi[bG][sbw][ch + c4]) =
+                f32x4{fe1[0] * fe2[0], fe1[1] * fe2[1], fe1[2] * fe2[2], fe1[3] * fe2[3]};
+            if (sbw == 0)
+              *reinterpret_cast<f32x4*>(&sm.psi[bG][ch + c4]) =
+                  f32x4{fast_exp2(mid[0]), fast_exp2(mid[1]), fast_exp2(mid[2]), fast_exp2(mid[3])};
           }
         }
-        // the chunk's decay e^{G_C}: the last row of the chunk
-        if (rb == Cfg::NRB - 1) {
-          *reinterpret_cast<f32x4*>(&sm.gam[bG][ch]) = f32x4{eL[0], eL[1], eL[2], eL[3]};
-          *reinterpret_cast<f32x4*>(&sm.gam[bG][ch + 4]) = f32x4{eL[4], eL[5], eL[6], eL[7]};
+#pragma unroll
+        for (int j = 0; j < NVL; ++j) {
+          const int u = tid + Cfg::NA * j;
+          if (VU % Cfg::NA == 0 || u < VU) {  // the loaded elements as they are
+            E* dst = &sm.v[bG][u / (VS / 8)][8 * (u % (VS / 8))];
+            if constexpr (sizeof(E) == 2) {
+              *reinterpret_cast<bf16x4*>(dst) = __builtin_shufflevector(rv[j], rv[j], 0, 1, 2, 3);
+              *reinterpret_cast<bf16x4*>(dst + 4) = __builtin_shufflevector(rv[j], rv[j], 4, 5, 6, 7);
+            } else {
+              store4<E>(dst, f32x4{elem(rv[j], 0), elem(rv[j], 1), elem(rv[j], 2), elem(rv[j], 3)});
+              store4<E>(dst + 4, f32x4{elem(rv[j], 4), elem(rv[j], 5), elem(rv[j], 6), elem(rv[j], 7)});
+            }
+          }
         }
-        if (cG + 1 < nchunks) load_qk(cG + 1);  // prefetch (q, k registers are free)
       }
+      load_qk(min(cG + 1, last));  // prefetch (q, k, v registers are free)
     }
     return;
   }
@@ -474,9 +503,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
   // The state pass carries the recurrence; its short VALU/LDS/MFMA bursts are
   // issued ahead of the producers' long VALU streams on the same SIMD.
   __builtin_amdgcn_s_setprio(2);
-  f32x4 S[TPW][KT];  // S: rows (key channels) 16mt + 4kg + i, column l16
-  f32x4 R[TPW][4];   // R, then U: token rows 16t + 4kg + i, column l16
-  f32x4 O[TPW][4];   // O^T: lane holds token 16t + l16, columns 4kg + i
+  // S' = Diag(e^M) S of the current sub-block (S itself between chunks):
+  // rows (key channels) 16mt + 4kg + i, column l16
+  f32x4 S[TPW][KT];
   {
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -489,138 +518,129 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     }
   }
 
-  const int rsv = H * DV * (int)sizeof(T);  // token stride of v and o (bytes)
-  // V rows of the next chunk: lane holds 4 columns of token 16t + l16
-  typename Row4<T>::type vr[TPW][4];
-  auto load_v = [&](int ck) {
-    const int nv = min(C, len - ck * C);
-    const rsrc_t bv = make_rsrc(gv + ((size_t)(tok0 + ck * C) * H + h) * DV + col0, (nv - 1) * rsv + VS * (int)sizeof(T));
+  const int rsv = H * DV * (int)sizeof(T);  // token stride of o (bytes)
+  typedef typename Row4<T>::type VR;
+
+  // One sub-block t of the chunk ck in buffer b.
+  auto sub_step = [&](int b, int ck, int t) {
+    // operands of the sub-block from LDS first: none depends on the state
+    FV ka[SK], qa[SK];
+    {
+      const E* krow = &sm.k[b][0][0] + opaque(l16 * KP) + 16 * t * KP;
+      const E* qrow = &sm.q[b][0][0] + opaque(l16 * KP) + 16 * t * KP;
+#pragma unroll
+      for (int s = 0; s < SK; ++s) {
+        ka[s] = F::ld(krow, s, kg);
+        qa[s] = F::ld(qrow, s, kg);
+      }
+    }
+    VR vr[TPW];  // lane: 4 columns of token 16t + l16
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+      vr[j] = *reinterpret_cast<const VR*>(&sm.v[b][16 * t + l16][16 * (TPW * bw + j) + 4 * kg]);
+    const auto Tt = sm.t[b][t][lane];
+    const auto Pt = sm.p[b][t][lane];
+    FV SF[TPW][SK];
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        vr[j][t] = bload<typename Row4<T>::type>(bv, (16 * t + l16) * rsv + (16 * (TPW * bw + j) + 4 * kg) * (int)sizeof(T));
+      for (int s = 0; s < SK; ++s) SF[j][s] = acc_frag(S[j], s, E());
+    // ---- R = V - KB S (V enters through an exact identity product) ----
+    f32x4 R[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) R[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SK; ++s)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) R[j] = F::mma(ka[s], acc_frag_neg(S[j], s, E()), R[j]);
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) R[j] = Reg16<E>::rows(vr[j], ident, R[j]);
+    // ---- O^T = S^T QB^T ----
+    f32x4 O[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SK; ++s)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) O[j] = F::mma(SF[j][s], qa[s], O[j]);
+    // ---- U = T R (R unrounded), O^T += U^T P^T, write o of the sub-block ----
+    f32x4 U[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      U[j] = RegLds<E>::prod_f32(Tt, R[j]);
+      O[j] += RegLds<E>::prod(U[j], Pt);
+    }
+    if (go) {
+      const int nv = min(CL, len - ck * CL) - 16 * t;
+      const rsrc_t bo = make_rsrc(go + ((size_t)(tok0 + ck * CL + 16 * t) * H + h) * DV + col0,
+                                  nv > 0 ? (nv - 1) * rsv + VS * (int)sizeof(T) : 0);
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+        bstore4(O[j], bo, l16 * rsv + (16 * (TPW * bw + j) + 4 * kg) * (int)sizeof(T), T());
+    }
+    // ---- S' <- Diag(e^{G_end - M + M'}) S' + KE^T U ----
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.phi[b][t][16 * mt + 4 * kg]);
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) S[j][mt] *= gm;
+      if constexpr (Cfg::TR) {
+        // (KE^T) rows 16mt .. 16mt+15 over the sub-block's 16 tokens: in each
+        // 16-lane group a transposing read hands lane l16 element l16 % 4 of
+        // the 4-element pieces addressed by lanes l16 / 4 + {0, 4, 8, 12}, so
+        // lane 4e + q of group kg addresses token 16t + 4kg + e, channels
+        // 16mt + 4q .. 16mt + 4q + 3 (units XOR-permuted by token / 4).
+        const int e = l16 >> 2, q = l16 & 3;
+        const bf16* p = &sm.ke[b][0][0] + (16 * t + 4 * kg + e) * KEP + 4 * (4 * mt + (q ^ kg));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+          S[j][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, Reg16<bf16>::cvt(U[j]), S[j][mt], 0, 0, 0);
+      } else {
+        // fp32: step s takes tokens 4kg + s of the sub-block (element s of U's tile)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float a = sm.ke[b][16 * t + 4 * kg + s][16 * mt + l16];
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) S[j][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, U[j][s], S[j][mt], 0, 0, 0);
+        }
+      }
+    }
   };
-  if (nchunks > 0) load_v(0);
 
-  for (int i = -2; i < nchunks; ++i) {
+  for (int i = -3; i < nchunks; ++i) {  // the same iterations as the producers'
     lds_barrier();  // ------------------------------------------------------ P
     if (i >= 0) {
       const int b = i & 1;
-      // ---- U = Tm R (Tm lower triangular: tile t needs k < 16(t+1)) ----
-      FV UF[TPW][SC];  // U as operand fragments
-      {
-        FV RF[TPW][SC];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-          for (int s = 0; s < SC; ++s) RF[j][s] = acc_frag(R[j], s, E());
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) R[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const E* trow = &sm.t[b][16 * t + l16][0];
-#pragma unroll
-          for (int s = 0; s < (16 * (t + 1) + SLAB - 1) / SLAB; ++s) {
-            const FV a = F::ld(trow, s, kg);
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) R[j][t] = F::mma(a, RF[j][s], R[j][t]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-          for (int s = 0; s < SC; ++s) UF[j][s] = acc_frag(R[j], s, E());
-      }
-      // ---- O^T += U^T P^T, then write o of chunk i (rows of 4 columns) ----
-      const int nv = min(C, len - i * C);
-      const rsrc_t bo = make_rsrc(go + ((size_t)(tok0 + i * C) * H + h) * DV + col0, (nv - 1) * rsv + VS * (int)sizeof(T));
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const E* prow = &sm.p[b][16 * t + l16][0];
-#pragma unroll
-        for (int s = 0; s < (16 * (t + 1) + SLAB - 1) / SLAB; ++s) {
-          const FV pb = F::ld(prow, s, kg);
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(UF[j][s], pb, O[j][t]);
-        }
-        if (go) {
-#pragma unroll
-          for (int j = 0; j < TPW; ++j)
-            bstore4(O[j][t], bo, (16 * t + l16) * rsv + (16 * (TPW * bw + j) + 4 * kg) * (int)sizeof(T), T());
-        }
-      }
-      // ---- S <- Diag(e^{G_C}) (S + Kh^T U) ----
-#pragma unroll
-      for (int mt = 0; mt < KT; ++mt) {
-#pragma unroll
-        for (int s = 0; s < SC; ++s) {
-          const FV a = F::template ld_tr<KHP>(&sm.kh[b][0][0], 16 * mt, s, l16, kg);
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) S[j][mt] = F::mma(a, UF[j][s], S[j][mt]);
-        }
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[b][16 * mt + 4 * kg]);
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) S[j][mt] *= gm;
-      }
+      for (int t = 0; t < HSB; ++t) sub_step(b, i, HSB + t);
     }
     lds_barrier();  // ------------------------------------------------------ Q
     if (i + 1 >= 0 && i + 1 < nchunks) {
-      const int b = (i + 1) & 1;
-      // ---- optional: the state entering chunk i + 1, in the operand type
-      // (rows of four columns through an exact transposing product) ----
-      if (args.hs) {
-        E* hs = static_cast<E*>(args.hs) + ((size_t)(hs_slot0 + i + 1) * H + h) * DK * DV;
+      const int c = i + 1, b = c & 1;
+      // ---- optional: the state entering each 64-token chunk, in the operand
+      // type (rows of four columns through an exact transposing product) ----
+      if constexpr (Cfg::TR && CL == 64) {
+        if (args.hs) {
+          E* hs = static_cast<E*>(args.hs) + ((size_t)(hs_slot0 + c) * H + h) * DK * DV;
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
+          for (int j = 0; j < TPW; ++j)
 #pragma unroll
-          for (int mt = 0; mt < KT; ++mt)
-            store4<E>(hs + (size_t)(16 * mt + l16) * DV + col0 + 16 * (TPW * bw + j) + 4 * kg,
-                      Reg16<E>::prod(S[j][mt], ident));
-      }
-      // ---- R = V - Kt S (V enters through an exact identity product) ----
-      {
-        FV SF[TPW][SK];  // -S as B-operand fragments
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-          for (int s = 0; s < SK; ++s) SF[j][s] = acc_frag_neg(S[j], s, E());
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) R[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const E* krow = &sm.k[b][16 * t + l16][0];
-#pragma unroll
-          for (int s = 0; s < SK; ++s) {
-            const FV a = F::ld(krow, s, kg);
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) R[j][t] = F::mma(a, SF[j][s], R[j][t]);
-          }
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) R[j][t] = Reg16<E>::rows(vr[j][t], ident, R[j][t]);
+            for (int mt = 0; mt < KT; ++mt)
+              store4<E>(hs + (size_t)(16 * mt + l16) * DV + col0 + 16 * (TPW * bw + j) + 4 * kg,
+                        Reg16<E>::prod(S[j][mt], ident));
         }
       }
-      if (i + 2 < nchunks) load_v(i + 2);  // prefetch (V registers are free)
-      // ---- O^T = S^T Qt^T ----
-      {
-        FV SF[TPW][SK];
+      // ---- S' = Diag(e^M) S for the chunk's first sub-block ----
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
+      for (int mt = 0; mt < KT; ++mt) {
+        const f32x4 ps = *reinterpret_cast<const f32x4*>(&sm.psi[b][16 * mt + 4 * kg]);
 #pragma unroll
-          for (int s = 0; s < SK; ++s) SF[j][s] = acc_frag(S[j], s, E());
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) O[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const E* qrow = &sm.q[b][16 * t + l16][0];
-#pragma unroll
-          for (int s = 0; s < SK; ++s) {
-            const FV qb = F::ld(qrow, s, kg);
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) O[j][t] = F::mma(SF[j][s], qb, O[j][t]);
-          }
-        }
+        for (int j = 0; j < TPW; ++j) S[j][mt] *= ps;
       }
+#pragma unroll
+      for (int t = 0; t < HSB; ++t) sub_step(b, c, t);
     }
   }
 
@@ -638,7 +658,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
 }
 
 // ---------------------------------------------------------------------------
-// Host-side dispatch (bf16 inputs).
+// Host-side dispatch.
 // ---------------------------------------------------------------------------
 template <class Cfg>
 static hipError_t launch_pipe_cfg(const PrefillArgs& a, hipStream_t stream) {
@@ -652,9 +672,9 @@ static hipError_t launch_pipe_cfg(const PrefillArgs& a, hipStream_t stream) {
 }
 
 template <int GG>
-static hipError_t launch_pipe_dims(int Dk, int Dv, int VS, const PrefillArgs& a, hipStream_t s) {
+static hipError_t launch_pipe_bf16(int Dk, int Dv, int VS, const PrefillArgs& a, hipStream_t s) {
 #define KDA_CASE(DK_, DV_, VS_) \
-  if (Dk == DK_ && Dv == DV_ && VS == VS_) return launch_pipe_cfg<PrefillCfg<DK_, DV_, VS_, bf16, GG>>(a, s);
+  if (Dk == DK_ && Dv == DV_ && VS == VS_) return launch_pipe_cfg<PrefillCfg<DK_, DV_, VS_, bf16, GG, 64>>(a, s);
   KDA_CASE(64, 64, 64)
   KDA_CASE(64, 64, 32)
   KDA_CASE(64, 128, 128)
@@ -668,8 +688,29 @@ static hipError_t launch_pipe_dims(int Dk, int Dv, int VS, const PrefillArgs& a,
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill_pipe(int Dk, int Dv, int g_group, int VS, const PrefillArgs& a, hipStream_t stream) {
-  return g_group == 1 ? launch_pipe_dims<1>(Dk, Dv, VS, a, stream) : launch_pipe_dims<64>(Dk, Dv, VS, a, stream);
+// fp32: 64-token chunks at 64 key channels, 32-token chunks at 128 (the
+// double-buffered fp32 operand tiles must fit the 160 KB of LDS).
+template <int GG>
+static hipError_t launch_pipe_f32(int Dk, int Dv, int VS, const PrefillArgs& a, hipStream_t s) {
+#define KDA_CASE(DK_, DV_, VS_, CL_) \
+  if (Dk == DK_ && Dv == DV_ && VS == VS_) return launch_pipe_cfg<PrefillCfg<DK_, DV_, VS_, float, GG, CL_>>(a, s);
+  KDA_CASE(64, 64, 32, 64)
+  KDA_CASE(64, 64, 16, 64)
+  KDA_CASE(64, 128, 32, 64)
+  KDA_CASE(64, 128, 16, 64)
+  KDA_CASE(128, 64, 32, 32)
+  KDA_CASE(128, 64, 16, 32)
+  KDA_CASE(128, 128, 32, 32)
+  KDA_CASE(128, 128, 16, 32)
+#undef KDA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_pipe(bool bf16_io, int Dk, int Dv, int g_group, int VS, const PrefillArgs& a,
+                               hipStream_t stream) {
+  if (bf16_io)
+    return g_group == 1 ? launch_pipe_bf16<1>(Dk, Dv, VS, a, stream) : launch_pipe_bf16<64>(Dk, Dv, VS, a, stream);
+  return g_group == 1 ? launch_pipe_f32<1>(Dk, Dv, VS, a, stream) : launch_pipe_f32<64>(Dk, Dv, VS, a, stream);
 }
 
 }  // namespace kda

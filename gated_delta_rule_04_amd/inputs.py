@@ -113,6 +113,18 @@ def _decay_fn(decay):
         return _neg_softplus_shift(6.0)
     if decay == "none":
         return lambda z: np.zeros_like(z)
+    if decay.startswith("strong:"):
+        # "strong:S": every third key channel (or decay group) decays by about
+        # e^S over 64 tokens, g = (S / 64) (1 + 0.2 tanh z) per token; the
+        # others as "config"
+        per_token = float(decay.split(":", 1)[1]) / 64.0
+        cfg = _neg_softplus_shift(2.0)
+
+        def fn(z):
+            out = cfg(z)
+            out[..., ::3] = per_token * (1.0 + 0.2 * np.tanh(z[..., ::3]))
+            return out
+        return fn
     raise ValueError("unknown decay recipe %r" % (decay,))
 
 
@@ -158,13 +170,15 @@ def make_prefill(B, T, H, dk, dv, dtype="bf16", g_group=1, seed=0, decay="config
 
 
 def make_prologue(B, T, H, dk, dv, dtype="bf16", g_group=1, seed=0, h0=False, cu_seqlens=None, state_std=0.02,
-                  qk_scale=(0.25, 8.0)):
+                  qk_scale=(0.25, 8.0), a_log_mean=0.0):
     """Raw inputs of the fused gate/normalisation prologue.  q_raw, k_raw
     [B,T,H,dk]: N(0,1) rows times a per-row scale drawn log-uniformly from
     qk_scale (not normalised); v [B,T,H,dv] N(0,1); gate logits f
     [B,T,H,dk//g_group] N(0,1); beta logits b_raw [B,T,H] N(0,1); A_log,
     dt_bias [H, dk//g_group] float32 ~ N(0, 0.1^2) and N(-2, 0.1^2), so that
-    the gate reproduces the -softplus(z - 2) decay of the other workloads."""
+    the gate reproduces the -softplus(z - 2) decay of the other workloads;
+    a_log_mean shifts A_log (ln 16: a Mamba-style A of about 16, per-token
+    log-decays near -2 and summed over 64 tokens near -130)."""
     rng = np.random.default_rng(seed)
     rows = B * T
     lo, hi = np.log(qk_scale[0]), np.log(qk_scale[1])
@@ -174,7 +188,7 @@ def make_prologue(B, T, H, dk, dv, dtype="bf16", g_group=1, seed=0, h0=False, cu
     v = _draw(rng, (rows, H, dv), dtype).view(B, T, H, dv)
     b = _draw(rng, (rows, H), dtype).view(B, T, H)
     f = _draw(rng, (rows, H, dk // g_group), dtype).view(B, T, H, dk // g_group)
-    A_log = torch.as_tensor(0.1 * rng.standard_normal((H, dk // g_group)), dtype=torch.float32)
+    A_log = torch.as_tensor(a_log_mean + 0.1 * rng.standard_normal((H, dk // g_group)), dtype=torch.float32)
     dt_bias = torch.as_tensor(-2.0 + 0.1 * rng.standard_normal((H, dk // g_group)), dtype=torch.float32)
     cu = None
     N = B

@@ -65,8 +65,9 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
                                      kda_dtype dt);
 
 /* Chunked prefill (the chunked parallel form of the miniKimiK3 card's KDA
- * bullet; chunk size 64 internally).  Computes o_t for every token and,
- * optionally, each sequence's final state.
+ * bullet).  Computes o_t for every token and, optionally, each sequence's
+ * final state.  Internally the decay is referenced inside 16-token
+ * sub-blocks, the state carried across them in fp32.
  *
  *   H      heads, 1 .. 65535 (a 64-token span of one tensor must stay below
  *          2 GiB: the kernels address a chunk with 32-bit byte offsets);
@@ -90,10 +91,13 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
  *   workspace  device memory of at least kda_chunk_fwd_workspace_bytes(...)
  *          bytes (may be NULL when that is 0); contents are scratch.
  *
- * Input domain: the chunked form references decay to the start of each
- * 64-token chunk; per key channel the summed log-decay over any chunk must
- * stay above -80 (a chunk decay of at least e^-80), otherwise outputs may be
- * non-finite.  Outside that domain use kda_recurrent_step token by token.
+ * Decay domain: the chunked form references decay to the start of each
+ * aligned 16-token sub-block of a sequence (tokens 16j .. 16j+15 counted from
+ * the sequence's first token).  Per key channel, the log-decay summed over
+ * the tokens of one sub-block must stay above -87 (the sub-block's decay
+ * product at least e^-87 = 1.6e-38, the float exponent range); the decay
+ * over longer spans is unrestricted.  A sub-block outside that domain makes
+ * outputs non-finite; kda_recurrent_step has no such limit.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* h0, void* o, float* ht, const int* cu_seqlens, int num_seqs, int B,
@@ -143,8 +147,11 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
  * internally, so o is not an input.
  *
  *   q, k, v, g, beta, h0, cu_seqlens, num_seqs, B, T, H, Dk, Dv, g_group:
- *          as for kda_chunk_fwd (same layouts, same chunk-decay domain, same
- *          head limit).
+ *          as for kda_chunk_fwd (same layouts, same head limit).  Decay
+ *          domain: the backward references decay to the start of each
+ *          64-token chunk, so per key channel the log-decay summed over one
+ *          chunk must stay above -80; outside that, gradients may be
+ *          non-finite.
  *   dout   [B, T, H, Dv]   bf16  cotangent of o
  *   dht    [N, H, Dk, Dv]  f32 or NULL (NULL = zero)  cotangent of ht
  *   dq, dk [B, T, H, Dk]   bf16  gradients (every token written)
@@ -185,8 +192,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
  *   b_raw  [B, T, H] dt              write-strength logits
  *   A_log, dt_bias  [H, Dk/g_group] f32 (device)
  *   everything else as for kda_chunk_fwd.
- * dt = KDA_BF16 only (KDA_F32: KDA_ERR_UNSUPPORTED).  The chunk-decay domain
- * of kda_chunk_fwd applies to the g the prologue produces.
+ * dt = KDA_BF16 or KDA_F32.  The decay domain of kda_chunk_fwd applies to
+ * the g the prologue produces.
  */
 kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
                                   const void* b_raw, const float* A_log, const float* dt_bias, const float* h0,

@@ -55,7 +55,6 @@ def test_chunk_fwd_validation():
     assert fwd(Dk=96) == UNSUPPORTED
     assert fwd(Dv=256) == UNSUPPORTED
     assert fwd(gg=32) == UNSUPPORTED
-    assert fwd(dt=0, Dk=128) == UNSUPPORTED           # float32 prefill supports Dk = 64
     assert fwd(N=2, B=1) == SHAPE                     # without cu_seqlens N must equal B
     assert fwd(cu=P, B=2, N=2) == SHAPE               # varlen needs B == 1
     assert fwd(q=None) == NULL
@@ -178,7 +177,6 @@ def test_prologue_validation():
     pf = lambda dt=1, A=P, Dk=64: L.kda_chunk_fwd_prologue(P, P, P, P, P, A, P, None, P, None, None, 1, 1, 64, 1, Dk,
                                                            64, 1, dt, None, 0, None)
     assert pf(dt=9) == DTYPE
-    assert pf(dt=0) == UNSUPPORTED                    # the fused prefill prologue is bf16 only
     assert pf(A=None) == NULL
     assert pf(Dk=32) == UNSUPPORTED
     ps = lambda dt=1, A=P, N=1, H=1, q=P: L.kda_recurrent_step_prologue(q, P, P, P, P, A, P, P, P, N, H, 64, 64, 1,

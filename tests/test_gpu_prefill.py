@@ -200,3 +200,51 @@ def test_empty_sequence_returns_initial_state():
     o, ht = _gpu(d)
     assert o.numel() == 0
     assert torch.equal(ht, d["h0"])
+
+
+# ---------------------------------------------------------------- strong decay
+@pytest.mark.parametrize("chunk_sum", [-100.0, -300.0])
+@pytest.mark.parametrize("dtype,dk,g_group", [("bf16", 128, 1), ("bf16", 64, 1), ("bf16", 128, 64),
+                                              ("f32", 64, 1), ("f32", 128, 1)])
+def test_strong_decay(chunk_sum, dtype, dk, g_group):
+    """Every third key channel (or decay group) decays by about e^chunk_sum
+    over 64 tokens (alpha ~ e^-1.6 or e^-4.7 per token), far beyond what one
+    reference per 64-token chunk can hold in floats, inside the 16-token
+    sub-block domain.  Against the oracle on every token and the final states,
+    with initial states and a ragged tail."""
+    d = inputs.make_prefill(2, 333, 3, dk, dk, dtype, g_group, seed=int(-chunk_sum) + dk + g_group, h0=True,
+                            decay="strong:%g" % chunk_sum)
+    o, ht = _gpu(d)
+    _check(d, o, ht, tag="strong %g %s dk%d gg%d" % (chunk_sum, dtype, dk, g_group))
+
+
+def test_strong_decay_packed_documents():
+    lens = [200, 1, 77, 0, 300]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = inputs.make_prefill(1, int(cu[-1]), 2, 128, 128, "bf16", 1, seed=77, h0=True, cu_seqlens=cu,
+                            decay="strong:-300")
+    o, ht = _gpu(d)
+    _check(d, o, ht, tag="strong varlen")
+
+
+# ---------------------------------------------------------------- fp32, 128 key channels
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 31, 32, 33, 100, 257])
+def test_f32_dk128_ragged(T):
+    d = inputs.make_prefill(2, T, 3, 128, 128, "f32", 1, seed=500 + T, h0=True)
+    o, ht = _gpu(d)
+    _check(d, o, ht, tag="f32 dk128 T=%d" % T)
+
+
+@pytest.mark.parametrize("dv,g_group", [(64, 1), (128, 64)])
+def test_f32_dk128_shapes(dv, g_group):
+    d = inputs.make_prefill(1, 600, 2, 128, dv, "f32", g_group, seed=600 + dv + g_group, h0=True)
+    o, ht = _gpu(d)
+    _check(d, o, ht, tag="f32 dk128 dv%d gg%d" % (dv, g_group))
+
+
+def test_f32_dk128_packed_documents():
+    lens = [100, 0, 33, 64, 1, 250]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = inputs.make_prefill(1, int(cu[-1]), 2, 128, 128, "f32", 1, seed=601, h0=True, cu_seqlens=cu)
+    o, ht = _gpu(d)
+    _check(d, o, ht, tag="f32 dk128 varlen")

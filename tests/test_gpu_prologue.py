@@ -99,12 +99,6 @@ def test_decode_prologue(dtype, gg):
         q, k = k, q  # vary the next step's inputs
 
 
-def test_prologue_rejects_fp32_prefill():
-    d = inputs.make_prologue(1, 64, 1, 64, 64, "f32", seed=1)
-    with pytest.raises(kda.KdaError):
-        _gpu_chunk(d)
-
-
 def test_chunk_prologue_kimi_k3_heads_sampled():
     """The fused prologue at the bench's prefill shape (B=1, T=32768, H=96,
     dk=dv=128): two sampled heads against the oracle over the whole
@@ -117,3 +111,26 @@ def test_chunk_prologue_kimi_k3_heads_sampled():
                                             sel(d["b_raw"]), f64(d["A_log"][heads]), f64(d["dt_bias"][heads]))
     assert_close("prologue K3 heads o", o[:, :, heads], o_ref, torch.bfloat16)
     assert_close("prologue K3 heads ht", ht[:, heads], h_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_chunk_prologue_mamba_style_gate(dtype, dk):
+    """A_log = ln 16, the Mamba-style A of 16: per-token log-decays near -3
+    and summed over 64 tokens near -190, with single tokens near -50 (a
+    chunk-start reference would overflow on most chunks).  Against the
+    prologue oracle on every token and the final states."""
+    d = inputs.make_prologue(2, 700, 2, dk, 128, dtype, seed=16 + dk, h0=True, a_log_mean=float(np.log(16.0)))
+    o, ht = _gpu_chunk(d)
+    o_ref, h_ref = _oracle_chunk(d)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    assert_close("prologue A16 %s dk%d o" % (dtype, dk), o, o_ref, dt)
+    assert_close("prologue A16 %s dk%d ht" % (dtype, dk), ht, h_ref, dt)
+
+
+@pytest.mark.parametrize("dk,g_group", [(64, 1), (128, 1), (128, 64)])
+def test_chunk_prologue_f32(dk, g_group):
+    d = inputs.make_prologue(2, 300, 2, dk, 64, "f32", g_group=g_group, seed=40 + dk + g_group, h0=True)
+    o, ht = _gpu_chunk(d)
+    o_ref, h_ref = _oracle_chunk(d)
+    assert_close("prologue f32 dk%d gg%d o" % (dk, g_group), o, o_ref, torch.float32)
+    assert_close("prologue f32 dk%d gg%d ht" % (dk, g_group), ht, h_ref, torch.float32)

@@ -66,7 +66,7 @@ def test_random_prefill_bf16(seed):
 
 @pytest.mark.parametrize("seed", range(6))
 def test_random_prefill_f32(seed):
-    c = _draw(600 + seed, dks=(64,))
+    c = _draw(600 + seed)
     d = _prefill(c, "f32", 600 + seed)
     o, ht = _gpu_fwd(d)
     o_ref, h_ref = _oracle_fwd(d)
