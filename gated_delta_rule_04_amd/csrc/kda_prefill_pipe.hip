@@ -88,7 +88,7 @@ struct PipeSmem {
   E ke[2][Cfg::CL][Cfg::KEP];  // KE = K e^{G_end-G+M'}   (token-major; bf16: swizzled)
   E kd[Cfg::CL][Cfg::KP];      // KD = K e^{M-G}          (token-major), transform only
   E v[2][Cfg::CL][Cfg::VS + Cfg::PADE];  // V rows of the slice (loaded by the producers)
-  TT t[2][Cfg::NSB][64];       // T^T of each sub-block, accumulator form
+  TT t[2][Cfg::NSB][64];       // -T^T of each sub-block, accumulator form
   TT p[2][Cfg::NSB][64];       // P^T of each sub-block, accumulator form
   alignas(16) float beta[2][Cfg::CL];
   alignas(16) float phi[2][Cfg::NSB][Cfg::DK];  // e^{G_end - M + M'} of each sub-block
@@ -184,9 +184,12 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
   T* __restrict__ go = static_cast<T*>(args.o);
   const size_t state_off = ((size_t)seq * H + h) * DK * DV;
 
-  f32x4 ident;  // 16x16 identity, accumulator form
+  f32x4 ident, nident;  // 16x16 identity and its negative, accumulator form
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
+  for (int i = 0; i < 4; ++i) {
+    ident[i] = (4 * kg + i == l16) ? 1.f : 0.f;
+    nident[i] = -ident[i];
+  }
 
   // Fragments of the 16-row block blk of a token-major operand tile.
   auto ld_rows = [&](FV (&fr)[SK], const E (*tile)[KP], int blk) {
@@ -303,8 +306,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         Pt[i] = r <= l16 ? Pt[i] : 0.f;       // lower including the diagonal
       }
       const f32x4 X = unit_lower_inverse16<E>(N, Nt, ident);
-      // T^T in accumulator form: lane holds T[l16][4kg + i] = X[l16][4kg + i] b_{4kg + i}
-      const f32x4 Tt = Reg16<E>::prod(X, ident) * br;
+      // -T^T in accumulator form: lane holds -T[l16][4kg + i] = -X[l16][4kg + i] b_{4kg + i}
+      // (stored negated: the state pass forms -R)
+      const f32x4 Tt = Reg16<E>::prod(X, ident) * (-br);
       sm.t[b][I][lane] = TL::pack(Tt);
       sm.p[b][I][lane] = TL::pack(Pt);
     };
@@ -441,11 +445,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         const bool writer = wave % WPB == 0 && rbw == 0;  // one per (sub-block, channel group)
 #pragma unroll
         for (int c4 = 0; c4 < 8; c4 += 4) {
-          float mid[4], fe1[4], fe2[4];
+          // base: the decay before this thread's rows, less M; fe1 = e^{G_end - M} = e^M
+          float base[4], fe1[4], fe2[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            mid[c] = 0.5f * gend[c4 + c];
-            fe1[c] = fast_exp2(gend[c4 + c] - mid[c]);
+            const float mid = 0.5f * gend[c4 + c];
+            base[c] = pre[c4 + c] + off[c4 + c] - mid;
+            fe1[c] = fast_exp2(mid);
             fe2[c] = fast_exp2(0.5f * gnext[c4 + c]);
           }
 #pragma unroll
@@ -454,8 +460,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
             float qo[4], ko[4], eo[4], dd[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const float Gc = pre[c4 + c] + off[c4 + c] + G[j][c4 + c];
-              const float el = fast_exp2(Gc - mid[c]), er = fast_exp2(mid[c] - Gc);
+              const float x = base[c] + G[j][c4 + c];  // G - M at this row
+              const float el = fast_exp2(x), er = fast_exp2(-x);
               const float kx = elem(rk[j], c4 + c) * ik[j];
               qo[c] = elem(rq[j], c4 + c) * iq[j] * el;
               ko[c] = kx * el;
@@ -473,9 +479,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
           if (writer) {  // the state factors of the sub-block (and e^M of a chunk's first)
             *reinterpret_cast<f32x4*>(&sm.phi[bG][sbw][ch + c4]) =
                 f32x4{fe1[0] * fe2[0], fe1[1] * fe2[1], fe1[2] * fe2[2], fe1[3] * fe2[3]};
-            if (sbw == 0)
-              *reinterpret_cast<f32x4*>(&sm.psi[bG][ch + c4]) =
-                  f32x4{fast_exp2(mid[0]), fast_exp2(mid[1]), fast_exp2(mid[2]), fast_exp2(mid[3])};
+            if (sbw == 0) *reinterpret_cast<f32x4*>(&sm.psi[bG][ch + c4]) = f32x4{fe1[0], fe1[1], fe1[2], fe1[3]};
           }
         }
 #pragma unroll
@@ -545,16 +549,17 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
       for (int s = 0; s < SK; ++s) SF[j][s] = acc_frag(S[j], s, E());
-    // ---- R = V - KB S (V enters through an exact identity product) ----
+    // ---- -R = KB S - V (V enters through an exact product with the negated
+    // identity; the transform is stored negated, so that U = (-T)(-R)) ----
     f32x4 R[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) R[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < SK; ++s)
 #pragma unroll
-      for (int j = 0; j < TPW; ++j) R[j] = F::mma(ka[s], acc_frag_neg(S[j], s, E()), R[j]);
+      for (int j = 0; j < TPW; ++j) R[j] = F::mma(ka[s], SF[j][s], R[j]);
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) R[j] = Reg16<E>::rows(vr[j], ident, R[j]);
+    for (int j = 0; j < TPW; ++j) R[j] = Reg16<E>::rows(vr[j], nident, R[j]);
     // ---- O^T = S^T QB^T ----
     f32x4 O[TPW];
 #pragma unroll
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     for (int s = 0; s < SK; ++s)
 #pragma unroll
       for (int j = 0; j < TPW; ++j) O[j] = F::mma(SF[j][s], qa[s], O[j]);
-    // ---- U = T R (R unrounded), O^T += U^T P^T, write o of the sub-block ----
+    // ---- U = (-T)(-R) (-R unrounded), O^T += U^T P^T, write o of the sub-block ----
     f32x4 U[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
