@@ -330,6 +330,19 @@ def main():
             "alg_bytes_per_launch": pre_bytes,
             "avg_launch_ms": pre_avg,
         },
+        # MFMA beside HBM for the prefill: algorithmic flops against the bf16
+        # dense peak (the prefill's arithmetic intensity, ~104 flop/B at d=128,
+        # is below the MI355X ridge of ~315 flop/B, so HBM is the binding roof)
+        "roofline_prefill_mfma": {
+            "kernel": "chunk_fwd_pipe_kernel (prefill, bf16)",
+            "bound": "mfma",
+            "achieved": pre_tfs,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": pre_tfs / PEAK_BF16_TFLOPS,
+            "alg_flops_per_launch": pre_flops,
+            "avg_launch_ms": pre_avg,
+        },
         "roofline_decode": {
             "kernel": "decode_step_kernel",
             "bound": "hbm",
@@ -383,12 +396,27 @@ def main():
         ev_run[i + 1].record()
     torch.cuda.synchronize()
     run_ms = [ev_run[i].elapsed_time(ev_run[i + 1]) for i in range(len(D))]
+    run_med = pct(run_ms, 50)
     line["decode"]["consecutive_steps"] = {
         "steps": len(D),
         "ms_total": sum(run_ms),
-        "ms_median": pct(run_ms, 50),
+        "ms_median": run_med,
         "ms_p10": pct(run_ms, 10),
         "ms_p90": pct(run_ms, 90),
+        "tokens_per_s": N / (run_med * 1e-3),
+        "hbm_frac_alg": dec_bytes / (run_med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    # the decode workload as stated (64 back-to-back steps): its own roofline
+    # line, beside the step timed between prefill calls above
+    line["roofline_decode_consecutive"] = {
+        "kernel": "decode_step_kernel (64 consecutive steps, median step)",
+        "bound": "hbm",
+        "achieved": dec_bytes / (run_med * 1e-3) / 1e9,
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": dec_bytes / (run_med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "alg_bytes_per_launch": dec_bytes,
+        "median_launch_ms": run_med,
     }
     del st_run
     # Serving form (outside the timed step above): the same decode inputs over a
