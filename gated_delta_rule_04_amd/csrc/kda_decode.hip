@@ -18,12 +18,15 @@
 // per row) and a strided set of rows; a wavefront's loads cover whole
 // contiguous rows, so every access is a fully coalesced 16-byte load/store.
 // The state is read with non-temporal loads: it is streamed once per step and
-// the pool is far larger than the caches.  A bf16 pool is also written with
-// non-temporal stores; the fp32 state keeps ordinary stores, which measured
-// faster when the step runs between prefill calls.  The two column reductions run
-// through cross-lane shuffles and an LDS exchange between the 8 wavefronts.
-// An in-place read-modify-write stream of this shape runs at about 67% of the
-// 8 TB/s peak on MI355X (measured: read-only about 74%, write-only about 70%).
+// the pool is far larger than the caches.  It is written back with
+// non-temporal stores except by the last eighth of the grid, whose ordinary
+// stores stay in the 256 MB memory-side cache and drain under the next kernel:
+// at N=256, H=96, d=128 (1.6 GB of fp32 state) this runs 64 back-to-back steps
+// at 0.557 ms each, against 0.602 ms with ordinary stores throughout and 0.567
+// ms with non-temporal stores throughout, and keeps a step that alternates
+// with the prefill at 0.553 ms (0.576 ms with non-temporal stores throughout).
+// The two column reductions run through cross-lane shuffles and an LDS
+// exchange between the 8 wavefronts.
 //
 // Serving form: the states live in a pool and sequence n uses slot slots[n]
 // (the state pool that bounds concurrency in the K3-Tiny-L13 card's serving
@@ -61,14 +64,23 @@ __device__ __forceinline__ f32x4 load_state4(const f16* p) {
   const f16x4 h = __builtin_bit_cast(f16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p)));
   return __builtin_convertvector(h, f32x4);
 }
-__device__ __forceinline__ void store_state4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
-__device__ __forceinline__ void store_state4(bf16* p, const f32x4& x) {
-  const bf16x4 b = to_bf16x4(x);  // RNE
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, b), reinterpret_cast<u32x2v*>(p));
+// Write-back of four state values; NT selects non-temporal stores.
+template <bool NT>
+__device__ __forceinline__ void store_state4(float* p, const f32x4& x) {
+  if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+  else *reinterpret_cast<f32x4*>(p) = x;
 }
+template <bool NT>
+__device__ __forceinline__ void store_state4(bf16* p, const f32x4& x) {
+  const u32x2v b = __builtin_bit_cast(u32x2v, to_bf16x4(x));  // RNE
+  if constexpr (NT) __builtin_nontemporal_store(b, reinterpret_cast<u32x2v*>(p));
+  else *reinterpret_cast<u32x2v*>(p) = b;
+}
+template <bool NT>
 __device__ __forceinline__ void store_state4(f16* p, const f32x4& x) {
-  const f16x4 h = __builtin_convertvector(x, f16x4);  // RNE (the default rounding mode)
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, h), reinterpret_cast<u32x2v*>(p));
+  const u32x2v h = __builtin_bit_cast(u32x2v, __builtin_convertvector(x, f16x4));  // RNE (the default rounding mode)
+  if constexpr (NT) __builtin_nontemporal_store(h, reinterpret_cast<u32x2v*>(p));
+  else *reinterpret_cast<u32x2v*>(p) = h;
 }
 
 template <int DK, int DV, typename T, int GG, typename SE, bool PRO>
@@ -218,10 +230,26 @@ __global__ __launch_bounds__(512) void decode_step_kernel(const T* __restrict__ 
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[u * DV + 4 * cg + c] = from_f32<T>(out[c]);
   }
+  // Write-back: the workgroups of the first seven eighths of the grid stream
+  // their states out with non-temporal stores; the last eighth uses ordinary
+  // stores, which stay in the memory-side cache and drain under whatever runs
+  // next.  The empty asm statements around the first sequence keep the
+  // compiler from hoisting or sinking the two store sequences into one (which
+  // drops the non-temporal hint).
+  if (blockIdx.x < gridDim.x - gridDim.x / 8) {
+    asm volatile("" ::: "memory");
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int r = rg + RG * m;
-    store_state4(S + (size_t)r * DV + 4 * cg, s[m] + (s_k[r] * kscale) * uu);
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + RG * m;
+      store_state4<true>(S + (size_t)r * DV + 4 * cg, s[m] + (s_k[r] * kscale) * uu);
+    }
+    asm volatile("" ::: "memory");
+  } else {
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + RG * m;
+      store_state4<false>(S + (size_t)r * DV + 4 * cg, s[m] + (s_k[r] * kscale) * uu);
+    }
   }
 }
 
