@@ -30,6 +30,19 @@
 //        dg = reverse cumulative sum of dG over the chunk (summed over a
 //             decay group when one log-decay value serves 64 channels).
 //
+// Decay references.  Written with chunk-start factors, Kh = K e^{-G} grows as
+// e^{-G} and leaves fp32 once a channel's decay over the chunk passes about
+// -88.  No factor here is referenced further away than one 16-token block:
+// the operand rows are stored as qt = Q e^{G - m}, kt = K e^{G - m},
+// kh = K e^{m - G} with m the midpoint of the row's block (factors within
+// e^{|block sum| / 2}); a product of block-I rows with block-J rows (I > J)
+// carries the per-channel shift e^{m_I - m_J} <= 1 on one operand; the state
+// side uses Kt = kt e^{m}, Qt = qt e^{m} and Kb = Kh Diag(gam) = kh e^{G_last - m}
+// (all <= 1).  Every product equals its chunk-start form exactly (the
+// references cancel), so the gradients are taken with the references held
+// constant, and the path is exact while every 16-token block's decay sum
+// stays above about -170 per channel.
+//
 // Design for MI355X.  Steps 2 and 4 are fully parallel over (chunk, head):
 // one workgroup per chunk-head, one wavefront per 16 key channels, all
 // operand tiles in LDS and every product on v_mfma_f32_16x16x32_bf16 with
@@ -120,6 +133,32 @@ __device__ __forceinline__ void lower_tile(int j, int& I, int& J) {
   }
 }
 
+// A bf16 operand fragment scaled elementwise: elements 0..3 by lo, 4..7 by hi
+// (rounded to nearest even).
+__device__ __forceinline__ FV scale8(const FV& a, const f32x4& lo, const f32x4& hi) {
+  const f32x4 x = f32x4{(float)a[0], (float)a[1], (float)a[2], (float)a[3]} * lo;
+  const f32x4 y = f32x4{(float)a[4], (float)a[5], (float)a[6], (float)a[7]} * hi;
+  return __builtin_shufflevector(to_bf16x4(x), to_bf16x4(y), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 splat4(float x) { return f32x4{x, x, x, x}; }
+// The per-channel values of v for the 8 channels of a row fragment of slab s
+// (channels 32s + 4kg .. +3 and 32s + 16 + 4kg .. +3).
+__device__ __forceinline__ void row_vals(const float* v, int s, int kg, f32x4& lo, f32x4& hi) {
+  lo = *reinterpret_cast<const f32x4*>(v + 32 * s + 4 * kg);
+  hi = *reinterpret_cast<const f32x4*>(v + 32 * s + 16 + 4 * kg);
+}
+// e^{a_c - b_c} (a, b in log2 units) for the channels of a row fragment of slab s.
+__device__ __forceinline__ void row_shift(const float* a, const float* b, int s, int kg, f32x4& lo, f32x4& hi) {
+  f32x4 a0, a1, b0, b1;
+  row_vals(a, s, kg, a0, a1);
+  row_vals(b, s, kg, b0, b1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = fast_exp2(a0[i] - b0[i]);
+    hi[i] = fast_exp2(a1[i] - b1[i]);
+  }
+}
+
 // Sequence geometry shared by the kernels.
 struct Seq {
   int seq, tok0, len;
@@ -172,9 +211,14 @@ struct FrontTiles {
   bf16 u1[C * CTP];  // local: T^T rows; prep: P rows
   bf16 u2[C * CTP];  // local: P^T rows
   bf16 x[C * CTP];   // local: X rows
-  alignas(16) float gam[DK];
+  alignas(16) float gam[DK];    // e^{G_last}
+  alignas(16) float glast[DK];  // G_last (log2 units)
   alignas(16) float beta[C];
+  // the blocks' decay sums while gating; afterwards the block references m_b
+  // (log2 units, the midpoint of block b's decay, chunk-relative)
   alignas(16) float gsum[Cfg::NB][DK];
+  alignas(16) float em[Cfg::NB][DK];  // e^{m_b}: block-referenced rows -> chunk start
+  alignas(16) float eb[Cfg::NB][DK];  // e^{G_last - m_b}: block-referenced rows -> chunk end
 };
 template <class Cfg>
 struct FrontScratch {
@@ -184,7 +228,8 @@ struct FrontScratch {
 
 template <class Cfg, bool LOCAL>
 __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int h, int c, FrontTiles<Cfg>& ft,
-                                            FrontScratch<Cfg>& fs, float (&G2)[Cfg::TB], const f32x4& ident) {
+                                            FrontScratch<Cfg>& fs, float (&G2)[Cfg::TB], float& mref, float& glref,
+                                            const f32x4& ident) {
   constexpr int DK = Cfg::DK, C = Cfg::C, GG = Cfg::GG, KHP = Cfg::KHP, CTP = Cfg::CTP, AP = Cfg::AP;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, TB = Cfg::TB, SK = DK / 32;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
@@ -232,20 +277,32 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
   {
     float off = 0.f;
     for (int b = 0; b < tb; ++b) off += ft.gsum[b][ch];
+    // the block's reference: the midpoint of its decay, so that the factors
+    // e^{+-(G - m)} of its rows stay within e^{|block sum| / 2}
+    const float m = off + 0.5f * ft.gsum[tb][ch];
+    mref = m;
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       G2[j] += off;
       const int r = tb * TB + j;
       const float q = to_f32(qv[j]), kk = to_f32(kv[j]);
-      const float eg = fast_exp2(G2[j]), emg = fast_exp2(-G2[j]);
+      const float eu = fast_exp2(G2[j] - m), ed = fast_exp2(m - G2[j]);
       const int o = r * KHP + swz(r, ch);
-      ft.qt[o] = (bf16)(q * eg);
-      ft.kt[o] = (bf16)(kk * eg);
-      ft.kh[o] = (bf16)(kk * emg);
+      ft.qt[o] = (bf16)(q * eu);
+      ft.kt[o] = (bf16)(kk * eu);
+      ft.kh[o] = (bf16)(kk * ed);
     }
-    if (tb == Cfg::NB - 1) ft.gam[ch] = fast_exp2(G2[TB - 1]);
+    if (tb == Cfg::NB - 1) {
+      ft.gam[ch] = fast_exp2(G2[TB - 1]);
+      ft.glast[ch] = G2[TB - 1];
+    }
+    __syncthreads();  // every thread has read the block sums
+    ft.gsum[tb][ch] = m;
+    ft.em[tb][ch] = fast_exp2(m);
   }
   __syncthreads();
+  glref = ft.glast[ch];
+  ft.eb[tb][ch] = fast_exp2(glref - mref);
 
   auto rows = [&](FV (&fr)[SK], const bf16* tile, int blk) {
 #pragma unroll
@@ -299,14 +356,21 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
         st_acc<CTP>(ft.x, 16 * I, 16 * I, Xdiag, ident, l16, kg);
       }
     } else {
-      FV ktr[SK], khr[SK];
+      FV ktr[SK], khr[SK], qtr[SK];
       rows(ktr, ft.kt, I);
       rows(khr, ft.kh, J);
+      rows(qtr, ft.qt, I);
+      // the pair's reference shift e^{m_I - m_J} (<= 1) on the block-I operands
+#pragma unroll
+      for (int s = 0; s < SK; ++s) {
+        f32x4 lo, hi;
+        row_shift(ft.gsum[I], ft.gsum[J], s, kg, lo, hi);
+        ktr[s] = scale8(ktr[s], lo, hi);
+        qtr[s] = scale8(qtr[s], lo, hi);
+      }
       // A_IJ rows: lane holds B[16I + l16][16J + 4kg + i], scaled by b of its row
       const f32x4 Bt = mma_rows(khr, ktr) * ft.beta[16 * I + l16];
       *reinterpret_cast<f32x4*>(&fs.a[(16 * I + l16) * AP + 16 * J + 4 * kg]) = Bt;
-      FV qtr[SK];
-      rows(qtr, ft.qt, I);
       if constexpr (LOCAL)
         st_acc_t<CTP>(ft.u2, 16 * I, 16 * J, mma_rows(qtr, khr), l16, kg);  // P^T rows
       else
@@ -388,8 +452,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
       op[j] = bload<u32x4>(bo, r * rsv + c8 * 2);
     }
   }
-  float G2[Cfg::TB];
-  chunk_front<Cfg, false>(A, sq, h, c, sm.ft, sm.u.fs, G2, ident);
+  float G2[Cfg::TB], mref, glref;
+  chunk_front<Cfg, false>(A, sq, h, c, sm.ft, sm.u.fs, G2, mref, glref, ident);
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int p = tid + NT * j, r = p / (DV / 8), c8 = 8 * (p % (DV / 8));
@@ -397,15 +461,21 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
     *reinterpret_cast<u32x2*>(&sm.u.dO[r * DVP + swz(r, c8 + 4)]) = u32x2{op[j][2], op[j][3]};
   }
 
-  // W = T Kt (column tile w, all token tiles), Z = Qt - P W
+  // W = T Kt (column tile w, all token tiles), Z = Qt - P W, with the
+  // chunk-start forms Kt = kt e^{m}, Qt = qt e^{m} of the block-referenced
+  // tiles (factors <= 1; lane channel 16w + l16)
+  const int cw = 16 * w + l16;
   f32x4 W[4], Z[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     f32x4 acc = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      if (32 * s <= 16 * tt + 15) acc = F::mma(ld_row<CTP>(sm.ft.t, 16 * tt + l16, s, kg),
-                                               F::ld_tr<KHP>(sm.ft.kt, 16 * w, s, l16, kg), acc);
+      if (32 * s <= 16 * tt + 15)
+        acc = F::mma(ld_row<CTP>(sm.ft.t, 16 * tt + l16, s, kg),
+                     scale8(F::ld_tr<KHP>(sm.ft.kt, 16 * w, s, l16, kg), splat4(sm.ft.em[2 * s][cw]),
+                            splat4(sm.ft.em[2 * s + 1][cw])),
+                     acc);
     W[tt] = acc;
   }
 #pragma unroll
@@ -418,14 +488,15 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * tt + 4 * kg + i;
-      Z[tt][i] = (float)sm.ft.qt[r * KHP + swz(r, 16 * w + l16)] - pw[i];
+      Z[tt][i] = (float)sm.ft.qt[r * KHP + swz(r, cw)] * sm.ft.em[tt][cw] - pw[i];
     }
   }
   __syncthreads();  // dO complete
 
   const size_t uh = (size_t)slot * A.H + h;
-  // F = Diag(gam)(I - Kh^T W) = Diag(gam) - M.  The decay part is kept apart
-  // (gam, fp32) and applied exactly by the reverse pass; only -M, a
+  // F = Diag(gam)(I - Kh^T W) = Diag(gam) - M, M = Kb^T W with Kb = Kh
+  // Diag(gam) = kh e^{G_last - m} (factors <= 1).  The decay part is kept
+  // apart (gam, fp32) and applied exactly by the reverse pass; only -M, a
   // correction that is small where the chain is long and undamped, is rounded
   // to bf16.  Rounding F whole would round its near-1 diagonal in every chunk.
   // Tile (r, w) of -M is stored as A-operand fragments of -M^T,
@@ -436,11 +507,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
   for (int r = 0; r < DK / 16; ++r) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int s = 0; s < 2; ++s) acc = F::mma(F::ld_tr<KHP>(sm.ft.kh, 16 * r, s, l16, kg), F::acc2(W[2 * s], W[2 * s + 1]), acc);
-    const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.ft.gam[16 * r + 4 * kg]);
-    f32x4 f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = -gm[i] * acc[i];
+    for (int s = 0; s < 2; ++s) {
+      const int cr = 16 * r + l16;
+      const FV kb = scale8(F::ld_tr<KHP>(sm.ft.kh, 16 * r, s, l16, kg), splat4(sm.ft.eb[2 * s][cr]),
+                           splat4(sm.ft.eb[2 * s + 1][cr]));
+      acc = F::mma(kb, F::acc2(W[2 * s], W[2 * s + 1]), acc);
+    }
+    const f32x4 f = -acc;
     store4<bf16>(fw + ((size_t)(w * KS + r / 2) * 64 + lane) * 8 + 4 * (r & 1), f);
   }
   // b = Z^T dO, bf16 accumulator tiles [row tile w][column tile][lane][4]
@@ -666,9 +739,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   load_slice(0);
   load_v(0);
 
-  float G2[TB];
+  float G2[TB], mref, glref;
   FrontTiles<Cfg>& ft = sm.m.ft;
-  chunk_front<Cfg, true>(A, sq, h, c, ft, sm.m.u.fs, G2, ident);
+  chunk_front<Cfg, true>(A, sq, h, c, ft, sm.m.u.fs, G2, mref, glref, ident);
   auto& sl = sm.m.u.sl;
   auto& cc = sm.m.u.cc;
 
@@ -683,13 +756,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   for (int v0 = 0; v0 < DV; v0 += VSL) {
     __syncthreads();  // the front, or the previous slice, is done with the slice tiles
     {
-      // S and dSt = Diag(gam) dS_out; dO
+      // S and dS_out; dO
       const int r = pr, p8 = pp8;
       *reinterpret_cast<u32x2*>(&sl.S[r * SP + swz(r, p8)]) = u32x2{s8[0], s8[1]};
       *reinterpret_cast<u32x2*>(&sl.S[r * SP + swz(r, p8 + 4)]) = u32x2{s8[2], s8[3]};
-      const float gm = ft.gam[r];
-      store4<bf16>(&sl.dS[r * SP + swz(r, p8)], f32x4{(float)d8[0], (float)d8[1], (float)d8[2], (float)d8[3]} * gm);
-      store4<bf16>(&sl.dS[r * SP + swz(r, p8 + 4)], f32x4{(float)d8[4], (float)d8[5], (float)d8[6], (float)d8[7]} * gm);
+      const u32x4 d4 = __builtin_bit_cast(u32x4, d8);
+      *reinterpret_cast<u32x2*>(&sl.dS[r * SP + swz(r, p8)]) = u32x2{d4[0], d4[1]};
+      *reinterpret_cast<u32x2*>(&sl.dS[r * SP + swz(r, p8 + 4)]) = u32x2{d4[2], d4[3]};
       if (tid < 4 * C) {
         *reinterpret_cast<u32x2*>(&sl.dO[r * SP + swz(r, p8)]) = u32x2{o8[0], o8[1]};
         *reinterpret_cast<u32x2*>(&sl.dO[r * SP + swz(r, p8 + 4)]) = u32x2{o8[2], o8[3]};
@@ -697,18 +770,28 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     }
     if (v0 + VSL < DV) load_slice(v0 + VSL);
     __syncthreads();
-    // R = V - Kt S and dU = Kh dSt + P^T dO (independent of each other)
+    // R = V - Kt S and dU = Kh dSt + P^T dO = Kb dS_out + P^T dO (independent
+    // of each other), with the chunk-start Kt = kt e^{m} and the chunk-end
+    // Kb = kh e^{G_last - m} of the block-referenced rows
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
       f32x4 acc = zero4(), du = zero4();
 #pragma unroll
-      for (int s = 0; s < SK; ++s)
-        acc = F::mma(ld_row<KHP>(ft.kt, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.S, 16 * ct, s, l16, kg), acc);
+      for (int s = 0; s < SK; ++s) {
+        f32x4 lo, hi;
+        row_vals(ft.em[tt], s, kg, lo, hi);
+        acc = F::mma(scale8(ld_row<KHP>(ft.kt, 16 * tt + l16, s, kg), lo, hi), F::ld_tr<SP>(sl.S, 16 * ct, s, l16, kg),
+                     acc);
+      }
       st_acc<SP>(sl.R, 16 * tt, 16 * ct, Reg16<bf16>::rows(vr[jj], ident, -acc), ident, l16, kg);
 #pragma unroll
-      for (int s = 0; s < SK; ++s)
-        du = F::mma(ld_row<KHP>(ft.kh, 16 * tt + l16, s, kg), F::ld_tr<SP>(sl.dS, 16 * ct, s, l16, kg), du);
+      for (int s = 0; s < SK; ++s) {
+        f32x4 lo, hi;
+        row_vals(ft.eb[tt], s, kg, lo, hi);
+        du = F::mma(scale8(ld_row<KHP>(ft.kh, 16 * tt + l16, s, kg), lo, hi), F::ld_tr<SP>(sl.dS, 16 * ct, s, l16, kg),
+                    du);
+      }
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         if (32 * s + 31 >= 16 * tt)
@@ -782,7 +865,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     }
   }
   rs = rows4_sum(rs);
-  if (kg == 0) sm.dgc[16 * w + l16] = rs;
+  if (kg == 0) sm.dgc[16 * w + l16] = rs * ft.gam[16 * w + l16];
   __syncthreads();  // slice tiles are free: the C x C gradient tiles take their place
 
   // zero the C x C gradient tiles (their zero blocks are never written)
@@ -837,14 +920,26 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
       if (32 * s <= 16 * J + 15)
         acc = F::mma(ld_row<CTP>(cc.Y, 16 * I + l16, s, kg), ld_row<CTP>(ft.x, 16 * J + l16, s, kg), acc);
 #pragma unroll
-    for (int s = 0; s < SK; ++s)
-      bm = F::mma(ld_row<KHP>(ft.kt, 16 * I + l16, s, kg), ld_row<KHP>(ft.kh, 16 * J + l16, s, kg), bm);
-    f32x4 dA = -acc;
-    if (I == J) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dA[i] = l16 < 4 * kg + i ? dA[i] : 0.f;
+    for (int s = 0; s < SK; ++s) {
+      FV kt = ld_row<KHP>(ft.kt, 16 * I + l16, s, kg);
+      if (I != J) {
+        f32x4 lo, hi;
+        row_shift(ft.gsum[I], ft.gsum[J], s, kg, lo, hi);
+        kt = scale8(kt, lo, hi);
+      }
+      bm = F::mma(kt, ld_row<KHP>(ft.kh, 16 * J + l16, s, kg), bm);
     }
-    f32x4 pr = dA * bm;
+    f32x4 dA = -acc, pr = dA * bm;
+    if (I == J) {
+      // strictly lower part only; the upper part of a diagonal B tile holds
+      // e^{G_i - G_j} with G_i > G_j, which may overflow: select, not scale
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool lower = l16 < 4 * kg + i;
+        dA[i] = lower ? dA[i] : 0.f;
+        pr[i] = lower ? pr[i] : 0.f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = row_sum<16>(pr[i]);
     if (l16 == 0) *reinterpret_cast<f32x4*>(&sm.dba[J][16 * I + 4 * kg]) = pr;
@@ -852,19 +947,33 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     st_acc<CTP>(cc.dB, 16 * I, 16 * J, dA * br, ident, l16, kg);
   }
   __syncthreads();
-  // the [DK][C] results of wave w
+  // the [DK][C] results of wave w, as gradients of the block-referenced tiles
+  // (row channel 16w + 4kg + i, column token 16tt + l16): the state terms
+  // carry e^{m} of the token's block; a pair of blocks (I, J) contributes
+  // through its reference shift e^{m_I - m_J} (zero for I < J, where the
+  // masked tiles vanish), applied to the transposed operand of lane channel
+  // 16w + l16 whose elements 0..3 and 4..7 lie in blocks 2s and 2s + 1
+  const int cw = 16 * w + l16;
+  const float* mw0 = &ft.gsum[0][cw];
+  auto shift = [&](int I, int J) { return I >= J ? fast_exp2(mw0[I * DK] - mw0[J * DK]) : 0.f; };
   f32x4 dKtT[4], dKhT[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    dKtT[tt] = -SdR[tt];
+    const f32x4 emr = *reinterpret_cast<const f32x4*>(&ft.em[tt][16 * w + 4 * kg]);
+    dQtT[tt] *= emr;
+    dKtT[tt] = -SdR[tt] * emr;
     dKhT[tt] = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const FV khT = F::ld_tr<KHP>(ft.kh, 16 * w, s, l16, kg);
+      const FV khT = scale8(F::ld_tr<KHP>(ft.kh, 16 * w, s, l16, kg), splat4(shift(tt, 2 * s)),
+                            splat4(shift(tt, 2 * s + 1)));
       dQtT[tt] = F::mma(khT, ld_row<CTP>(cc.dP, 16 * tt + l16, s, kg), dQtT[tt]);
       dKtT[tt] = F::mma(khT, ld_row<CTP>(cc.dB, 16 * tt + l16, s, kg), dKtT[tt]);
-      dKhT[tt] = F::mma(F::ld_tr<KHP>(ft.kt, 16 * w, s, l16, kg), F::ld_tr<CTP>(cc.dB, 16 * tt, s, l16, kg), dKhT[tt]);
-      dKhT[tt] = F::mma(F::ld_tr<KHP>(ft.qt, 16 * w, s, l16, kg), F::ld_tr<CTP>(cc.dP, 16 * tt, s, l16, kg), dKhT[tt]);
+      const f32x4 lo = splat4(shift(2 * s, tt)), hi = splat4(shift(2 * s + 1, tt));
+      dKhT[tt] = F::mma(scale8(F::ld_tr<KHP>(ft.kt, 16 * w, s, l16, kg), lo, hi),
+                        F::ld_tr<CTP>(cc.dB, 16 * tt, s, l16, kg), dKhT[tt]);
+      dKhT[tt] = F::mma(scale8(F::ld_tr<KHP>(ft.qt, 16 * w, s, l16, kg), lo, hi),
+                        F::ld_tr<CTP>(cc.dP, 16 * tt, s, l16, kg), dKhT[tt]);
     }
   }
   __syncthreads();  // every tile is consumed: the final stage reuses the space
@@ -887,13 +996,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
 #pragma unroll
   for (int j = 0; j < TB; ++j) {
     const int r = tb * TB + j;
-    const float dqt = sm.fin[0][r][ch], dkt = sm.fin[1][r][ch], dkb = sm.fin[3][r][ch];
-    const float dkh = sm.fin[2][r][ch] + dkb;
-    const float eg = fast_exp2(G2[j]), emg = fast_exp2(-G2[j]);
+    const float dqt = sm.fin[0][r][ch], dkt = sm.fin[1][r][ch], dkh = sm.fin[2][r][ch], dkb = sm.fin[3][r][ch];
+    // back from the block reference m and from the chunk end
+    const float eu = fast_exp2(G2[j] - mref), ed = fast_exp2(mref - G2[j]), ee = fast_exp2(glref - G2[j]);
     const float q = to_f32(qf[j]), kk = to_f32(kf[j]);
-    const float dq = dqt * eg, a = dkt * eg, b = dkh * emg;
+    const float dq = dqt * eu, a = dkt * eu, kbe = dkb * ee, b = dkh * ed + kbe;
     dG[j] = q * dq + kk * (a - b);
-    skb += dkb * kk * emg;
+    skb += kbe * kk;
     bstore_bf16(dq, bdq, r * rsk + ch * 2);
     bstore_bf16(a + b, bdk, r * rsk + ch * 2);
   }

@@ -140,3 +140,100 @@ def chunked_backward(q, k, v, g, beta, S0, do, dST, C):
         res["dg"][s:e] = np.cumsum(dG[::-1], axis=0)[::-1]
         res["dbeta"][s:e] = db
     return res
+
+
+def _block_refs(g, B):
+    """Chunk-local cumulative decay G and, per row, the reference m of its
+    B-row block: the midpoint of the block's decay, so that the factors
+    e^{+-(G - m)} of its rows stay within e^{|block sum| / 2}."""
+    G = np.cumsum(g, axis=0)
+    m = np.zeros_like(G)
+    for a in range(0, G.shape[0], B):
+        e = min(G.shape[0], a + B)
+        prev = G[a - 1] if a > 0 else np.zeros(G.shape[1])
+        m[a:e] = prev + 0.5 * (G[e - 1] - prev)
+    return G, m
+
+
+def chunked_backward_blockref(q, k, v, g, beta, S0, do, dST, C=64, B=16, rnd=None):
+    """The same gradients as chunked_backward, with every factor of the block
+    algebra referenced so that none exceeds 1 beyond one B-row block: the
+    operand rows qt = Q e^{G - m}, kt = K e^{G - m}, kh = K e^{m - G} use
+    their block's reference m; a pair of blocks (I, J), I >= J, of the k-k
+    and q-k products carries the shift e^{m_I - m_J} <= 1; the state side
+    uses Kt = kt e^{m}, Qt = qt e^{m} and Kb = kh e^{G_c - m} (all <= 1).
+    Each product is the chunk-start one exactly (the references cancel), so
+    the gradients follow with the references held constant.  rnd, if given,
+    is applied where the GPU path stores a bf16 operand (the referenced rows
+    and their scaled forms, T, S, dS and the per-chunk transfer), to model its
+    roundings."""
+    r = rnd if rnd is not None else (lambda x: x)
+    L, dk = q.shape
+    S = np.array(S0, dtype=np.float64, copy=True)
+    chunks, S_in = [], []
+    for s in range(0, L, C):
+        e = min(L, s + C)
+        c = e - s
+        G, m = _block_refs(g[s:e], B)
+        qt, kt, kh = r(q[s:e] * np.exp(G - m)), r(k[s:e] * np.exp(G - m)), r(k[s:e] * np.exp(m - G))
+        blk = np.arange(c) // B
+        mb = m[np.minimum(np.arange(0, c, B), c - 1)]           # [blocks, dk]
+        shift = np.where((blk[:, None] >= blk[None, :])[:, :, None], mb[blk][:, None, :] - mb[blk][None, :, :], -np.inf)
+        D = np.exp(shift)                                        # e^{m_I - m_J} for I >= J, else 0
+        Bm = np.tril(np.einsum("ic,jc,ijc->ij", kt, kh, D), -1)
+        P = np.tril(np.einsum("ic,jc,ijc->ij", qt, kh, D), 0)
+        b = beta[s:e]
+        X = np.linalg.inv(np.eye(c) + b[:, None] * Bm)
+        T = r(X * b[None, :])
+        Kt, Qt, Kb = r(kt * np.exp(m)), r(qt * np.exp(m)), r(kh * np.exp(G[-1] - m))
+        gam = np.exp(G[-1])
+        chunks.append(dict(s=s, e=e, G=G, m=m, qt=qt, kt=kt, kh=kh, D=D, B=Bm, P=P, X=X, T=T, Kt=Kt, Qt=Qt,
+                           Kb=Kb, gam=gam))
+        S_in.append(r(S.copy()))
+        U = T @ (v[s:e] - Kt @ S)
+        S = gam[:, None] * S + Kb.T @ U
+    # per-chunk transfer F = Diag(gam) - Kb^T W (the decay part kept apart) and offset
+    Mt, off = [], []
+    for ch in chunks:
+        W = ch["T"] @ ch["Kt"]
+        Z = ch["Qt"] - ch["P"] @ W
+        Mt.append(r(W.T @ ch["Kb"]))                             # M^T
+        off.append(r(Z.T @ do[ch["s"]:ch["e"]]))
+    dS = np.array(dST, dtype=np.float64, copy=True)
+    dS_out = [None] * len(chunks)
+    for i in range(len(chunks) - 1, -1, -1):
+        dS_out[i] = r(dS.copy())
+        dS = chunks[i]["gam"][:, None] * dS - Mt[i] @ dS + off[i]
+    res = {n: np.zeros(x.shape) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta))}
+    res["dh0"] = dS
+    for i, ch in enumerate(chunks):
+        s, e = ch["s"], ch["e"]
+        Sc, dSo, dO, bb = S_in[i], dS_out[i], do[s:e], beta[s:e]
+        T, X, P, D = ch["T"], ch["X"], ch["P"], ch["D"]
+        R = v[s:e] - ch["Kt"] @ Sc
+        U = T @ R
+        dU = ch["Kb"] @ dSo + P.T @ dO
+        dR = T.T @ dU
+        dP = np.tril(dO @ U.T, 0)
+        dT = np.tril(dU @ R.T, 0)
+        dA = -np.tril(X.T @ (dT * bb[None, :]) @ X.T, -1)
+        dB = bb[:, None] * dA
+        db = np.sum(dT * X, axis=0) + np.sum(dA * ch["B"], axis=1)
+        em = np.exp(ch["m"])
+        dqt = em * (dO @ Sc.T) + np.einsum("ij,jc,ijc->ic", dP, ch["kh"], D)
+        dkt = -em * (dR @ Sc.T) + np.einsum("ij,jc,ijc->ic", dB, ch["kh"], D)
+        dkh = np.einsum("ij,ic,ijc->jc", dB, ch["kt"], D) + np.einsum("ij,ic,ijc->jc", dP, ch["qt"], D)
+        dkb = U @ dSo.T
+        G, m = ch["G"], ch["m"]
+        up, dn, tail = np.exp(G - m), np.exp(m - G), np.exp(G[-1][None, :] - G)
+        dq = dqt * up
+        a = dkt * up
+        bt = dkh * dn + dkb * tail
+        dG = q[s:e] * dq + k[s:e] * (a - bt)
+        dG[-1] += np.sum(dkb * tail * k[s:e], axis=0) + ch["gam"] * np.sum(Sc * dSo, axis=1)
+        res["dq"][s:e] = dq
+        res["dk"][s:e] = a + bt
+        res["dv"][s:e] = dR
+        res["dg"][s:e] = np.cumsum(dG[::-1], axis=0)[::-1]
+        res["dbeta"][s:e] = db
+    return res

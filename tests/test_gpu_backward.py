@@ -206,6 +206,64 @@ def test_long_reverse_chain(decay):
     compare("T4096 decay=%s beta/10" % decay, d, ct)
 
 
+@pytest.mark.parametrize("chunk_sum", [-100.0, -300.0, -440.0])
+@pytest.mark.parametrize("dk,dv,gg", [(128, 128, 1), (64, 64, 1), (128, 64, 64)])
+def test_strong_decay(chunk_sum, dk, dv, gg):
+    """Every third key channel (or decay group) decays by about e^chunk_sum
+    over 64 tokens: far beyond what a chunk-start reference can carry in
+    fp32 (e^{+-G} would reach e^{300}).  Two sequences with h0, dht and a
+    ragged tail; every gradient against the oracle."""
+    d, ct = case(2, 300, 2, dk, dv, gg=gg, seed=int(-chunk_sum) + dk + gg, decay="strong:%g" % chunk_sum)
+    compare("strong %g dk%d dv%d gg%d" % (chunk_sum, dk, dv, gg), d, ct)
+
+
+def test_strong_decay_packed_documents():
+    cu = [0, 17, 17, 150, 333]
+    d, ct = case(1, 333, 3, 128, 128, cu=cu, seed=303, decay="strong:-300")
+    compare("strong -300 varlen", d, ct)
+
+
+def test_mamba_style_gate_decay():
+    """g from the gate -exp(A_log) softplus(f + dt_bias) with A_log = ln 16 (a
+    Mamba-style A of 16): per-token log-decays near -3, single tokens near
+    -50 and 64-token sums near -190.  The gate is evaluated by the prologue
+    oracle in fp64 and rounded to bf16; the backward takes it as g."""
+    import oracle.prologue as pro
+    from tests._chunked_model import chunked_backward_blockref
+    p = inputs.make_prologue(2, 400, 2, 128, 128, "bf16", seed=1616, h0=True, a_log_mean=float(np.log(16.0)))
+    d, ct = case(2, 400, 2, 128, 128, seed=1617)
+    g = pro.gate(f64(p["f"]), f64(p["A_log"]), f64(p["dt_bias"]))
+    d["g"] = torch.from_numpy(g).float().to(torch.bfloat16)
+    assert float(d["g"].float().sum(1).min()) < -800.0  # sums over 400 tokens
+    got = run_gpu(d, ct)
+    ref = run_oracle(d, ct)
+    # dg here is a sum of terms that cancel to about a tenth of their size
+    # (a token's decay reaches only a few tokens), so its relative error is
+    # larger than elsewhere.  Its bound is derived from a float64 model of the
+    # same block algebra with bf16 rounding at the GPU path's storage points:
+    # twice that model's relative L2 error on these inputs.
+    bf = lambda x: torch.from_numpy(np.asarray(x)).float().bfloat16().double().numpy()
+    model = np.zeros(ref["dg"].shape)
+    for b in range(2):
+        for h in range(2):
+            sel = lambda t: f64(t)[b, :, h]
+            model[b, :, h] = chunked_backward_blockref(*(sel(d[n]) for n in ("q", "k", "v", "g", "beta")),
+                                                       f64(d["h0"])[b, h], sel(ct["do"]), f64(ct["dht"])[b, h],
+                                                       rnd=bf)["dg"]
+    model_rel = errors(model, ref["dg"])[1]
+    print("dg of the bf16 rounding model: rel-L2 %.3e" % model_rel)
+    bound = max(2e-2, 2.0 * model_rel)
+    for n in NAMES:
+        if n == "dg":
+            ma, rel = errors(f64(got[n]), ref[n])
+            assert np.all(np.isfinite(f64(got[n])))
+            print("PARITY %-34s %-6s max-abs %.3e rel-L2 %.3e (bound %.3e)" % ("A_log ln16 gate", n, ma, rel, bound),
+                  flush=True)
+            assert rel <= bound and ma <= 2e-2 * float(np.max(np.abs(ref[n])))
+        else:
+            check_grad("A_log ln16 gate", n, got[n], ref[n])
+
+
 def test_kimi_k3_heads_full_chain():
     """At the bench's prefill shape (B=1, T=32768, H=96, dk=dv=128): every
     gradient of two heads over all 32,768 tokens, and their dh0, against the

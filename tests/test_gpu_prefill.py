@@ -203,7 +203,7 @@ def test_empty_sequence_returns_initial_state():
 
 
 # ---------------------------------------------------------------- strong decay
-@pytest.mark.parametrize("chunk_sum", [-100.0, -300.0])
+@pytest.mark.parametrize("chunk_sum", [-100.0, -300.0, -440.0])
 @pytest.mark.parametrize("dtype,dk,g_group", [("bf16", 128, 1), ("bf16", 64, 1), ("bf16", 128, 64),
                                               ("f32", 64, 1), ("f32", 128, 1)])
 def test_strong_decay(chunk_sum, dtype, dk, g_group):

@@ -23,7 +23,7 @@ import pytest
 
 import oracle.kda_oracle as orc
 from oracle.kda_backward import kda_backward
-from tests._chunked_model import chunked_backward
+from tests._chunked_model import chunked_backward, chunked_backward_blockref
 
 
 def _unit(rng, *shape):
@@ -221,6 +221,32 @@ def test_chunked_backward_model_matches_oracle(C):
     ref = kda_backward(q, k, v, g, beta, do, h0=h0, dht=dht)
     got = chunked_backward(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0], beta[0, :, 0], h0[0, 0], do[0, :, 0],
                            dht[0, 0], C)
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        r = ref[name][0, :, 0]
+        assert np.max(np.abs(got[name] - r)) <= 1e-10 * max(1.0, np.max(np.abs(r))), name
+    assert np.max(np.abs(got["dh0"] - ref["dh0"][0, 0])) <= 1e-10 * max(1.0, np.max(np.abs(ref["dh0"])))
+
+
+@pytest.mark.parametrize("C,B", [(64, 16), (16, 4), (20, 16)])
+def test_block_referenced_backward_model_matches_oracle(C, B):
+    """The block-referenced algebra (factors of at most one block's decay;
+    pairs of blocks through e^{m_I - m_J}), in float64, against the oracle's
+    reverse mode on decays of about -1,000 per 64 tokens on some channels:
+    there the chunk-start factors e^{+-G} exceed float64's range, the block
+    ones (at most e^{125} for B = 16) do not."""
+    rng = np.random.default_rng(300 + C + B)
+    T, dk, dv = 90, 6, 5
+    q, k, v, g, beta = _case(rng, 1, T, 1, dk, dv)
+    g[..., ::3] = -(1000.0 / 64.0) * (1.0 + 0.2 * np.tanh(rng.standard_normal(g[..., ::3].shape)))
+    h0 = rng.standard_normal((1, 1, dk, dv))
+    do = rng.standard_normal((1, T, 1, dv))
+    dht = rng.standard_normal((1, 1, dk, dv))
+    ref = kda_backward(q, k, v, g, beta, do, h0=h0, dht=dht)
+    sl = lambda x: x[0, :, 0]
+    with np.errstate(over="ignore", invalid="ignore"):
+        plain = chunked_backward(sl(q), sl(k), sl(v), sl(g), sl(beta), h0[0, 0], sl(do), dht[0, 0], 64)
+    assert not all(np.all(np.isfinite(plain[n])) for n in ("dq", "dk", "dg")), "chunk-start factors stayed finite"
+    got = chunked_backward_blockref(sl(q), sl(k), sl(v), sl(g), sl(beta), h0[0, 0], sl(do), dht[0, 0], C, B)
     for name in ("dq", "dk", "dv", "dg", "dbeta"):
         r = ref[name][0, :, 0]
         assert np.max(np.abs(got[name] - r)) <= 1e-10 * max(1.0, np.max(np.abs(r))), name
