@@ -39,16 +39,16 @@ DECODE_SRCS = [os.path.join(CSRC, f) for f in ("kda_common.h", "kda_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 
 
-def alg_prefill(B, T, H, dk, dv, g_group, elem=2, final_state=True, C=64):
+def alg_prefill(B, T, H, dk, dv, g_group, elem=2, final_state=True, C=64, N=None):
     """Algorithmic bytes and flops of one prefill call.
     Bytes per head-token: q, k, v, g in, o out (elem bytes each), beta in;
-    plus the final fp32 state once per (sequence, head).
+    plus the final fp32 state once per (sequence, head) (N sequences, default B).
     Flops per head-token: 6 dk dv (state pass: Kt S, Qt S, Kb^T U) + (C-1) dk
     (k-k block) + (C+1) dk (q-k block) + 2 (C+1) dv (P U, Tm R) + C^2/3
     (triangular solve), masked triangles counted at half."""
     ht = B * T * H
     per_tok_bytes = elem * (2 * dk + dv + dk // g_group + 1 + dv)
-    nbytes = ht * per_tok_bytes + (B * H * dk * dv * 4 if final_state else 0)
+    nbytes = ht * per_tok_bytes + ((B if N is None else N) * H * dk * dv * 4 if final_state else 0)
     flops = ht * (6 * dk * dv + (C - 1) * dk + (C + 1) * dk + 2 * (C + 1) * dv + C * C / 3.0)
     return nbytes, flops
 
@@ -176,12 +176,94 @@ def cpu_baseline(pre, dec, budget_s=12.0):
     }
 
 
+CONFIGS = (("0", "tiny_f32"), ("1", "minikimi_bf16"), ("2", "mini1h_g64_bf16"), ("3", "varlen_bf16"),
+           ("4a", "k3_prefill_bf16"))
+
+
+def run_configs(warmup, steps):
+    """Per-configuration figures (not the bench line): every prefill workload
+    timed on its own (median of `steps` calls with final states, after
+    `warmup`), the decode workload's 64 consecutive steps, and the CPU oracle
+    on a bounded sample of each.  One JSON line per configuration."""
+    import numpy as np
+    import torch
+    import oracle.kda_oracle as orc
+    from gated_delta_rule_04_amd import inputs, kda
+
+    f64 = lambda t: t.double().numpy()
+    for cfg, name in CONFIGS:
+        d = inputs.workload_prefill(name)
+        P = {n: d[n].cuda() for n in ("q", "k", "v", "g", "beta")}
+        cu = None if d.get("cu_seqlens") is None else d["cu_seqlens"].cuda()
+        B, T, H, dk = d["q"].shape
+        dv, gg = d["v"].shape[-1], d["g_group"]
+        N = B if cu is None else cu.numel() - 1
+        call = lambda: kda.chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], output_final_state=True,
+                                     cu_seqlens=cu)
+        for _ in range(warmup):
+            call()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in ev:
+            e[0].record()
+            call()
+            e[1].record()
+        torch.cuda.synchronize()
+        ms = pct([e[0].elapsed_time(e[1]) for e in ev], 50)
+        elem = d["q"].element_size()
+        nbytes, flops = alg_prefill(B, T, H, dk, dv, gg, elem=elem, N=N)
+        # the oracle on a bounded sample: head 0 of the first sequence, about 2 s
+        q, k, v, g, beta = (f64(d[n][0, :, :1]) for n in ("q", "k", "v", "g", "beta"))
+        S = np.zeros((1, dk, dv))
+        t0, ntok = time.perf_counter(), 0
+        while ntok < q.shape[0] and time.perf_counter() - t0 < 2.0:
+            sl = slice(ntok, ntok + 128)
+            _, S = orc.kda_sequence(q[sl], k[sl], v[sl], orc.expand_decay(g[sl], dk, gg), beta[sl], S)
+            ntok += min(128, q.shape[0] - ntok)
+        orc_headtok_s = ntok / (time.perf_counter() - t0)
+        print(json.dumps({"config": cfg, "workload": name, "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+                          "g_group": gg, "num_seqs": N, "dtype": str(d["q"].dtype).replace("torch.", ""),
+                          "ms_median": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                          "alg_bytes": nbytes, "alg_gbs": nbytes / (ms * 1e-3) / 1e9,
+                          "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "alg_tflops": flops / (ms * 1e-3) / 1e12,
+                          "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                          "oracle_tokens_per_s": orc_headtok_s / H, "oracle_sample": "%d tokens of one head" % ntok}),
+              flush=True)
+        del P, cu, d
+    dec = inputs.workload_decode("k3_decode_bf16")
+    state = dec["state"].cuda()
+    Nd, H, dk, dv = state.shape
+    D = [{n: st[n].cuda() for n in st} for st in dec["steps"]]
+    od = torch.empty((Nd, H, dv), dtype=torch.bfloat16, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(D) + 1)]
+    ev[0].record()
+    for i, s in enumerate(D):
+        kda.recurrent_step(s["q"], s["k"], s["v"], s["g"], s["beta"], state, out=od)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = pct([ev[i].elapsed_time(ev[i + 1]) for i in range(len(D))], 50)
+    nbytes = alg_decode(Nd, H, dk, dv, 1)
+    Sd = f64(dec["state"][:4])
+    t0, nstep = time.perf_counter(), 0
+    while time.perf_counter() - t0 < 2.0:
+        Sd, _ = orc.kda_decode_step(Sd, *(f64(dec["steps"][0][n][:4]) for n in ("q", "k", "v", "g", "beta")))
+        nstep += 1
+    print(json.dumps({"config": "4b", "workload": "k3_decode_bf16", "N": Nd, "H": H, "dk": dk, "dv": dv,
+                      "steps": len(D), "ms_median_per_step": ms, "tokens_per_s": Nd / (ms * 1e-3),
+                      "alg_bytes_per_step": nbytes, "alg_gbs": nbytes / (ms * 1e-3) / 1e9,
+                      "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "oracle_tokens_per_s": nstep * 4 / (time.perf_counter() - t0),
+                      "oracle_sample": "4 sequences x %d heads, %d steps" % (H, nstep)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)  # the clocks settle within the first ~8 prefill calls
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs", action="store_true",
+                    help="only print per-configuration figures (one JSON line per configuration)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run one plain device copy of this many MiB (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -189,6 +271,10 @@ def main():
         print("bench.py measures one GPU: the KDA hot path shards by sequences and heads with no exchange, "
               "so only --gpus 1 is supported", file=sys.stderr)
         sys.exit(2)
+
+    if args.configs:
+        run_configs(args.warmup, args.steps)
+        return
 
     import torch
     from gated_delta_rule_04_amd import inputs, kda

@@ -228,8 +228,8 @@ struct FrontScratch {
 
 template <class Cfg, bool LOCAL>
 __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int h, int c, FrontTiles<Cfg>& ft,
-                                            FrontScratch<Cfg>& fs, float (&G2)[Cfg::TB], float& mref, float& glref,
-                                            const f32x4& ident) {
+                                            FrontScratch<Cfg>& fs, float (&G2)[Cfg::TB], float& offref, float& mref,
+                                            float& glref, const f32x4& ident) {
   constexpr int DK = Cfg::DK, C = Cfg::C, GG = Cfg::GG, KHP = Cfg::KHP, CTP = Cfg::CTP, AP = Cfg::AP;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, TB = Cfg::TB, SK = DK / 32;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
@@ -281,6 +281,7 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
     // e^{+-(G - m)} of its rows stay within e^{|block sum| / 2}
     const float m = off + 0.5f * ft.gsum[tb][ch];
     mref = m;
+    offref = off;
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       G2[j] += off;
@@ -452,8 +453,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
       op[j] = bload<u32x4>(bo, r * rsv + c8 * 2);
     }
   }
-  float G2[Cfg::TB], mref, glref;
-  chunk_front<Cfg, false>(A, sq, h, c, sm.ft, sm.u.fs, G2, mref, glref, ident);
+  float G2[Cfg::TB], offref, mref, glref;
+  chunk_front<Cfg, false>(A, sq, h, c, sm.ft, sm.u.fs, G2, offref, mref, glref, ident);
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int p = tid + NT * j, r = p / (DV / 8), c8 = 8 * (p % (DV / 8));
@@ -739,9 +740,12 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   load_slice(0);
   load_v(0);
 
-  float G2[TB], mref, glref;
+  float offref, mref, glref;
   FrontTiles<Cfg>& ft = sm.m.ft;
-  chunk_front<Cfg, true>(A, sq, h, c, ft, sm.m.u.fs, G2, mref, glref, ident);
+  {
+    float G2f[TB];  // recomputed in the final stage (not kept live across the slices)
+    chunk_front<Cfg, true>(A, sq, h, c, ft, sm.m.u.fs, G2f, offref, mref, glref, ident);
+  }
   auto& sl = sm.m.u.sl;
   auto& cc = sm.m.u.cc;
 
@@ -751,7 +755,22 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   f32x4 dQtT[4], SdR[4], dKbT[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) dQtT[tt] = SdR[tt] = dKbT[tt] = zero4();
-  float rs = 0.f;  // rowsum(S * dSt): channel 16w + l16, columns 8kg .. 8kg + 7 of each slice
+  float rs = 0.f;  // rowsum(S * dS_out): channel 16w + l16, columns 8kg .. 8kg + 7 of each slice
+  // the chunk-start Kt = kt e^{m} and chunk-end Kb = kh e^{G_last - m} row
+  // fragments of this wave's R / dU tiles, the same for every value slice
+  FV ktS[NJ][SK], kbS[NJ][SK];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int tt = (w + NW * jj) >> 1;
+#pragma unroll
+    for (int s = 0; s < SK; ++s) {
+      f32x4 lo, hi;
+      row_vals(ft.em[tt], s, kg, lo, hi);
+      ktS[jj][s] = scale8(ld_row<KHP>(ft.kt, 16 * tt + l16, s, kg), lo, hi);
+      row_vals(ft.eb[tt], s, kg, lo, hi);
+      kbS[jj][s] = scale8(ld_row<KHP>(ft.kh, 16 * tt + l16, s, kg), lo, hi);
+    }
+  }
 
   for (int v0 = 0; v0 < DV; v0 += VSL) {
     __syncthreads();  // the front, or the previous slice, is done with the slice tiles
@@ -778,20 +797,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
       const int job = w + NW * jj, tt = job >> 1, ct = job & 1;
       f32x4 acc = zero4(), du = zero4();
 #pragma unroll
-      for (int s = 0; s < SK; ++s) {
-        f32x4 lo, hi;
-        row_vals(ft.em[tt], s, kg, lo, hi);
-        acc = F::mma(scale8(ld_row<KHP>(ft.kt, 16 * tt + l16, s, kg), lo, hi), F::ld_tr<SP>(sl.S, 16 * ct, s, l16, kg),
-                     acc);
-      }
+      for (int s = 0; s < SK; ++s) acc = F::mma(ktS[jj][s], F::ld_tr<SP>(sl.S, 16 * ct, s, l16, kg), acc);
       st_acc<SP>(sl.R, 16 * tt, 16 * ct, Reg16<bf16>::rows(vr[jj], ident, -acc), ident, l16, kg);
 #pragma unroll
-      for (int s = 0; s < SK; ++s) {
-        f32x4 lo, hi;
-        row_vals(ft.eb[tt], s, kg, lo, hi);
-        du = F::mma(scale8(ld_row<KHP>(ft.kh, 16 * tt + l16, s, kg), lo, hi), F::ld_tr<SP>(sl.dS, 16 * ct, s, l16, kg),
-                    du);
-      }
+      for (int s = 0; s < SK; ++s) du = F::mma(kbS[jj][s], F::ld_tr<SP>(sl.dS, 16 * ct, s, l16, kg), du);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         if (32 * s + 31 >= 16 * tt)
@@ -854,14 +863,16 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   // fetched now so that the loads overlap the C x C stage
   const int ch = tid % DK, tb = tid / DK;
   const int rsk = H * DK * 2, rsg = H * (DK / GG) * 2, rsb = H * 2;
-  bf16 qf[TB], kf[TB];
+  bf16 qf[TB], kf[TB], gf[TB];
   {
     const rsrc_t bq = make_rsrc(A.q + row0 * DK, (nv - 1) * rsk + DK * 2);
     const rsrc_t bk = make_rsrc(A.k + row0 * DK, (nv - 1) * rsk + DK * 2);
+    const rsrc_t bg = make_rsrc(A.g + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * 2);
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       qf[j] = bload<bf16>(bq, (tb * TB + j) * rsk + ch * 2);
       kf[j] = bload<bf16>(bk, (tb * TB + j) * rsk + ch * 2);
+      gf[j] = bload<bf16>(bg, (tb * TB + j) * rsg + (ch / GG) * 2);
     }
   }
   rs = rows4_sum(rs);
@@ -954,8 +965,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   // masked tiles vanish), applied to the transposed operand of lane channel
   // 16w + l16 whose elements 0..3 and 4..7 lie in blocks 2s and 2s + 1
   const int cw = 16 * w + l16;
-  const float* mw0 = &ft.gsum[0][cw];
-  auto shift = [&](int I, int J) { return I >= J ? fast_exp2(mw0[I * DK] - mw0[J * DK]) : 0.f; };
+  float mw[4], sh[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) mw[b] = ft.gsum[b][cw];
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int J = 0; J < 4; ++J) sh[I][J] = I > J ? fast_exp2(mw[I] - mw[J]) : (I == J ? 1.f : 0.f);
+  auto shift = [&](int I, int J) { return sh[I][J]; };
   f32x4 dKtT[4], dKhT[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
@@ -991,6 +1008,18 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   const rsrc_t bdq = make_rsrc(A.dq + row0 * DK, (nv - 1) * rsk + DK * 2);
   const rsrc_t bdk = make_rsrc(A.dk + row0 * DK, (nv - 1) * rsk + DK * 2);
   const rsrc_t bdg = make_rsrc(A.dg + row0 * (DK / GG), (nv - 1) * rsg + (DK / GG) * 2);
+  // the chunk-start cumulative decay of this thread's tokens (log2 units),
+  // formed exactly as the front formed it
+  const float ebref = fast_exp2(glref - mref);
+  float G2[TB];
+  {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      acc += to_f32(gf[j]) * kLog2e;
+      G2[j] = acc + offref;
+    }
+  }
   float dG[TB];
   float skb = 0.f;
 #pragma unroll
@@ -998,7 +1027,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     const int r = tb * TB + j;
     const float dqt = sm.fin[0][r][ch], dkt = sm.fin[1][r][ch], dkh = sm.fin[2][r][ch], dkb = sm.fin[3][r][ch];
     // back from the block reference m and from the chunk end
-    const float eu = fast_exp2(G2[j] - mref), ed = fast_exp2(mref - G2[j]), ee = fast_exp2(glref - G2[j]);
+    // e^{G_last - G} = e^{G_last - m} e^{m - G}: where the first factor
+    // underflows the product is below e^-17 of the terms it joins
+    const float eu = fast_exp2(G2[j] - mref), ed = fast_exp2(mref - G2[j]), ee = ebref * ed;
     const float q = to_f32(qf[j]), kk = to_f32(kf[j]);
     const float dq = dqt * eu, a = dkt * eu, kbe = dkb * ee, b = dkh * ed + kbe;
     dG[j] = q * dq + kk * (a - b);
