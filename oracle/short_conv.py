@@ -14,6 +14,14 @@ the token axis, per channel c with weights w[c, 0..W-1]:
 
 with the W-1 positions before a sequence's first token taken from an initial
 conv state (the inputs that preceded it) or zero; no bias, no activation.
+
+Backward: the convolution is linear in x (and in the initial state) and in
+the weights, so with L = <dy, y> + <dfinal, conv_final>:
+
+    dx[t, c]      = sum_w w[c, w] dy[t + (W-1) - w, c]   (positions in the
+                    same sequence) + dfinal where x[t] is one of the last W-1
+    dw[c, w]      = sum_t dy[t, c] * ext[t + w, c]     (ext: history + x)
+    dconv0[j, c]  = the same sums as dx for the W-1 history positions.
 """
 
 import numpy as np
@@ -65,3 +73,35 @@ def short_conv_step(x, weight, conv_state):
     win = np.concatenate([st, x[:, None, :]], axis=1)  # [N, W, C]
     y = np.einsum("cw,nwc->nc", w, win)
     return y, win[:, 1:]
+
+
+def short_conv_backward(x, weight, dy, conv0=None, dfinal=None, cu_seqlens=None):
+    """Gradients of L = <dy, y> + <dfinal, conv_final> for short_conv_forward:
+    returns (dx [B, T, C], dweight [C, W], dconv0 [N, W-1, C]).  dfinal
+    [N, W-1, C] or None (zero)."""
+    x = _f64(x)
+    w = _f64(weight)
+    dy = _f64(dy)
+    B, T, C = x.shape
+    W = w.shape[1]
+    if cu_seqlens is not None:
+        cu = [int(c) for c in np.asarray(cu_seqlens)]
+        seqs = [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+    else:
+        seqs = [(b, 0, T) for b in range(B)]
+    dx = np.zeros((B, T, C))
+    dw = np.zeros((C, W))
+    dc0 = np.zeros((len(seqs), W - 1, C))
+    for n, (b, s, e) in enumerate(seqs):
+        L = e - s
+        hist = _f64(conv0)[n] if conv0 is not None else np.zeros((W - 1, C))
+        ext = np.concatenate([hist, x[b, s:e]], axis=0)       # ext[i] feeds y[t] for i = t + j
+        dext = np.zeros_like(ext)
+        for j in range(W):
+            dext[j:j + L] += w[:, j][None, :] * dy[b, s:e]
+            dw[:, j] += np.sum(ext[j:j + L] * dy[b, s:e], axis=0)
+        if dfinal is not None and W > 1:
+            dext[ext.shape[0] - (W - 1):] += _f64(dfinal)[n]
+        dx[b, s:e] = dext[W - 1:]
+        dc0[n] = dext[:W - 1]
+    return dx, dw, dc0
