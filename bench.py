@@ -592,7 +592,26 @@ def main():
         "alg_bytes_per_launch": conv_bytes,
         "hbm_frac_alg": conv_bytes / (conv_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
-    del xc, yc
+    # its backward (dx, dweight), with a seeded cotangent
+    dyc = torch.randn((B, T, Cc), generator=gc).to(torch.bfloat16).to(dev)
+    cws = torch.empty(kda.lib().kda_short_conv_bwd_workspace_bytes(B, T, Cc, Wc), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        kda.short_conv_bwd(xc, wc, dyc, workspace=cws)
+    cbev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        cbev[i][0].record()
+        kda.short_conv_bwd(xc, wc, dyc, workspace=cws)
+        cbev[i][1].record()
+    torch.cuda.synchronize()
+    cb_avg = mean([e[0].elapsed_time(e[1]) for e in cbev])
+    cb_bytes = 2 * (3 * B * T * Cc) + 2 * Cc * Wc + 4 * Cc * Wc
+    line["short_conv_bf16"]["backward"] = {
+        "kernels": "short_conv_bwd_kernel, short_conv_bwd_weight_kernel",
+        "ms": cb_avg,
+        "alg_bytes_per_call": cb_bytes,
+        "hbm_frac_alg": cb_bytes / (cb_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    del xc, yc, dyc, cws
     # Prefill with the fused gate/normalisation prologue (outside the timed
     # step): the same tensors taken as raw projections (q, k rows, gate logits
     # f = g, write logits b = beta), A_log = 0 and dt_bias = -2 per channel.
@@ -621,7 +640,32 @@ def main():
         "hbm_frac_alg": pro_bytes / (pro_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "separate_pass_bytes_avoided": 2 * 2 * B * T * H * (2 * dk + dk // g_group + 1),
     }
-    del A_log, dt_bias
+    # the backward through the prologue (prepare, chunked backward, chain rule)
+    gp = torch.Generator().manual_seed(29)
+    dop = torch.randn((B, T, H, dv), generator=gp).to(torch.bfloat16).to(dev)
+    dhtp = torch.randn((B, H, dk, dv), generator=gp).to(dev)
+    pws = torch.empty(kda.lib().kda_chunk_bwd_prologue_workspace_bytes(B, T, H, dk, dv, B, 0, g_group, kda.KDA_BF16),
+                      dtype=torch.uint8, device=dev)
+    for _ in range(min(args.warmup, 3)):
+        kda.chunk_bwd_prologue(P["q"], P["k"], P["v"], P["g"], P["beta"], A_log, dt_bias, dop, dht=dhtp,
+                               workspace=pws)
+    pbev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(min(args.steps, 5))]
+    for e in pbev:
+        e[0].record()
+        kda.chunk_bwd_prologue(P["q"], P["k"], P["v"], P["g"], P["beta"], A_log, dt_bias, dop, dht=dhtp,
+                               workspace=pws)
+        e[1].record()
+    torch.cuda.synchronize()
+    pb_avg = mean([e[0].elapsed_time(e[1]) for e in pbev])
+    line["prefill_prologue_bf16"]["backward"] = {
+        "entry_point": "kda_chunk_bwd_prologue",
+        "ms": pb_avg,
+        "tokens_per_s": B * T / (pb_avg * 1e-3),
+        "alg_bytes_per_call": alg_backward(B, T, H, dk, dv, g_group) + 2 * 2 * H * (dk // g_group) * 4,
+    }
+    line["prefill_prologue_bf16"]["backward"]["hbm_frac_alg"] = (
+        line["prefill_prologue_bf16"]["backward"]["alg_bytes_per_call"] / (pb_avg * 1e-3) / 1e9 / PEAK_HBM_GBS)
+    del A_log, dt_bias, dop, dhtp, pws
     # Backward pass of the prefill (outside the timed step): the same inputs,
     # seeded cotangents of o and of the final state.
     gb = torch.Generator().manual_seed(23)

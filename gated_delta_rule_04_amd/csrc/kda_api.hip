@@ -298,6 +298,43 @@ kda_status kda_short_conv_fwd(const void* x, const void* weight, const void* con
   return KDA_OK;
 }
 
+size_t kda_short_conv_bwd_workspace_bytes(int B, int T, int C, int W) {
+  if (B < 0 || T < 0 || !conv_dims_ok(C, W) || !prod_fits({B, T}, INT_MAX)) return 0;
+  const long long runs = kda::short_conv_bwd_runs((long long)B * T);
+  if (!prod_fits({runs, W, C}, LLONG_MAX / 8)) return 0;
+  return ((size_t)runs * W * C * 4 + 255) / 256 * 256;
+}
+
+kda_status kda_short_conv_bwd(const void* x, const void* weight, const void* conv0, const void* dy,
+                              const void* dconv_final, void* dx, float* dweight, void* dconv0,
+                              const int* cu_seqlens, int num_seqs, int B, int T, int C, int W, kda_dtype dt,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 0 || T < 0 || num_seqs < 0 || C <= 0) return KDA_ERR_SHAPE;
+  if (!conv_dims_ok(C, W)) return KDA_ERR_UNSUPPORTED;
+  if (cu_seqlens) {
+    if (B != 1) return KDA_ERR_SHAPE;
+  } else if (num_seqs != B) {
+    return KDA_ERR_SHAPE;
+  }
+  if (!prod_fits({B, T}, INT_MAX) || !prod_fits({B, T, C}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  if (!prod_fits({num_seqs, W, C}, LLONG_MAX / 8)) return KDA_ERR_SHAPE;
+  const size_t need = kda_short_conv_bwd_workspace_bytes(B, T, C, W);
+  const bool has_tokens = (long long)B * T > 0;
+  if (!weight || !dweight) return KDA_ERR_NULL;
+  if (has_tokens && (!x || !dy || !dx)) return KDA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(conv0) || !aligned16(dconv_final) ||
+      !aligned16(dconv0))
+    return KDA_ERR_UNSUPPORTED;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_WORKSPACE;
+  if (kda::launch_short_conv_bwd(dt == KDA_BF16, x, weight, conv0, dy, dconv_final, dx, dweight, dconv0,
+                                 static_cast<float*>(workspace), cu_seqlens, num_seqs, B, T, C, W,
+                                 static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
 kda_status kda_short_conv_step(const void* x, const void* weight, void* conv_state, void* y, int N, int C, int W,
                                kda_dtype dt, void* stream) {
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
@@ -476,6 +513,117 @@ kda_status kda_chunk_bwd_saved(const void* q, const void* k, const void* v, cons
                                size_t workspace_bytes, void* stream) {
   return chunk_bwd_impl(q, k, v, g, beta, h0, nullptr, nullptr, dout, dht, dq, dk, dv, dg, dbeta, dh0, cu_seqlens,
                         num_seqs, B, T, H, Dk, Dv, g_group, dt, workspace, workspace_bytes, stream, BwdMode::kSaved);
+}
+
+}  // extern "C"
+
+namespace {
+// Workspace of the prologue backward: the chunked backward's own workspace,
+// then the prepared inputs, their gradients and the parameter partial sums.
+struct ProBwdLayout {
+  size_t q, k, g, beta, dq, dk, dg, dbeta, pa, pb, total;
+};
+bool pro_bwd_layout(int B, int T, int H, int Dk, int Dv, int g_group, int N, bool varlen, ProBwdLayout& P) {
+  BwdLayout L;
+  long long slots;
+  if (!bwd_layout(B, T, H, Dk, Dv, N, varlen, L, slots)) return false;
+  if (g_group <= 0 || !prod_fits({B, T, H, Dk}, LLONG_MAX / 16)) return false;
+  const size_t rows = (size_t)B * T * H, ng = (size_t)(Dk / g_group);
+  const size_t nblk = (size_t)kda::prologue_bwd_blocks((long long)B * T);
+  size_t o = align256(L.total);
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  P.q = take(rows * Dk * 2);
+  P.k = take(rows * Dk * 2);
+  P.g = take(rows * ng * 2);
+  P.beta = take(rows * 2);
+  P.dq = take(rows * Dk * 2);
+  P.dk = take(rows * Dk * 2);
+  P.dg = take(rows * ng * 2);
+  P.dbeta = take(rows * 2);
+  P.pa = take(nblk * H * ng * 4);
+  P.pb = take(nblk * H * ng * 4);
+  P.total = o;
+  return true;
+}
+}  // namespace
+
+extern "C" {
+
+size_t kda_chunk_bwd_prologue_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs, int varlen,
+                                              int g_group, kda_dtype dt) {
+  (void)dt;
+  if (!head_dims_ok(Dk, Dv, g_group) || H <= 0) return 0;
+  ProBwdLayout P;
+  if (!pro_bwd_layout(B, T, H, Dk, Dv, g_group, num_seqs, varlen != 0, P)) return 0;
+  return P.total;
+}
+
+kda_status kda_chunk_bwd_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
+                                  const void* b_raw, const float* A_log, const float* dt_bias, const float* h0,
+                                  const void* dout, const float* dht, void* dq_raw, void* dk_raw, void* dv, void* df,
+                                  void* db_raw, float* dA_log, float* ddt_bias, float* dh0, const int* cu_seqlens,
+                                  int num_seqs, int B, int T, int H, int Dk, int Dv, int g_group, kda_dtype dt,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 0 || T < 0 || H <= 0 || H > kMaxChunkedHeads || num_seqs < 0) return KDA_ERR_SHAPE;
+  if (!head_dims_ok(Dk, Dv, g_group)) return KDA_ERR_UNSUPPORTED;
+  if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen) {
+    if (B != 1) return KDA_ERR_SHAPE;
+  } else if (num_seqs != B) {
+    return KDA_ERR_SHAPE;
+  }
+  ProBwdLayout P;
+  if (!pro_bwd_layout(B, T, H, Dk, Dv, g_group, num_seqs, varlen, P)) return KDA_ERR_SHAPE;
+  if (!A_log || !dt_bias || !dA_log || !ddt_bias) return KDA_ERR_NULL;
+  const bool has_tokens = (long long)B * T > 0;
+  if (has_tokens && (!q_raw || !k_raw || !v || !f || !b_raw || !dout || !dq_raw || !dk_raw || !dv || !df || !db_raw))
+    return KDA_ERR_NULL;
+  if (!aligned16(q_raw) || !aligned16(k_raw) || !aligned16(dq_raw) || !aligned16(dk_raw)) return KDA_ERR_UNSUPPORTED;
+  if (g_group == 1 && (!aligned16(f) || !aligned16(df))) return KDA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < P.total) return KDA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  kda::PrologueBwdArgs a;
+  a.q_raw = static_cast<const kda::bf16*>(q_raw);
+  a.k_raw = static_cast<const kda::bf16*>(k_raw);
+  a.f = static_cast<const kda::bf16*>(f);
+  a.b_raw = static_cast<const kda::bf16*>(b_raw);
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.q = reinterpret_cast<kda::bf16*>(ws + P.q);
+  a.k = reinterpret_cast<kda::bf16*>(ws + P.k);
+  a.g = reinterpret_cast<kda::bf16*>(ws + P.g);
+  a.beta = reinterpret_cast<kda::bf16*>(ws + P.beta);
+  a.dq = reinterpret_cast<const kda::bf16*>(ws + P.dq);
+  a.dk = reinterpret_cast<const kda::bf16*>(ws + P.dk);
+  a.dg = reinterpret_cast<const kda::bf16*>(ws + P.dg);
+  a.dbeta = reinterpret_cast<const kda::bf16*>(ws + P.dbeta);
+  a.dq_raw = static_cast<kda::bf16*>(dq_raw);
+  a.dk_raw = static_cast<kda::bf16*>(dk_raw);
+  a.df = static_cast<kda::bf16*>(df);
+  a.db_raw = static_cast<kda::bf16*>(db_raw);
+  a.part_a = reinterpret_cast<float*>(ws + P.pa);
+  a.part_b = reinterpret_cast<float*>(ws + P.pb);
+  a.dA_log = dA_log;
+  a.ddt_bias = ddt_bias;
+  a.ntok = (long long)B * T;
+  a.H = H;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // 1. the prepared inputs; 2. the chunked backward on them; 3. the prologue's chain rule
+  if (kda::launch_prologue_prepare(Dk, g_group, a, s) != hipSuccess) return KDA_ERR_HIP;
+  const kda_status st = chunk_bwd_impl(a.q, a.k, v, a.g, a.beta, h0, nullptr, nullptr, dout, dht, ws + P.dq,
+                                       ws + P.dk, dv, ws + P.dg, ws + P.dbeta, dh0, cu_seqlens, num_seqs, B, T, H, Dk,
+                                       Dv, g_group, dt, workspace, P.q, stream, BwdMode::kRecompute);
+  if (st != KDA_OK) return st;
+  if (kda::launch_prologue_grad(Dk, g_group, a, s) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
 }
 
 }  // extern "C"

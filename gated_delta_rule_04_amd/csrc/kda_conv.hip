@@ -204,6 +204,129 @@ __global__ __launch_bounds__(256) void short_conv_step_kernel(const T* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Backward.  With L = <dy, y> + <dfinal, conv_final>, per channel, for a
+// token t of a sequence [s, e):
+//   dx[t]  = sum_{u=0}^{W-1} weight[W-1-u] dy[t+u]  (terms with t+u >= e absent)
+//            + dfinal[t - (e - (W-1))]              (for t >= e - (W-1))
+//   dw[j] += dy[t] x[t - (W-1) + j]                  (history / zeros before s)
+//   dconv0[row] for the history position p = s - (W-1) + row: the dx sum at p.
+// A thread owns 8 channels and a run of 256 tokens, with a window of the
+// next W dy rows in registers (the forward's window, mirrored) and the last
+// W-1 x rows for dw; its dw sums go to a per-run partial that a second
+// kernel adds in run order (bitwise deterministic).
+// ---------------------------------------------------------------------------
+template <typename T, int W>
+__global__ __launch_bounds__(256) void short_conv_bwd_kernel(const T* __restrict__ x, const T* __restrict__ weight,
+                                                             const T* __restrict__ conv0, const T* __restrict__ dy,
+                                                             const T* __restrict__ dfinal, T* __restrict__ dx,
+                                                             float* __restrict__ part, const int* __restrict__ cu,
+                                                             int num_seqs, int B, int T_, int C) {
+  const int CG = C / 8;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long ntok = (long long)B * T_;
+  const int cg = (int)(gid % CG);
+  const long long run = gid / CG;
+  const long long t0l = run * kConvRun;
+  if (t0l >= ntok) return;
+  const int t0 = (int)t0l, t1 = (int)min(t0l + kConvRun, ntok);
+  const int ch = 8 * cg;
+  const f32x8 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x8 wg[W], dw[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    dw[w] = zero;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) wg[w][c] = to_f32(weight[(size_t)(ch + c) * W + w]);
+  }
+  int n = seq_of(cu, num_seqs, T_, t0), s, e;
+  seq_range(cu, n, B, T_, s, e);
+  f32x8 dwin[W], xwin[W];  // dwin[u] = dy[t + u]; xwin[j] = x[t - (W-1) + j]
+  auto seed = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < W; ++u) dwin[u] = t + u < e ? load8(dy + (size_t)(t + u) * C + ch) : zero;
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+      const int p = t - (W - 1) + j;
+      xwin[j] = p >= s ? load8(x + (size_t)p * C + ch) : history<T, W>(conv0, n, C, ch, p - s + W - 1);
+    }
+  };
+  seed(t0);
+  for (int t = t0; t < t1; ++t) {
+    if (t >= e && n + 1 < num_seqs) {  // the next non-empty sequence starts here
+      do {
+        ++n;
+        seq_range(cu, n, B, T_, s, e);
+      } while (t >= e && n + 1 < num_seqs);
+      seed(t);
+    }
+    xwin[W - 1] = load8(x + (size_t)t * C + ch);
+    f32x8 acc = wg[W - 1] * dwin[0];
+#pragma unroll
+    for (int u = 1; u < W; ++u) acc += wg[W - 1 - u] * dwin[u];
+    if (dfinal && W > 1 && t >= e - (W - 1)) acc += load8(dfinal + ((size_t)n * (W - 1) + t - (e - (W - 1))) * C + ch);
+    store8(dx + (size_t)t * C + ch, acc);
+#pragma unroll
+    for (int j = 0; j < W; ++j) dw[j] += dwin[0] * xwin[j];
+#pragma unroll
+    for (int u = 0; u < W - 1; ++u) dwin[u] = dwin[u + 1];
+    dwin[W - 1] = t + W < e ? load8(dy + (size_t)(t + W) * C + ch) : zero;
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) xwin[j] = xwin[j + 1];
+  }
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    float* pr = part + ((size_t)run * W + j) * C + ch;
+    *reinterpret_cast<f32x4*>(pr) = __builtin_shufflevector(dw[j], dw[j], 0, 1, 2, 3);
+    *reinterpret_cast<f32x4*>(pr + 4) = __builtin_shufflevector(dw[j], dw[j], 4, 5, 6, 7);
+  }
+}
+
+// dconv0 of each sequence: the dx sums at its W-1 history positions.
+template <typename T, int W>
+__global__ __launch_bounds__(256) void short_conv_bwd_state_kernel(const T* __restrict__ weight,
+                                                                   const T* __restrict__ dy,
+                                                                   const T* __restrict__ dfinal,
+                                                                   T* __restrict__ dconv0, const int* __restrict__ cu,
+                                                                   int num_seqs, int B, int T_, int C) {
+  const int CG = C / 8;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)num_seqs * CG) return;
+  const int cg = (int)(gid % CG), n = (int)(gid / CG), ch = 8 * cg;
+  int s, e;
+  seq_range(cu, n, B, T_, s, e);
+  f32x8 wg[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) wg[w][c] = to_f32(weight[(size_t)(ch + c) * W + w]);
+#pragma unroll
+  for (int row = 0; row < W - 1; ++row) {
+    const int p = s - (W - 1) + row;
+    f32x8 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      const int t = p + u;
+      if (t >= s && t < e) acc += wg[W - 1 - u] * load8(dy + (size_t)t * C + ch);
+    }
+    // the final state holds position p when the sequence is shorter than W-1
+    if (dfinal && p >= e - (W - 1)) acc += load8(dfinal + ((size_t)n * (W - 1) + p - (e - (W - 1))) * C + ch);
+    store8(dconv0 + ((size_t)n * (W - 1) + row) * C + ch, acc);
+  }
+}
+
+// dweight [C][W] (fp32): the per-run partial sums added in run order.
+__global__ __launch_bounds__(256) void short_conv_bwd_weight_kernel(const float* __restrict__ part,
+                                                                    float* __restrict__ dweight, long long runs, int C,
+                                                                    int W) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // i = j * C + c
+  if (i >= C * W) return;
+  const int j = i / C, c = i % C;
+  float a = 0.f;
+  for (long long r = 0; r < runs; ++r) a += part[(r * W + j) * C + c];
+  dweight[(size_t)c * W + j] = a;
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
 template <typename T, int W>
@@ -234,6 +357,35 @@ static hipError_t conv_step_w(const void* x, const void* weight, void* state, vo
                      (const T*)x, (const T*)weight, (T*)state, (T*)y, N, C);
   return hipGetLastError();
 }
+
+template <typename T, int W>
+static hipError_t conv_bwd_w(const void* x, const void* weight, const void* conv0, const void* dy, const void* dfinal,
+                             void* dx, float* dweight, void* dconv0, float* part, const int* cu, int num_seqs, int B,
+                             int T_, int C, hipStream_t s) {
+  const long long ntok = (long long)B * T_;
+  const long long runs = (ntok + kConvRun - 1) / kConvRun;
+  const long long threads = runs * (C / 8);
+  if (threads > 0) {
+    hipLaunchKernelGGL((short_conv_bwd_kernel<T, W>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       (const T*)x, (const T*)weight, (const T*)conv0, (const T*)dy, (const T*)dfinal, (T*)dx, part,
+                       cu, num_seqs, B, T_, C);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(short_conv_bwd_weight_kernel, dim3((unsigned)((C * W + 255) / 256)), dim3(256), 0, s, part,
+                     dweight, runs, C, W);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (dconv0 && W > 1 && num_seqs > 0) {
+    const long long ft = (long long)num_seqs * (C / 8);
+    hipLaunchKernelGGL((short_conv_bwd_state_kernel<T, W>), dim3((unsigned)((ft + 255) / 256)), dim3(256), 0, s,
+                       (const T*)weight, (const T*)dy, (const T*)dfinal, (T*)dconv0, cu, num_seqs, B, T_, C);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+long long short_conv_bwd_runs(long long ntok) { return (ntok + kConvRun - 1) / kConvRun; }
 
 #define KDA_CONV_SWITCH(W_, CALL) \
   switch (W_) {                   \
@@ -273,6 +425,19 @@ hipError_t launch_short_conv_step(bool bf16_io, const void* x, const void* weigh
 #undef CALL
 }
 
+
+hipError_t launch_short_conv_bwd(bool bf16_io, const void* x, const void* weight, const void* conv0, const void* dy,
+                                 const void* dfinal, void* dx, float* dweight, void* dconv0, float* part,
+                                 const int* cu, int num_seqs, int B, int T, int C, int W, hipStream_t s) {
+  if (bf16_io) {
+#define CALL(w) conv_bwd_w<bf16, w>(x, weight, conv0, dy, dfinal, dx, dweight, dconv0, part, cu, num_seqs, B, T, C, s)
+    KDA_CONV_SWITCH(W, CALL)
+#undef CALL
+  }
+#define CALL(w) conv_bwd_w<float, w>(x, weight, conv0, dy, dfinal, dx, dweight, dconv0, part, cu, num_seqs, B, T, C, s)
+  KDA_CONV_SWITCH(W, CALL)
+#undef CALL
+}
 #undef KDA_CONV_SWITCH
 
 }  // namespace kda

@@ -60,6 +60,22 @@ struct BwdArgs {
 };
 
 hipError_t launch_chunk_bwd(int Dk, int Dv, int g_group, const BwdArgs& a, hipStream_t stream);
+
+// Backward of the gate and normalisation prologue (bf16 rows [ntok][H][...]).
+struct PrologueBwdArgs {
+  const bf16 *q_raw, *k_raw, *f, *b_raw;  // the prologue's inputs
+  const float *A_log, *dt_bias;          // [H][Dk / g_group]
+  bf16 *q, *k, *g, *beta;                // prepared inputs (written by the prepare kernel)
+  const bf16 *dq, *dk, *dg, *dbeta;      // their gradients (from the chunked backward)
+  bf16 *dq_raw, *dk_raw, *df, *db_raw;   // gradients of the prologue's inputs
+  float *part_a, *part_b;                // [blocks][H][Dk / g_group] partial sums
+  float *dA_log, *ddt_bias;              // [H][Dk / g_group]
+  long long ntok;                        // B * T
+  int H;
+};
+long long prologue_bwd_blocks(long long ntok);
+hipError_t launch_prologue_prepare(int Dk, int g_group, const PrologueBwdArgs& a, hipStream_t stream);
+hipError_t launch_prologue_grad(int Dk, int g_group, const PrologueBwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, float* state, void* o, int NH, hipStream_t stream);
 hipError_t launch_decode_prologue(bool bf16_io, int Dk, int Dv, int g_group, const void* q, const void* k,
@@ -74,6 +90,10 @@ hipError_t launch_decode_pool(bool bf16_io, int state_kind, int Dk, int Dv, int 
 hipError_t launch_short_conv_fwd(bool bf16_io, const void* x, const void* weight, const void* conv0, void* y,
                                  void* conv_final, const int* cu, int num_seqs, int B, int T, int C, int W,
                                  hipStream_t s);
+long long short_conv_bwd_runs(long long ntok);
+hipError_t launch_short_conv_bwd(bool bf16_io, const void* x, const void* weight, const void* conv0, const void* dy,
+                                 const void* dfinal, void* dx, float* dweight, void* dconv0, float* part,
+                                 const int* cu, int num_seqs, int B, int T, int C, int W, hipStream_t stream);
 hipError_t launch_short_conv_step(bool bf16_io, const void* x, const void* weight, void* state, void* y, int N,
                                   int C, int W, hipStream_t s);
 hipError_t launch_prefill(bool bf16_io, int Dk, int Dv, int g_group, int VS, const PrefillArgs& a,

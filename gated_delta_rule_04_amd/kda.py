@@ -28,10 +28,11 @@ _STATUS = {
     4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
 # KDA_ABI_VERSION of include/kda.h that these bindings are written for.
-ABI_VERSION = 9
+ABI_VERSION = 10
 
-EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_save", "kda_chunk_bwd_saved", "kda_recurrent_step", "kda_recurrent_step_pool", "kda_recurrent_step_pool_prologue",
-            "kda_short_conv_fwd", "kda_short_conv_step", "kda_status_str", "kda_abi_version"]
+EXPORTED = ["kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_prologue", "kda_recurrent_step_prologue", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_save", "kda_chunk_bwd_saved", "kda_chunk_bwd_prologue_workspace_bytes", "kda_chunk_bwd_prologue", "kda_recurrent_step", "kda_recurrent_step_pool", "kda_recurrent_step_pool_prologue",
+            "kda_short_conv_fwd", "kda_short_conv_bwd_workspace_bytes", "kda_short_conv_bwd", "kda_short_conv_step",
+            "kda_status_str", "kda_abi_version"]
 
 _lib = None
 
@@ -83,6 +84,14 @@ def lib():
     L.kda_recurrent_step_pool_prologue.argtypes = [vp] * 9 + [i, vp, vp, i, i, i, i, i, i, i, vp]
     L.kda_short_conv_fwd.restype = i
     L.kda_short_conv_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    L.kda_chunk_bwd_prologue_workspace_bytes.restype = sz
+    L.kda_chunk_bwd_prologue_workspace_bytes.argtypes = [i] * 9
+    L.kda_chunk_bwd_prologue.restype = i
+    L.kda_chunk_bwd_prologue.argtypes = [vp] * 19 + [i] * 8 + [vp, sz, vp]
+    L.kda_short_conv_bwd_workspace_bytes.restype = sz
+    L.kda_short_conv_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    L.kda_short_conv_bwd.restype = i
+    L.kda_short_conv_bwd.argtypes = [vp] * 9 + [i] * 6 + [vp, sz, vp]
     L.kda_short_conv_step.restype = i
     L.kda_short_conv_step.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     _lib = L
@@ -372,6 +381,46 @@ def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=Non
     return out
 
 
+def chunk_bwd_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, do, initial_state=None, dht=None, cu_seqlens=None,
+                       workspace=None):
+    """Gradients of <do, o> + <dht, ht> for chunk_fwd_prologue (bf16).
+    Returns a dict with dq_raw, dk_raw, dv, df, db_raw (bf16, shaped like
+    the inputs), dA_log, ddt_bias (float32 [H, Dk/g_group]) and dh0 (float32
+    [N, H, Dk, Dv])."""
+    B, T, H, Dk, Dv, g_group = _prefill_shapes(q_raw, k_raw, v, f, b_raw, g_name="f")
+    dt = _dt(q_raw)
+    for t in (k_raw, v, f, b_raw, do):
+        if t.dtype != q_raw.dtype:
+            raise TypeError("q_raw, k_raw, v, f, b_raw, do must share one dtype")
+    _gate_params(A_log, dt_bias, H, f.shape[-1])
+    for t in (initial_state, dht):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("initial_state and dht must be float32")
+    N = _num_seqs(B, cu_seqlens)
+    _expect(do, (B, T, H, Dv), "do")
+    _expect(initial_state, (N, H, Dk, Dv), "initial_state")
+    _expect(dht, (N, H, Dk, Dv), "dht")
+    _check_dev(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, do, initial_state, dht, cu_seqlens)
+    out = {"dq_raw": torch.empty_like(q_raw), "dk_raw": torch.empty_like(k_raw), "dv": torch.empty_like(v),
+           "df": torch.empty_like(f), "db_raw": torch.empty_like(b_raw), "dA_log": torch.empty_like(A_log),
+           "ddt_bias": torch.empty_like(dt_bias),
+           "dh0": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q_raw.device)}
+    need = int(lib().kda_chunk_bwd_prologue_workspace_bytes(B, T, H, Dk, Dv, N, int(cu_seqlens is not None), g_group,
+                                                            dt))
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q_raw.device)
+    st = lib().kda_chunk_bwd_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(f), _ptr(b_raw), _ptr(A_log),
+                                      _ptr(dt_bias), _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(out["dq_raw"]),
+                                      _ptr(out["dk_raw"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["db_raw"]),
+                                      _ptr(out["dA_log"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(cu_seqlens),
+                                      N, B, T, H, Dk, Dv, g_group, dt, _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream())
+    if st != 0:
+        raise KdaError(st, "kda_chunk_bwd_prologue")
+    return out
+
+
 def recurrent_step(q, k, v, g, beta, state, out=None):
     """One KDA decode step; `state` [N, H, Dk, Dv] float32 is updated in place."""
     N, H, Dk, Dv, g_group = _decode_shapes(q, k, v, g, beta)
@@ -486,6 +535,39 @@ def short_conv_fwd(x, weight, conv0=None, output_final_state=False, cu_seqlens=N
     if st != 0:
         raise KdaError(st, "kda_short_conv_fwd")
     return y, cf
+
+
+def short_conv_bwd(x, weight, dy, conv0=None, dconv_final=None, cu_seqlens=None, workspace=None):
+    """Gradients of <dy, y> + <dconv_final, conv_final> for short_conv_fwd(x,
+    weight, conv0, cu_seqlens).  Returns a dict with dx (x's dtype), dweight
+    (float32 [C, W]) and dconv0 (x's dtype [N, W-1, C])."""
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be [B, T, C] and weight [C, W]")
+    B, T, C = x.shape
+    W = weight.shape[-1]
+    dt = _dt(x)
+    for t in (weight, conv0, dy, dconv_final):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError("x, weight, dy and conv states must share one dtype")
+    _expect(weight, (C, W), "weight")
+    N = _num_seqs(B, cu_seqlens)
+    _expect(dy, (B, T, C), "dy")
+    _expect(conv0, (N, max(W - 1, 0), C), "conv0")
+    _expect(dconv_final, (N, max(W - 1, 0), C), "dconv_final")
+    _check_dev(x, weight, dy, conv0, dconv_final, cu_seqlens)
+    out = {"dx": torch.empty_like(x), "dweight": torch.empty((C, W), dtype=torch.float32, device=x.device),
+           "dconv0": torch.empty((N, max(W - 1, 0), C), dtype=x.dtype, device=x.device)}
+    need = int(lib().kda_short_conv_bwd_workspace_bytes(B, T, C, W))
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib().kda_short_conv_bwd(_ptr(x), _ptr(weight), _ptr(conv0), _ptr(dy), _ptr(dconv_final), _ptr(out["dx"]),
+                                  _ptr(out["dweight"]), _ptr(out["dconv0"]) if W > 1 and N > 0 else None,
+                                  _ptr(cu_seqlens), N, B, T, C, W, dt, _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream())
+    if st != 0:
+        raise KdaError(st, "kda_short_conv_bwd")
+    return out
 
 
 def short_conv_step(x, weight, conv_state, out=None):

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 9
+#define KDA_ABI_VERSION 10
 
 typedef enum {
   KDA_OK = 0,
@@ -200,6 +200,43 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   int Dk, int Dv, int g_group, kda_dtype dt, void* workspace, size_t workspace_bytes,
                                   void* stream);
 
+/* Bytes of device workspace kda_chunk_bwd_prologue needs: the chunked
+ * backward's workspace, the prepared inputs and their gradients (bf16), and
+ * per 64-token block and head the partial sums of dA_log and d dt_bias.  0
+ * for invalid sizes. */
+size_t kda_chunk_bwd_prologue_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs, int varlen,
+                                              int g_group, kda_dtype dt);
+
+/* Backward pass through the fused prologue and the chunked form (the
+ * miniKimiK3 card's KDA bullet: KDA trains through its chunked form; the
+ * Kimi-K3-Tiny-L13 card names A_log and dt_bias as its real parameters).
+ * Returns the gradients of L = <do, o> + <dht, ht> for what
+ * kda_chunk_fwd_prologue computes, with respect to q_raw, k_raw, v, f, b_raw,
+ * A_log, dt_bias and h0.  The prepared q, k, g, beta are formed into the
+ * workspace (bf16), kda_chunk_bwd runs on them, and the prologue's chain rule
+ * follows: dq_raw = r (dq - q (q . dq)) with r the row's inverse norm,
+ * df = dg * (-exp(A_log) sigmoid(f + dt_bias)), db_raw = dbeta beta (1 - beta),
+ * dA_log = sum over tokens of dg * g, d dt_bias = sum over tokens of df
+ * (summed in a fixed order: bitwise deterministic).
+ *
+ *   q_raw, k_raw, v, f, b_raw, A_log, dt_bias, h0, cu_seqlens, sizes: as for
+ *          kda_chunk_fwd_prologue (dt = KDA_BF16 only, like kda_chunk_bwd).
+ *   dout, dht, dv, dh0: as for kda_chunk_bwd.
+ *   dq_raw, dk_raw [B, T, H, Dk] bf16; df [B, T, H, Dk/g_group] bf16;
+ *   db_raw [B, T, H] bf16; dA_log, ddt_bias [H, Dk/g_group] f32 (always
+ *          written; zero without tokens).
+ *   workspace  at least kda_chunk_bwd_prologue_workspace_bytes(...) bytes,
+ *          256-byte aligned; contents are scratch.
+ * q_raw, k_raw, dq_raw, dk_raw (and f, df with g_group = 1) must be 16-byte
+ * aligned (KDA_ERR_UNSUPPORTED otherwise).  Other errors as for kda_chunk_bwd.
+ */
+kda_status kda_chunk_bwd_prologue(const void* q_raw, const void* k_raw, const void* v, const void* f,
+                                  const void* b_raw, const float* A_log, const float* dt_bias, const float* h0,
+                                  const void* dout, const float* dht, void* dq_raw, void* dk_raw, void* dv, void* df,
+                                  void* db_raw, float* dA_log, float* ddt_bias, float* dh0, const int* cu_seqlens,
+                                  int num_seqs, int B, int T, int H, int Dk, int Dv, int g_group, kda_dtype dt,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* One decode step with the same fused prologue (q_raw, k_raw [N, H, Dk];
  * v [N, H, Dv]; f [N, H, Dk/g_group]; b_raw [N, H]; A_log, dt_bias
  * [H, Dk/g_group] f32; state [N, H, Dk, Dv] f32 in place; o [N, H, Dv]).
@@ -322,6 +359,35 @@ kda_status kda_recurrent_step_pool_prologue(const void* q_raw, const void* k_raw
 kda_status kda_short_conv_fwd(const void* x, const void* weight, const void* conv0, void* y, void* conv_final,
                               const int* cu_seqlens, int num_seqs, int B, int T, int C, int W, kda_dtype dt,
                               void* stream);
+
+/* Bytes of device workspace kda_short_conv_bwd needs (fp32 partial sums of
+ * the weight gradient, one row per 256-token run); 0 for invalid sizes. */
+size_t kda_short_conv_bwd_workspace_bytes(int B, int T, int C, int W);
+
+/* Backward of kda_short_conv_fwd: the gradients of L = <dy, y> +
+ * <dconv_final, conv_final> (the convolution is linear in x and conv0, and
+ * in the weights).  Per channel, for a token t of a sequence [s, e):
+ *
+ *   dx[t]       = sum_{u=0}^{W-1} weight[W-1-u] dy[t+u]  over t+u < e,
+ *                 + dconv_final[t - (e - (W-1))]         for t >= e - (W-1)
+ *   dweight[w] += dy[t] x[t - (W-1) + w]   (positions before s: conv0 / zeros)
+ *   dconv0[row] = the same sum as dx, at the history position s - (W-1) + row
+ *
+ *   x, weight, conv0, cu_seqlens, num_seqs, B, T, C, W, dt: as for
+ *          kda_short_conv_fwd.
+ *   dy [B, T, C] dt; dconv_final [N, W-1, C] dt or NULL (zero).
+ *   dx [B, T, C] dt; dweight [C, W] f32 (summed over every token, in a fixed
+ *          order: bitwise deterministic); dconv0 [N, W-1, C] dt or NULL.
+ *   workspace  at least kda_short_conv_bwd_workspace_bytes(B, T, C, W) bytes,
+ *          256-byte aligned; contents are scratch.
+ * Supported sizes, alignment and errors as for kda_short_conv_fwd (dy, dx,
+ * dconv_final and dconv0 16-byte aligned); KDA_ERR_WORKSPACE for a missing
+ * or short workspace.
+ */
+kda_status kda_short_conv_bwd(const void* x, const void* weight, const void* conv0, const void* dy,
+                              const void* dconv_final, void* dx, float* dweight, void* dconv0,
+                              const int* cu_seqlens, int num_seqs, int B, int T, int C, int W, kda_dtype dt,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* One decode step of the short convolution for N sequences, state in place:
  * with the window [conv_state[n][0..W-2], x[n]], y[n] = sum_w weight[:, w] *

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 9 == kda.ABI_VERSION
+    assert L.kda_abi_version() == 10 == kda.ABI_VERSION
     for s in range(7):
         assert L.kda_status_str(s).decode().startswith(("KDA_OK", "KDA_ERR"))
     assert L.kda_status_str(99)
@@ -202,3 +202,47 @@ def test_saved_pair_validation():
     assert bs(dt=0) == UNSUPPORTED
     assert bs(do=None) == NULL
     assert bs(wsb=need - 1) == WORKSPACE
+
+
+def test_chunk_bwd_prologue_validation():
+    L = kda.lib()
+    need = L.kda_chunk_bwd_prologue_workspace_bytes(1, 64, 1, 64, 64, 1, 0, 1, 1)
+    assert need > L.kda_chunk_bwd_workspace_bytes(1, 64, 1, 64, 64, 1, 0, 1)
+    assert L.kda_chunk_bwd_prologue_workspace_bytes(1, 64, 1, 96, 64, 1, 0, 1, 1) == 0
+
+    def pb(qr=P, A=P, dA=P, dt=1, gg=1, ws=P, wsb=need, Dk=64, N=1, B=1, T=64, H=1, cu=None):
+        return L.kda_chunk_bwd_prologue(qr, P, P, P, P, A, P, None, P, None, P, P, P, P, P, dA, P, None, cu, N, B, T,
+                                        H, Dk, 64, gg, dt, ws, wsb, None)
+
+    assert pb(dt=7) == DTYPE
+    assert pb(dt=0) == UNSUPPORTED                    # bf16 only, like the backward
+    assert pb(Dk=96) == UNSUPPORTED
+    assert pb(A=None) == NULL
+    assert pb(dA=None) == NULL
+    assert pb(qr=None) == NULL
+    assert pb(N=2, B=1) == SHAPE
+    assert pb(cu=P, B=2, N=2) == SHAPE
+    assert pb(qr=ctypes.c_void_p(0x1008)) == UNSUPPORTED  # rows must be 16-byte aligned
+    assert pb(wsb=need - 1) == WORKSPACE
+    assert pb(ws=None) == WORKSPACE
+    assert pb(ws=ctypes.c_void_p(0x1010)) == WORKSPACE
+
+
+def test_short_conv_bwd_validation():
+    L = kda.lib()
+    need = L.kda_short_conv_bwd_workspace_bytes(1, 300, 16, 4)
+    assert need >= 2 * 4 * 16 * 4                     # two 256-token runs of W x C fp32 partials
+    assert L.kda_short_conv_bwd_workspace_bytes(1, 300, 12, 4) == 0
+
+    def cb(x=P, w=P, dy=P, dw=P, dt=1, W=4, C=16, ws=P, wsb=need, N=1, B=1, T=300, cu=None):
+        return L.kda_short_conv_bwd(x, w, None, dy, None, P, dw, None, cu, N, B, T, C, W, dt, ws, wsb, None)
+
+    assert cb(dt=7) == DTYPE
+    assert cb(W=9) == UNSUPPORTED
+    assert cb(C=12) == UNSUPPORTED
+    assert cb(dw=None) == NULL
+    assert cb(dy=None) == NULL
+    assert cb(N=2) == SHAPE
+    assert cb(x=ctypes.c_void_p(0x1008)) == UNSUPPORTED
+    assert cb(wsb=need - 1) == WORKSPACE
+    assert cb(ws=None) == WORKSPACE
