@@ -251,7 +251,37 @@ __global__ __launch_bounds__(256) void short_conv_bwd_kernel(const T* __restrict
     }
   };
   seed(t0);
-  for (int t = t0; t < t1; ++t) {
+  int t = t0;
+  // Fast path: groups of NG tokens whose look-ahead stays inside the current
+  // sequence and whose dx needs no final-state term; the x and dy loads of a
+  // group are issued together.  Pairs for W <= 5 (K3 width, W = 4: 0.62 ->
+  // 0.53 ms); wider windows keep one token at a time, where the extra
+  // registers of a group cost more than its loads in flight gain.
+  constexpr int NG = W <= 5 ? 2 : 1;
+  for (; t + NG <= t1 && t + NG + W <= e; t += NG) {
+    f32x8 xin[NG], dyin[NG];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      xin[u] = load8(x + (size_t)(t + u) * C + ch);
+      dyin[u] = load8(dy + (size_t)(t + u + W) * C + ch);
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      xwin[W - 1] = xin[u];
+      f32x8 acc = wg[W - 1] * dwin[0];
+#pragma unroll
+      for (int v = 1; v < W; ++v) acc += wg[W - 1 - v] * dwin[v];
+      store8(dx + (size_t)(t + u) * C + ch, acc);
+#pragma unroll
+      for (int j = 0; j < W; ++j) dw[j] += dwin[0] * xwin[j];
+#pragma unroll
+      for (int v = 0; v < W - 1; ++v) dwin[v] = dwin[v + 1];
+      dwin[W - 1] = dyin[u];
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j) xwin[j] = xwin[j + 1];
+    }
+  }
+  for (; t < t1; ++t) {
     if (t >= e && n + 1 < num_seqs) {  // the next non-empty sequence starts here
       do {
         ++n;

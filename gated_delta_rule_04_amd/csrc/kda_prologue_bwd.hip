@@ -17,7 +17,7 @@
 // Three launches around the chunked backward: prologue_prepare_kernel writes
 // the prepared inputs (bf16) for it; prologue_grad_kernel applies the rules
 // above and writes, per 64-token block and head, the partial sums of the two
-// parameter gradients; prologue_param_reduce_kernel sums the blocks in a
+// parameter gradients; prologue_param_reduce_kernel adds the blocks in a
 // fixed order (bitwise deterministic, no atomics).
 //
 // Design for MI355X: both row kernels are HBM-bound elementwise passes.  A
@@ -205,21 +205,33 @@ __global__ __launch_bounds__(256) void prologue_grad_kernel(
   }
 }
 
-// dA_log, d dt_bias [H][NG]: the blocks' partial sums in block order.
+// dA_log, d dt_bias [H][NG]: the blocks' partial sums.  A workgroup owns 64
+// consecutive outputs; its four wavefronts sum every fourth block each (in
+// block order, coalesced across the 64 outputs), then the four partial sums
+// are added in wavefront order: a fixed order, so the result is bitwise
+// deterministic.
 __global__ __launch_bounds__(256) void prologue_param_reduce_kernel(const float* __restrict__ part_a,
                                                                     const float* __restrict__ part_b,
                                                                     float* __restrict__ dA_log,
                                                                     float* __restrict__ ddt_bias, long long nblk,
                                                                     int HG) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= HG) return;
+  __shared__ float red[2][4][64];
+  const int lane = threadIdx.x % 64, grp = threadIdx.x / 64;
+  const int i = blockIdx.x * 64 + lane;
   float a = 0.f, b = 0.f;
-  for (long long t = 0; t < nblk; ++t) {
-    a += part_a[t * HG + i];
-    b += part_b[t * HG + i];
+  if (i < HG) {
+    for (long long t = grp; t < nblk; t += 4) {
+      a += part_a[t * HG + i];
+      b += part_b[t * HG + i];
+    }
   }
-  dA_log[i] = a;
-  ddt_bias[i] = b;
+  red[0][grp][lane] = a;
+  red[1][grp][lane] = b;
+  __syncthreads();
+  if (grp == 0 && i < HG) {
+    dA_log[i] = ((red[0][0][lane] + red[0][1][lane]) + red[0][2][lane]) + red[0][3][lane];
+    ddt_bias[i] = ((red[1][0][lane] + red[1][1][lane]) + red[1][2][lane]) + red[1][3][lane];
+  }
 }
 
 template <int DK, int GG>
@@ -243,7 +255,7 @@ hipError_t prologue_grad_t(const PrologueBwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int HG = a.H * (DK / GG);
-  hipLaunchKernelGGL(prologue_param_reduce_kernel, dim3((HG + 255) / 256), dim3(256), 0, s, a.part_a, a.part_b,
+  hipLaunchKernelGGL(prologue_param_reduce_kernel, dim3((HG + 63) / 64), dim3(256), 0, s, a.part_a, a.part_b,
                      a.dA_log, a.ddt_bias, nblk, HG);
   return hipGetLastError();
 }

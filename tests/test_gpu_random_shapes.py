@@ -114,3 +114,48 @@ def test_random_backward(seed):
         if n == "dh0" and d.get("h0") is None:
             continue
         check_grad("random bwd %d" % seed, n, got[n].cpu(), ref[n])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_prologue_backward(seed):
+    from tests.test_gpu_prologue_bwd import compare
+    c = _draw(1200 + seed, max_t=180)
+    d = inputs.make_prologue(c["B"], c["T"], c["H"], c["dk"], c["dv"], "bf16", g_group=c["gg"], seed=1200 + seed,
+                             h0=True, cu_seqlens=c["cu"])
+    N = c["B"] if c["cu"] is None else len(c["cu"]) - 1
+    ct = inputs.make_cotangents(c["B"], c["T"], c["H"], c["dk"], c["dv"], N, "bf16", seed=1300 + seed,
+                                final_state=True, state_std=1.0)
+    compare("random prologue bwd %d" % seed, d, ct)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_conv_backward(seed):
+    from oracle.short_conv import short_conv_backward
+    from tests.test_gpu_conv import _conv_bwd_check
+    rng = np.random.default_rng(1400 + seed)
+    W, C = int(rng.integers(1, 9)), 8 * int(rng.integers(1, 40))
+    dt = torch.bfloat16 if rng.integers(0, 2) else torch.float32
+    if rng.integers(0, 2):
+        lens = [int(x) for x in rng.integers(0, 300, int(rng.integers(1, 7)))]
+        if sum(lens) == 0:
+            lens[-1] = 1
+        cu = np.array([0] + list(np.cumsum(lens)), dtype=np.int32)
+        B, T = 1, int(cu[-1])
+    else:
+        cu, B, T = None, int(rng.integers(1, 4)), int(rng.integers(1, 700))
+    N = B if cu is None else len(cu) - 1
+    states = bool(rng.integers(0, 2))
+    print("case seed %d: W %d C %d %s B %d T %d docs %s states %s" % (seed, W, C, dt, B, T, None if cu is None
+                                                                       else list(np.diff(cu)), states), flush=True)
+    mk = lambda shape, s, scale=1.0: torch.from_numpy(
+        (np.random.default_rng(s).standard_normal(shape) * scale).astype(np.float32)).to(dt)
+    x, w, dy = mk((B, T, C), seed), mk((C, W), seed + 1, 0.5), mk((B, T, C), seed + 2)
+    c0 = mk((N, W - 1, C), seed + 3) if states else None
+    dfin = mk((N, W - 1, C), seed + 4) if states else None
+    dev = lambda t: None if t is None else t.cuda()
+    got = kda.short_conv_bwd(dev(x), dev(w), dev(dy), conv0=dev(c0), dconv_final=dev(dfin),
+                             cu_seqlens=None if cu is None else torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    f = lambda t: None if t is None else t.float()
+    ref = short_conv_backward(f(x), f(w), f(dy), conv0=f(c0), dfinal=f(dfin), cu_seqlens=cu)
+    _conv_bwd_check("random conv bwd %d" % seed, got, ref, dt)
