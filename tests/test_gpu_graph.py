@@ -112,3 +112,34 @@ def test_training_pair_in_a_graph():
         assert torch.equal(o, o_e) and torch.equal(ht, h_e), rep
         for n, t in gr_e.items():
             assert torch.equal(gr[n], t), (rep, n)
+
+
+def test_prologue_and_conv_backwards_in_a_graph():
+    d = inputs.make_prologue(1, 150, 2, 128, 128, "bf16", seed=35, h0=True)
+    ct = inputs.make_cotangents(1, 150, 2, 128, 128, 1, "bf16", seed=36, final_state=True, state_std=1.0)
+    dev = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
+    do, dht = ct["do"].cuda(), ct["dht"].cuda()
+    pargs = [dev[n] for n in ("q_raw", "k_raw", "v", "f", "b_raw", "A_log", "dt_bias")]
+    x = torch.randn((1, 300, 64), generator=torch.Generator().manual_seed(37)).bfloat16().cuda()
+    w = (0.5 * torch.randn((64, 4), generator=torch.Generator().manual_seed(38))).bfloat16().cuda()
+    dy = torch.randn((1, 300, 64), generator=torch.Generator().manual_seed(39)).bfloat16().cuda()
+    pe = kda.chunk_bwd_prologue(*pargs, do, initial_state=dev["h0"], dht=dht)
+    ce = kda.short_conv_bwd(x, w, dy)
+    torch.cuda.synchronize()
+    res = {}
+
+    def run():
+        res["p"] = kda.chunk_bwd_prologue(*pargs, do, initial_state=dev["h0"], dht=dht)
+        res["c"] = kda.short_conv_bwd(x, w, dy)
+
+    g = _capture(run)
+    for rep in range(REPLAYS):
+        for t in list(res["p"].values()) + list(res["c"].values()):
+            t.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in pe.items():
+            assert torch.equal(res["p"][n], t), (rep, n)
+        for n, t in ce.items():
+            assert torch.equal(res["c"][n], t), (rep, n)
