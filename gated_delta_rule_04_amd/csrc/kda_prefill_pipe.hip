@@ -390,36 +390,45 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       lds_barrier();  // ---------------------------------------------------- Q
       if (cG >= 0 && cG < nchunks) {
         // decay before this wavefront's rows within the sub-block, the
-        // sub-block's total and the next sub-block's total (log2 units): the
-        // other wavefronts' totals
+        // sub-block's total and the next sub-block's total (log2 units), from
+        // the wavefronts' totals.  The position P of this wavefront in its
+        // sub-block is a compile-time index, so each sum is a fixed sequence
+        // of adds; the totals are added in wavefront order (this
+        // wavefront's own in its place), so every wavefront of a sub-block
+        // computes the same bits for its reference.
         float pre[8], gend[8], gnext[8];
+        static_switch<WPB>(wave % WPB, [&](auto Pc) {
+          constexpr int P = decltype(Pc)::value;
+          const int w0 = sbw * WPB;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          pre[c] = 0.f;
-          gend[c] = tot[c];
-          gnext[c] = 0.f;
-        }
-        const int wend = (sbw + 1 < NSB ? sbw + 2 : sbw + 1) * WPB;  // uniform
+          for (int c4 = 0; c4 < 8; c4 += 4) {
+            f32x4 sum = {-0.f, -0.f, -0.f, -0.f};  // x + (-0) is x: folds away
 #pragma unroll
-        for (int u = 0; u < 2 * WPB; ++u) {
-          const int w = sbw * WPB + u;
-          if (w == wave || w >= wend) continue;  // uniform
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch]);
-          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.gsum[w][ch + 4]);
+            for (int u = 0; u < WPB; ++u) {
+              const f32x4 a = u == P ? f32x4{tot[c4], tot[c4 + 1], tot[c4 + 2], tot[c4 + 3]}
+                                     : *reinterpret_cast<const f32x4*>(&sm.gsum[w0 + u][ch + c4]);
+              if (u == P) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (u < WPB) {
-              gend[c] += a[c];
-              gend[c + 4] += b[c];
-              if (w < wave) {
-                pre[c] += a[c];
-                pre[c + 4] += b[c];
+                for (int c = 0; c < 4; ++c) pre[c4 + c] = sum[c];
               }
-            } else {
-              gnext[c] += a[c];
-              gnext[c + 4] += b[c];
+              sum = u == 0 ? a : sum + a;
             }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) gend[c4 + c] = sum[c];
           }
+        });
+        if (sbw + 1 < NSB) {  // uniform
+#pragma unroll
+          for (int c4 = 0; c4 < 8; c4 += 4) {
+            f32x4 sum = *reinterpret_cast<const f32x4*>(&sm.gsum[(sbw + 1) * WPB][ch + c4]);
+#pragma unroll
+            for (int u = 1; u < WPB; ++u) sum += *reinterpret_cast<const f32x4*>(&sm.gsum[(sbw + 1) * WPB + u][ch + c4]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) gnext[c4 + c] = sum[c];
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) gnext[c] = 0.f;
         }
         // prologue: inverse L2 norms of this thread's q and k rows (a row's
         // channels are spread over CGN consecutive lanes)
