@@ -63,6 +63,20 @@ __device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
   *reinterpret_cast<f32x2*>(p + 2) = f32x2{v[2], v[3]};
 }
 
+// N = 2 or 4 consecutive values to LDS.
+template <typename E, int N>
+__device__ __forceinline__ void store_run(E* p, const float (&v)[N]) {
+  if constexpr (N == 4) {
+    store4<E>(p, f32x4{v[0], v[1], v[2], v[3]});
+  } else {
+    static_assert(N == 2, "store_run");
+    if constexpr (sizeof(E) == 2)
+      *reinterpret_cast<unsigned*>(p) = pk_bf16(v[0], v[1]);
+    else
+      *reinterpret_cast<f32x2*>(p) = f32x2{v[0], v[1]};
+  }
+}
+
 template <typename T>
 struct Pair;
 template <>
@@ -123,13 +137,28 @@ struct Vec8<float> {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
+// CPT consecutive elements: Vec8, or a pair (one 4- or 8-byte access).
+template <typename T, int N>
+struct VecN;
+template <typename T>
+struct VecN<T, 8> : Vec8<T> {};
+template <>
+struct VecN<bf16, 2> {
+  typedef bf16x2 type;
+  __device__ __forceinline__ static type load(rsrc_t r, int off) { return bload<bf16x2>(r, off); }
+};
+template <>
+struct VecN<float, 2> {
+  typedef f32x2 type;
+  __device__ __forceinline__ static type load(rsrc_t r, int off) { return bload<f32x2>(r, off); }
+};
 template <typename V>
 __device__ __forceinline__ float elem(const V& v, int i) {
   return (float)v[i];
 }
-// Sum of squares of 8 elements (bf16: four v_dot2_f32_bf16, which take the
+// Sum of squares of the elements (bf16: v_dot2_f32_bf16, which take the
 // pairs straight from the loaded registers).
-__device__ __forceinline__ float sumsq8(const bf16x8& v) {
+__device__ __forceinline__ float sumsq(const bf16x8& v) {
   float s = 0.f;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -138,12 +167,14 @@ __device__ __forceinline__ float sumsq8(const bf16x8& v) {
   }
   return s;
 }
-__device__ __forceinline__ float sumsq8(const f32x8& v) {
+__device__ __forceinline__ float sumsq(const f32x8& v) {
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) s += v[c] * v[c];
   return s;
 }
+__device__ __forceinline__ float sumsq(const bf16x2& v) { return __builtin_amdgcn_fdot2_f32_bf16(v, v, 0.f, false); }
+__device__ __forceinline__ float sumsq(const f32x2& v) { return v[0] * v[0] + v[1] * v[1]; }
 // Four consecutive elements of a row (one 8- or 16-byte access).
 template <typename T>
 struct Row4;
@@ -189,7 +220,13 @@ struct PrefillCfg {
   // XOR-permuted.  fp32 reads that tile's columns directly.
   static constexpr bool TR = sizeof(E) == 2;
   static constexpr int KEP = TR ? DK + 16 : KP;  // pitch of the KE tile
-  static constexpr int CGN = DK / 8;             // gating: groups of 8 key channels
+  // gating: key channels per producer thread.  bf16 at 128 key channels: 2,
+  // so a wavefront's lanes span whole token rows (each lane's cumulative decay
+  // is a plain running sum, no cross-lane scan, and its per-channel factors
+  // serve 8 rows); else 8 (16-byte loads).
+  static constexpr int CPT = (DK_ == 128 && sizeof(T_) == 2) ? 2 : 8;
+  static constexpr int CG = CPT < 4 ? CPT : 4;   // gating: channels per LDS write
+  static constexpr int CGN = DK / CPT;           // gating: channel groups of a row
   static constexpr int NRB = NA / CGN;           // gating: row blocks
   static constexpr int RPB = CL / NRB;           // gating: rows per block
   static constexpr int RBW = 64 / CGN;           // gating: row blocks per wavefront
@@ -203,7 +240,7 @@ struct PrefillCfg {
   static_assert(NRB * CGN == NA && RPB * NRB == CL && RBW * CGN == 64, "gating map");
   static_assert(RPW <= 16 && WPB * RPW == 16, "a sub-block is whole wavefronts of gating rows");
   static_assert(NSB <= NPW && NSB % 2 == 0, "one producer wavefront per sub-block transform");
-  static_assert(RBW == 4 || WPB == 1, "cross-wavefront prefixes use the four-row-block scan");
+  static_assert(RBW == 4 || RBW == 1 || WPB == 1, "cross-wavefront prefixes: four row blocks or one");
 };
 
 // Cross-lane sums without LDS traffic (the LDS is the busiest unit of the

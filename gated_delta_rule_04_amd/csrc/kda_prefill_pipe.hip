@@ -94,6 +94,7 @@ struct PipeSmem {
   alignas(16) float phi[2][Cfg::NSB][Cfg::DK];  // e^{G_end - M + M'} of each sub-block
   alignas(16) float psi[2][Cfg::DK];            // e^M of the chunk's first sub-block
   alignas(16) float gsum[Cfg::NPW][Cfg::DK];    // per-wavefront log2-decay totals
+  alignas(16) float nrm[Cfg::NPW][16];          // prologue: per-wavefront inverse row norms
 };
 
 // 16x16 products whose first operand comes from LDS in accumulator form
@@ -206,14 +207,15 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
 
   if (producer) {
     // ================= producer wavefronts ===================================
-    // Gating map: thread = (8 key channels, block of RPB consecutive tokens).
+    // Gating map: thread = (CPT key channels, block of RPB consecutive tokens).
+    constexpr int CPT = Cfg::CPT, CG = Cfg::CG, CGN = Cfg::CGN, RBW = Cfg::RBW;
+    typedef typename VecN<T, CPT>::type VC;
     typedef typename Vec8<T>::type V8;
-    constexpr int CGN = Cfg::CGN, RBW = Cfg::RBW;
     const int cg = tid % CGN, rb = tid / CGN;
-    const int ch = 8 * cg;                 // first key channel of this thread
+    const int ch = CPT * cg;               // first key channel of this thread
     const int rbw = lane / CGN;            // row block within the wavefront
     const int sbw = wave / WPB;            // sub-block of this wavefront's rows
-    V8 rq[RPB], rk[RPB], rg[GG == 1 ? RPB : 1];
+    VC rq[RPB], rk[RPB], rg[GG == 1 ? RPB : 1];
     // V rows of the slice, in 8-element units spread over the producers
     constexpr int VU = CL * VS / 8, NVL = (VU + Cfg::NA - 1) / Cfg::NA;
     V8 rv[NVL];
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     const int rsg = H * (DK / GG) * (int)sizeof(T);  // token stride of g
     const int rsb = H * (int)sizeof(T);              // token stride of beta
     // prologue: -exp(A_log) and dt_bias log2(e) of this thread's channels (or group)
-    constexpr int NGC = PRO ? (GG == 1 ? 8 : 1) : 1;
+    constexpr int NGC = PRO ? (GG == 1 ? CPT : 1) : 1;
     float nA[NGC], gDs[NGC];
     if constexpr (PRO) {
 #pragma unroll
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       for (int j = 0; j < RPB; ++j) {
         const int r = rb * RPB + j;
         if constexpr (GG == 1)
-          rg[j] = Vec8<T>::load(bg, r * rsg + ch * (int)sizeof(T));
+          rg[j] = VecN<T, CPT>::load(bg, r * rsg + ch * (int)sizeof(T));
         else
           rgs[j] = bload<T>(bg, r * rsg + (ch / GG) * (int)sizeof(T));
       }
@@ -272,9 +274,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       const rsrc_t bk = make_rsrc(gk + chunk_row0(ck) * DK, span(nv, rsk, DK * (int)sizeof(T)));
       const rsrc_t bv = make_rsrc(gv + chunk_row0(ck) * DV + col0, span(nv, rsv, VS * (int)sizeof(T)));
 #pragma unroll
-      for (int j = 0; j < RPB; ++j) rq[j] = Vec8<T>::load(bq, (rb * RPB + j) * rsk + ch * (int)sizeof(T));
+      for (int j = 0; j < RPB; ++j) rq[j] = VecN<T, CPT>::load(bq, (rb * RPB + j) * rsk + ch * (int)sizeof(T));
 #pragma unroll
-      for (int j = 0; j < RPB; ++j) rk[j] = Vec8<T>::load(bk, (rb * RPB + j) * rsk + ch * (int)sizeof(T));
+      for (int j = 0; j < RPB; ++j) rk[j] = VecN<T, CPT>::load(bk, (rb * RPB + j) * rsk + ch * (int)sizeof(T));
 #pragma unroll
       for (int j = 0; j < NVL; ++j) {
         const int u = tid + Cfg::NA * j;
@@ -282,9 +284,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
           rv[j] = Vec8<T>::load(bv, (u / (VS / 8)) * rsv + 8 * (u % (VS / 8)) * (int)sizeof(T));
       }
     };
-    float G[RPB][8];  // cumulative log2-decay of this thread's rows (thread-local)
-    float off[8];     // log2-decay of the rows of this wavefront before this thread's block
-    float tot[8];     // log2-decay over this wavefront's rows
+    float G[RPB][CPT];  // cumulative log2-decay of this thread's rows (thread-local)
+    float off[CPT];     // log2-decay of the rows of this wavefront before this thread's block
+    float tot[CPT];     // log2-decay over this wavefront's rows
 
     // ---- transform of sub-block I of the chunk in buffer b: N = A_II and
     // N^T (registers only), P^T, X = (I + N)^-1; T^T = (X Diag(b))^T and P^T
@@ -327,9 +329,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       }
       if (cG >= 0 && cG < nchunks) {
         // thread-local cumulative decay; prefix over this wavefront's blocks
-        float acc[8];
+        float acc[CPT];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+        for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
         // rows past the end of the sequence stay inert under the prologue too:
         // their (zero) gate logits must not become a decay.  A full chunk
         // (uniform test) skips the per-row mask.
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
               if constexpr (!FULL) lrow = live ? lrow : 0.f;
             }
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
+            for (int c = 0; c < CPT; ++c) {
               float lx = lrow;
               if constexpr (GG == 1) {
                 lx = lg_gate(elem(rg[j], c), c);
@@ -360,29 +362,40 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
           gate_rows(IC<1>{});
         else
           gate_rows(IC<0>{});
-        if constexpr (RBW == 4) {  // the four row blocks are the wavefront's 16-lane rows
+        if constexpr (RBW == 1) {  // the wavefront's rows are this thread's
 #pragma unroll
-          for (int c = 0; c < 8; ++c) rows4_scan(acc[c], rbw, off[c], tot[c]);
+          for (int c = 0; c < CPT; ++c) {
+            off[c] = 0.f;
+            tot[c] = acc[c];
+          }
+        } else if constexpr (RBW == 4) {  // the four row blocks are the wavefront's 16-lane rows
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) rows4_scan(acc[c], rbw, off[c], tot[c]);
         } else {  // one wavefront is one sub-block: its total is the sub-block's
 #pragma unroll
-          for (int c = 0; c < 8; ++c) off[c] = acc[c];  // inclusive prefix over blocks
+          for (int c = 0; c < CPT; ++c) off[c] = acc[c];  // inclusive prefix over blocks
 #pragma unroll
           for (int d = 1; d < RBW; d <<= 1) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
+            for (int c = 0; c < CPT; ++c) {
               const float y = __shfl_up(off[c], d * CGN);
               if (rbw >= d) off[c] += y;
             }
           }
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
+          for (int c = 0; c < CPT; ++c) {
             tot[c] = __shfl(off[c], (RBW - 1) * CGN + cg);
             off[c] -= acc[c];  // exclusive within the wavefront
           }
         }
         if (rbw == RBW - 1) {  // this wavefront's total, for the other wavefronts
-          *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch]) = f32x4{tot[0], tot[1], tot[2], tot[3]};
-          *reinterpret_cast<f32x4*>(&sm.gsum[wave][ch + 4]) = f32x4{tot[4], tot[5], tot[6], tot[7]};
+#pragma unroll
+          for (int c4 = 0; c4 < CPT; c4 += CG) {
+            float t4[CG];
+#pragma unroll
+            for (int c = 0; c < CG; ++c) t4[c] = tot[c4 + c];
+            store_run<float, CG>(&sm.gsum[wave][ch + c4], t4);
+          }
         }
         if (tid < CL) sm.beta[bG][tid] = PRO ? (tid < nvG ? sigmoid_f(to_f32(rbeta)) : 0.f) : to_f32(rbeta);
       }
@@ -396,55 +409,102 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         // of adds; the totals are added in wavefront order (this
         // wavefront's own in its place), so every wavefront of a sub-block
         // computes the same bits for its reference.
-        float pre[8], gend[8], gnext[8];
+        typedef float fcg __attribute__((ext_vector_type(CG)));
+        float pre[CPT], gend[CPT], gnext[CPT];
         static_switch<WPB>(wave % WPB, [&](auto Pc) {
           constexpr int P = decltype(Pc)::value;
           const int w0 = sbw * WPB;
 #pragma unroll
-          for (int c4 = 0; c4 < 8; c4 += 4) {
-            f32x4 sum = {-0.f, -0.f, -0.f, -0.f};  // x + (-0) is x: folds away
+          for (int c4 = 0; c4 < CPT; c4 += CG) {
+            fcg sum = -0.f;  // x + (-0) is x: folds away
 #pragma unroll
             for (int u = 0; u < WPB; ++u) {
-              const f32x4 a = u == P ? f32x4{tot[c4], tot[c4 + 1], tot[c4 + 2], tot[c4 + 3]}
-                                     : *reinterpret_cast<const f32x4*>(&sm.gsum[w0 + u][ch + c4]);
+              fcg a;
               if (u == P) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) pre[c4 + c] = sum[c];
+                for (int c = 0; c < CG; ++c) {
+                  a[c] = tot[c4 + c];
+                  pre[c4 + c] = sum[c];
+                }
+              } else {
+                a = *reinterpret_cast<const fcg*>(&sm.gsum[w0 + u][ch + c4]);
               }
               sum = u == 0 ? a : sum + a;
             }
 #pragma unroll
-            for (int c = 0; c < 4; ++c) gend[c4 + c] = sum[c];
+            for (int c = 0; c < CG; ++c) gend[c4 + c] = sum[c];
           }
         });
         if (sbw + 1 < NSB) {  // uniform
 #pragma unroll
-          for (int c4 = 0; c4 < 8; c4 += 4) {
-            f32x4 sum = *reinterpret_cast<const f32x4*>(&sm.gsum[(sbw + 1) * WPB][ch + c4]);
+          for (int c4 = 0; c4 < CPT; c4 += CG) {
+            fcg sum = *reinterpret_cast<const fcg*>(&sm.gsum[(sbw + 1) * WPB][ch + c4]);
 #pragma unroll
-            for (int u = 1; u < WPB; ++u) sum += *reinterpret_cast<const f32x4*>(&sm.gsum[(sbw + 1) * WPB + u][ch + c4]);
+            for (int u = 1; u < WPB; ++u) sum += *reinterpret_cast<const fcg*>(&sm.gsum[(sbw + 1) * WPB + u][ch + c4]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) gnext[c4 + c] = sum[c];
+            for (int c = 0; c < CG; ++c) gnext[c4 + c] = sum[c];
           }
         } else {
 #pragma unroll
-          for (int c = 0; c < 8; ++c) gnext[c] = 0.f;
+          for (int c = 0; c < CPT; ++c) gnext[c] = 0.f;
         }
         // prologue: inverse L2 norms of this thread's q and k rows (a row's
         // channels are spread over CGN consecutive lanes)
         float iq[RPB], ik[RPB];
 #pragma unroll
         for (int j = 0; j < RPB; ++j) iq[j] = ik[j] = 1.f;
-        if constexpr (PRO) {
+        if constexpr (PRO && CGN == 64) {
+          // A row spans the wavefront, and its 8 rows are every lane's: the
+          // 16 sums of squares (q, k) are reduced together, halving the
+          // values a lane holds at each exchange (lanes l and l ^ 32, then
+          // l ^ 16), then summed over the 16-lane rows; lane 16R then holds
+          // the sums 4R .. 4R + 3 and hands their inverse roots to the whole
+          // wavefront through LDS (the wavefront's own slot: its LDS accesses
+          // complete in order).
+          static_assert(2 * RPB == 16, "16 sums per wavefront");
+          float x[16];
 #pragma unroll
           for (int j = 0; j < RPB; ++j) {
-            const float sq = row_sum<CGN>(sumsq8(rq[j]));
-            const float sk = row_sum<CGN>(sumsq8(rk[j]));
+            x[j] = sumsq(rq[j]);
+            x[RPB + j] = sumsq(rk[j]);
+          }
+          auto swap_add = [](float a, float b, bool by32) {
+            const unsigned ab = __builtin_bit_cast(unsigned, a), bb = __builtin_bit_cast(unsigned, b);
+            const auto r = by32 ? __builtin_amdgcn_permlane32_swap(ab, bb, false, false)
+                                : __builtin_amdgcn_permlane16_swap(ab, bb, false, false);
+            return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+          };
+#pragma unroll
+          for (int p = 0; p < 8; ++p) x[p] = swap_add(x[p], x[p + 8], true);   // p + 8 (lane >= 32)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) x[p] = swap_add(x[p], x[p + 4], false);  // p + 4 (lane / 16) % 2 + ...
+          f32x4 r4;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) r4[p] = __builtin_amdgcn_rsqf(row_sum<16>(x[p]) + kNormEps);
+          float* slot = &sm.nrm[wave][0];
+          if (l16 == 0) *reinterpret_cast<f32x4*>(slot + 4 * kg) = r4;
+          __builtin_amdgcn_wave_barrier();
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int j = 0; j < RPB; j += 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(slot + j);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(slot + RPB + j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              iq[j + i] = a[i];
+              ik[j + i] = b[i];
+            }
+          }
+        } else if constexpr (PRO) {
+#pragma unroll
+          for (int j = 0; j < RPB; ++j) {
+            const float sq = row_sum<CGN>(sumsq(rq[j]));
+            const float sk = row_sum<CGN>(sumsq(rk[j]));
             iq[j] = __builtin_amdgcn_rsqf(sq + kNormEps);
             ik[j] = __builtin_amdgcn_rsqf(sk + kNormEps);
           }
         }
-        // Four channels at a time: the references M of this sub-block and M'
+        // CG channels at a time: the references M of this sub-block and M'
         // of the next one in the chunk (0 after the chunk's last sub-block);
         // KE = KD e^{G_end - M} e^{M'} (two factors that each stay in range
         // inside the decay domain; a product that underflows there is below
@@ -453,11 +513,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         // (token-major) of this thread's rows.
         const bool writer = wave % WPB == 0 && rbw == 0;  // one per (sub-block, channel group)
 #pragma unroll
-        for (int c4 = 0; c4 < 8; c4 += 4) {
+        for (int c4 = 0; c4 < CPT; c4 += CG) {
           // base: the decay before this thread's rows, less M; fe1 = e^{G_end - M} = e^M
-          float base[4], fe1[4], fe2[4];
+          float base[CG], fe1[CG], fe2[CG];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < CG; ++c) {
             const float mid = 0.5f * gend[c4 + c];
             base[c] = pre[c4 + c] + off[c4 + c] - mid;
             fe1[c] = fast_exp2(mid);
@@ -466,9 +526,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
 #pragma unroll
           for (int j = 0; j < RPB; ++j) {
             const int r = rb * RPB + j;
-            float qo[4], ko[4], eo[4], dd[4];
+            float qo[CG], ko[CG], eo[CG], dd[CG];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < CG; ++c) {
               const float x = base[c] + G[j][c4 + c];  // G - M at this row
               const float el = fast_exp2(x), er = fast_exp2(-x);
               const float kx = elem(rk[j], c4 + c) * ik[j];
@@ -477,18 +537,21 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
               dd[c] = kx * er;
               eo[c] = (dd[c] * fe1[c]) * fe2[c];
             }
-            store4<E>(&sm.q[bG][r][ch + c4], f32x4{qo[0], qo[1], qo[2], qo[3]});
-            store4<E>(&sm.k[bG][r][ch + c4], f32x4{ko[0], ko[1], ko[2], ko[3]});
-            store4<E>(&sm.kd[r][ch + c4], f32x4{dd[0], dd[1], dd[2], dd[3]});
+            const int cc = ch + c4;
+            store_run<E, CG>(&sm.q[bG][r][cc], qo);
+            store_run<E, CG>(&sm.k[bG][r][cc], ko);
+            store_run<E, CG>(&sm.kd[r][cc], dd);
             if constexpr (Cfg::TR)
-              store4<E>(&sm.ke[bG][r][4 * (((ch + c4) >> 2) ^ kh_swizzle(r))], f32x4{eo[0], eo[1], eo[2], eo[3]});
+              store_run<E, CG>(&sm.ke[bG][r][4 * ((cc >> 2) ^ kh_swizzle(r)) + (cc & 3)], eo);
             else
-              store4<E>(&sm.ke[bG][r][ch + c4], f32x4{eo[0], eo[1], eo[2], eo[3]});
+              store_run<E, CG>(&sm.ke[bG][r][cc], eo);
           }
           if (writer) {  // the state factors of the sub-block (and e^M of a chunk's first)
-            *reinterpret_cast<f32x4*>(&sm.phi[bG][sbw][ch + c4]) =
-                f32x4{fe1[0] * fe2[0], fe1[1] * fe2[1], fe1[2] * fe2[2], fe1[3] * fe2[3]};
-            if (sbw == 0) *reinterpret_cast<f32x4*>(&sm.psi[bG][ch + c4]) = f32x4{fe1[0], fe1[1], fe1[2], fe1[3]};
+            float ph[CG];
+#pragma unroll
+            for (int c = 0; c < CG; ++c) ph[c] = fe1[c] * fe2[c];
+            store_run<float, CG>(&sm.phi[bG][sbw][ch + c4], ph);
+            if (sbw == 0) store_run<float, CG>(&sm.psi[bG][ch + c4], fe1);
           }
         }
 #pragma unroll
