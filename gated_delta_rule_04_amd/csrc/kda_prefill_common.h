@@ -220,11 +220,11 @@ struct PrefillCfg {
   // XOR-permuted.  fp32 reads that tile's columns directly.
   static constexpr bool TR = sizeof(E) == 2;
   static constexpr int KEP = TR ? DK + 16 : KP;  // pitch of the KE tile
-  // gating: key channels per producer thread.  bf16 at 128 key channels: 2,
-  // so a wavefront's lanes span whole token rows (each lane's cumulative decay
-  // is a plain running sum, no cross-lane scan, and its per-channel factors
-  // serve 8 rows); else 8 (16-byte loads).
-  static constexpr int CPT = (DK_ == 128 && sizeof(T_) == 2) ? 2 : 8;
+  // gating: key channels per producer thread.  bf16: 2, so a token row spans
+  // the wavefront (128 key channels: each lane's cumulative decay is a plain
+  // running sum, no cross-lane scan) or its half (64), and a lane's
+  // per-channel factors serve 8 rows; fp32: 8 (16-byte loads).
+  static constexpr int CPT = sizeof(T_) == 2 ? 2 : 8;
   static constexpr int CG = CPT < 4 ? CPT : 4;   // gating: channels per LDS write
   static constexpr int CGN = DK / CPT;           // gating: channel groups of a row
   static constexpr int NRB = NA / CGN;           // gating: row blocks
@@ -241,6 +241,7 @@ struct PrefillCfg {
   static_assert(RPW <= 16 && WPB * RPW == 16, "a sub-block is whole wavefronts of gating rows");
   static_assert(NSB <= NPW && NSB % 2 == 0, "one producer wavefront per sub-block transform");
   static_assert(RBW == 4 || RBW == 1 || WPB == 1, "cross-wavefront prefixes: four row blocks or one");
+  static_assert(RBW <= 2 || sizeof(T_) == 4, "bf16 gating: rows of 32 or 64 lanes");
 };
 
 // Cross-lane sums without LDS traffic (the LDS is the busiest unit of the
@@ -273,6 +274,16 @@ __device__ __forceinline__ void rows4_scan(float x, int row, float& excl, float&
   const auto r = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
   const float lower = __builtin_bit_cast(float, (unsigned)r[0]), upper = __builtin_bit_cast(float, (unsigned)r[1]);
   excl = ((row & 1) ? even : 0.f) + ((row & 2) ? lower : 0.f);
+  total = lower + upper;
+}
+// Over the two halves of a wavefront, lane by lane: the value of the lower
+// half for the upper half's lanes (0 for the lower half's) and the sum of
+// both (one v_permlane32_swap).
+__device__ __forceinline__ void rows2_scan(float x, int half, float& excl, float& total) {
+  const unsigned xb = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+  const float lower = __builtin_bit_cast(float, (unsigned)r[0]), upper = __builtin_bit_cast(float, (unsigned)r[1]);
+  excl = half ? lower : 0.f;
   total = lower + upper;
 }
 // The total of x over the four 16-lane rows, lane by lane (the sum that

@@ -94,7 +94,7 @@ struct PipeSmem {
   alignas(16) float phi[2][Cfg::NSB][Cfg::DK];  // e^{G_end - M + M'} of each sub-block
   alignas(16) float psi[2][Cfg::DK];            // e^M of the chunk's first sub-block
   alignas(16) float gsum[Cfg::NPW][Cfg::DK];    // per-wavefront log2-decay totals
-  alignas(16) float nrm[Cfg::NPW][16];          // prologue: per-wavefront inverse row norms
+  alignas(16) float nrm[Cfg::NPW][32];          // prologue: per-wavefront inverse row norms
 };
 
 // 16x16 products whose first operand comes from LDS in accumulator form
@@ -368,6 +368,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
             off[c] = 0.f;
             tot[c] = acc[c];
           }
+        } else if constexpr (RBW == 2) {  // the two row blocks are the wavefront's halves
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) rows2_scan(acc[c], rbw, off[c], tot[c]);
         } else if constexpr (RBW == 4) {  // the four row blocks are the wavefront's 16-lane rows
 #pragma unroll
           for (int c = 0; c < CPT; ++c) rows4_scan(acc[c], rbw, off[c], tot[c]);
@@ -453,15 +456,17 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         float iq[RPB], ik[RPB];
 #pragma unroll
         for (int j = 0; j < RPB; ++j) iq[j] = ik[j] = 1.f;
-        if constexpr (PRO && CGN == 64) {
-          // A row spans the wavefront, and its 8 rows are every lane's: the
-          // 16 sums of squares (q, k) are reduced together, halving the
-          // values a lane holds at each exchange (lanes l and l ^ 32, then
-          // l ^ 16), then summed over the 16-lane rows; lane 16R then holds
-          // the sums 4R .. 4R + 3 and hands their inverse roots to the whole
-          // wavefront through LDS (the wavefront's own slot: its LDS accesses
+        if constexpr (PRO && CGN >= 32) {
+          // A row spans the wavefront (CGN = 64) or its half (32), and the
+          // 8 rows of that span are every lane's: the 16 sums of squares
+          // (q, k) are reduced together, halving the values a lane holds at
+          // each exchange (lanes l and l ^ 32 for a whole-wavefront row,
+          // then l ^ 16), then summed over the 16-lane rows.  Lane 16R then
+          // holds NR consecutive sums and hands their inverse roots to its
+          // span through LDS (the wavefront's own slot: its LDS accesses
           // complete in order).
-          static_assert(2 * RPB == 16, "16 sums per wavefront");
+          static_assert(2 * RPB == 16, "16 sums per row span");
+          constexpr int NR = CGN == 64 ? 4 : 8;  // sums per 16-lane row after the exchanges
           float x[16];
 #pragma unroll
           for (int j = 0; j < RPB; ++j) {
@@ -474,15 +479,24 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
                                 : __builtin_amdgcn_permlane16_swap(ab, bb, false, false);
             return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
           };
+          if constexpr (CGN == 64) {
 #pragma unroll
-          for (int p = 0; p < 8; ++p) x[p] = swap_add(x[p], x[p + 8], true);   // p + 8 (lane >= 32)
+            for (int p = 0; p < 8; ++p) x[p] = swap_add(x[p], x[p + 8], true);  // sum p + 8 (lane >= 32)
+          }
 #pragma unroll
-          for (int p = 0; p < 4; ++p) x[p] = swap_add(x[p], x[p + 4], false);  // p + 4 (lane / 16) % 2 + ...
-          f32x4 r4;
+          for (int p = 0; p < NR; ++p) x[p] = swap_add(x[p], x[p + NR], false);  // sum p + NR ((lane / 16) % 2)
+          float r8[NR];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) r4[p] = __builtin_amdgcn_rsqf(row_sum<16>(x[p]) + kNormEps);
-          float* slot = &sm.nrm[wave][0];
-          if (l16 == 0) *reinterpret_cast<f32x4*>(slot + 4 * kg) = r4;
+          for (int p = 0; p < NR; ++p) r8[p] = __builtin_amdgcn_rsqf(row_sum<16>(x[p]) + kNormEps);
+          // the span's 16 results in its slot: lane 16R writes sums
+          // 4R .. 4R + 3 (CGN = 64), or 8 (R % 2) .. 8 (R % 2) + 7 of its half (CGN = 32)
+          float* slot = &sm.nrm[wave][CGN == 64 ? 0 : 16 * (kg >> 1)];
+          if (l16 == 0) {
+            float* dst = slot + NR * (CGN == 64 ? kg : (kg & 1));
+#pragma unroll
+            for (int p = 0; p < NR; p += 4)
+              *reinterpret_cast<f32x4*>(dst + p) = f32x4{r8[p], r8[p + 1], r8[p + 2], r8[p + 3]};
+          }
           __builtin_amdgcn_wave_barrier();
           asm volatile("" ::: "memory");
 #pragma unroll
