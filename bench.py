@@ -611,6 +611,26 @@ def main():
         "alg_bytes_per_call": cb_bytes,
         "hbm_frac_alg": cb_bytes / (cb_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
+    # A plain device copy of the same bytes (torch's copy kernel; outside the
+    # timed step): the rate a streaming read-and-write kernel reaches on this
+    # GPU, context for the HBM fractions (all of which are against 8 TB/s).
+    for _ in range(args.warmup):
+        yc.copy_(xc)
+    yev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        yev[i][0].record()
+        yc.copy_(xc)
+        yev[i][1].record()
+    torch.cuda.synchronize()
+    cp_avg = mean([e[0].elapsed_time(e[1]) for e in yev])
+    cp_bytes = 2 * (2 * B * T * Cc)
+    line["copy_reference"] = {
+        "what": "torch copy_ of a bf16 [T, C] tensor (read once, written once), the short conv's bytes",
+        "bytes": cp_bytes,
+        "ms": cp_avg,
+        "gbs": cp_bytes / (cp_avg * 1e-3) / 1e9,
+        "hbm_frac": cp_bytes / (cp_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
     del xc, yc, dyc, cws
     # Prefill with the fused gate/normalisation prologue (outside the timed
     # step): the same tensors taken as raw projections (q, k rows, gate logits
