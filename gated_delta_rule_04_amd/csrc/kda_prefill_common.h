@@ -220,11 +220,11 @@ struct PrefillCfg {
   // XOR-permuted.  fp32 reads that tile's columns directly.
   static constexpr bool TR = sizeof(E) == 2;
   static constexpr int KEP = TR ? DK + 16 : KP;  // pitch of the KE tile
-  // gating: key channels per producer thread.  bf16: 2, so a token row spans
-  // the wavefront (128 key channels: each lane's cumulative decay is a plain
+  // gating: key channels per producer thread: 2, so a token row spans the
+  // wavefront (128 key channels: each lane's cumulative decay is a plain
   // running sum, no cross-lane scan) or its half (64), and a lane's
-  // per-channel factors serve 8 rows; fp32: 8 (16-byte loads).
-  static constexpr int CPT = sizeof(T_) == 2 ? 2 : 8;
+  // per-channel factors serve all of its rows (8, or 4 in fp32 at 128).
+  static constexpr int CPT = 2;
   static constexpr int CG = CPT < 4 ? CPT : 4;   // gating: channels per LDS write
   static constexpr int CGN = DK / CPT;           // gating: channel groups of a row
   static constexpr int NRB = NA / CGN;           // gating: row blocks
@@ -241,7 +241,7 @@ struct PrefillCfg {
   static_assert(RPW <= 16 && WPB * RPW == 16, "a sub-block is whole wavefronts of gating rows");
   static_assert(NSB <= NPW && NSB % 2 == 0, "one producer wavefront per sub-block transform");
   static_assert(RBW == 4 || RBW == 1 || WPB == 1, "cross-wavefront prefixes: four row blocks or one");
-  static_assert(RBW <= 2 || sizeof(T_) == 4, "bf16 gating: rows of 32 or 64 lanes");
+  static_assert(RBW <= 2, "gating: token rows of 32 or 64 lanes");
 };
 
 // Cross-lane sums without LDS traffic (the LDS is the busiest unit of the

@@ -465,9 +465,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
           // holds NR consecutive sums and hands their inverse roots to its
           // span through LDS (the wavefront's own slot: its LDS accesses
           // complete in order).
-          static_assert(2 * RPB == 16, "16 sums per row span");
-          constexpr int NR = CGN == 64 ? 4 : 8;  // sums per 16-lane row after the exchanges
-          float x[16];
+          constexpr int NV0 = 2 * RPB;                    // sums per lane: 16, or 8 in fp32 at d_k = 128
+          constexpr int NV1 = CGN == 64 ? NV0 / 2 : NV0;  // after the exchange across halves
+          constexpr int NR = NV1 / 2;                     // after the exchange across 16-lane rows
+          static_assert(NV0 == 8 || NV0 == 16, "sums per row span");
+          float x[NV0];
 #pragma unroll
           for (int j = 0; j < RPB; ++j) {
             x[j] = sumsq(rq[j]);
@@ -481,21 +483,25 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
           };
           if constexpr (CGN == 64) {
 #pragma unroll
-            for (int p = 0; p < 8; ++p) x[p] = swap_add(x[p], x[p + 8], true);  // sum p + 8 (lane >= 32)
+            for (int p = 0; p < NV1; ++p) x[p] = swap_add(x[p], x[p + NV1], true);  // sum p + NV1 (lane >= 32)
           }
 #pragma unroll
           for (int p = 0; p < NR; ++p) x[p] = swap_add(x[p], x[p + NR], false);  // sum p + NR ((lane / 16) % 2)
           float r8[NR];
 #pragma unroll
           for (int p = 0; p < NR; ++p) r8[p] = __builtin_amdgcn_rsqf(row_sum<16>(x[p]) + kNormEps);
-          // the span's 16 results in its slot: lane 16R writes sums
-          // 4R .. 4R + 3 (CGN = 64), or 8 (R % 2) .. 8 (R % 2) + 7 of its half (CGN = 32)
-          float* slot = &sm.nrm[wave][CGN == 64 ? 0 : 16 * (kg >> 1)];
+          // the span's NV0 results in its slot: lane 16R writes sums
+          // NR R .. NR R + NR - 1 (CGN = 64), or NR (R % 2) .. of its half (CGN = 32)
+          float* slot = &sm.nrm[wave][CGN == 64 ? 0 : NV0 * (kg >> 1)];
           if (l16 == 0) {
             float* dst = slot + NR * (CGN == 64 ? kg : (kg & 1));
+            if constexpr (NR == 2) {
+              *reinterpret_cast<f32x2*>(dst) = f32x2{r8[0], r8[1]};
+            } else {
 #pragma unroll
-            for (int p = 0; p < NR; p += 4)
-              *reinterpret_cast<f32x4*>(dst + p) = f32x4{r8[p], r8[p + 1], r8[p + 2], r8[p + 3]};
+              for (int p = 0; p < NR; p += 4)
+                *reinterpret_cast<f32x4*>(dst + p) = f32x4{r8[p], r8[p + 1], r8[p + 2], r8[p + 3]};
+            }
           }
           __builtin_amdgcn_wave_barrier();
           asm volatile("" ::: "memory");
