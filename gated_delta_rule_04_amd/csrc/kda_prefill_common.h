@@ -137,11 +137,9 @@ struct Vec8<float> {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
-// CPT consecutive elements: Vec8, or a pair (one 4- or 8-byte access).
+// CPT = 2 consecutive elements (one 4- or 8-byte access).
 template <typename T, int N>
 struct VecN;
-template <typename T>
-struct VecN<T, 8> : Vec8<T> {};
 template <>
 struct VecN<bf16, 2> {
   typedef bf16x2 type;
@@ -156,23 +154,7 @@ template <typename V>
 __device__ __forceinline__ float elem(const V& v, int i) {
   return (float)v[i];
 }
-// Sum of squares of the elements (bf16: v_dot2_f32_bf16, which take the
-// pairs straight from the loaded registers).
-__device__ __forceinline__ float sumsq(const bf16x8& v) {
-  float s = 0.f;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const bf16x2 x = {v[2 * p], v[2 * p + 1]};
-    s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
-  }
-  return s;
-}
-__device__ __forceinline__ float sumsq(const f32x8& v) {
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) s += v[c] * v[c];
-  return s;
-}
+// Sum of squares of a pair (bf16: one v_dot2_f32_bf16 on the loaded pair).
 __device__ __forceinline__ float sumsq(const bf16x2& v) { return __builtin_amdgcn_fdot2_f32_bf16(v, v, 0.f, false); }
 __device__ __forceinline__ float sumsq(const f32x2& v) { return v[0] * v[0] + v[1] * v[1]; }
 // Four consecutive elements of a row (one 8- or 16-byte access).
@@ -240,8 +222,7 @@ struct PrefillCfg {
   static_assert(NRB * CGN == NA && RPB * NRB == CL && RBW * CGN == 64, "gating map");
   static_assert(RPW <= 16 && WPB * RPW == 16, "a sub-block is whole wavefronts of gating rows");
   static_assert(NSB <= NPW && NSB % 2 == 0, "one producer wavefront per sub-block transform");
-  static_assert(RBW == 4 || RBW == 1 || WPB == 1, "cross-wavefront prefixes: four row blocks or one");
-  static_assert(RBW <= 2, "gating: token rows of 32 or 64 lanes");
+  static_assert(RBW == 1 || RBW == 2, "gating: token rows of 64 or 32 lanes");
 };
 
 // Cross-lane sums without LDS traffic (the LDS is the busiest unit of the
@@ -260,21 +241,6 @@ __device__ __forceinline__ float row_sum(float x) {
   x += dpp_mov<0x141>(x);
   if constexpr (N == 16) x += dpp_mov<0x140>(x);
   return x;
-}
-// Over the four 16-lane rows of a wavefront, lane by lane: the exclusive
-// prefix of x over the rows before this lane's row, and the total of all
-// four (gfx950 v_permlane16_swap hands a lane the even and the odd row of its
-// row pair, v_permlane32_swap the lower and the upper half).
-__device__ __forceinline__ void rows4_scan(float x, int row, float& excl, float& total) {
-  const unsigned xb = __builtin_bit_cast(unsigned, x);
-  const auto s = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
-  const float even = __builtin_bit_cast(float, (unsigned)s[0]), odd = __builtin_bit_cast(float, (unsigned)s[1]);
-  const float pair = even + odd;
-  const unsigned pb = __builtin_bit_cast(unsigned, pair);
-  const auto r = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
-  const float lower = __builtin_bit_cast(float, (unsigned)r[0]), upper = __builtin_bit_cast(float, (unsigned)r[1]);
-  excl = ((row & 1) ? even : 0.f) + ((row & 2) ? lower : 0.f);
-  total = lower + upper;
 }
 // Over the two halves of a wavefront, lane by lane: the value of the lower
 // half for the upper half's lanes (0 for the lower half's) and the sum of

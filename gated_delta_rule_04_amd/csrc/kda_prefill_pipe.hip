@@ -368,28 +368,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
             off[c] = 0.f;
             tot[c] = acc[c];
           }
-        } else if constexpr (RBW == 2) {  // the two row blocks are the wavefront's halves
+        } else {  // the two row blocks are the wavefront's halves
 #pragma unroll
           for (int c = 0; c < CPT; ++c) rows2_scan(acc[c], rbw, off[c], tot[c]);
-        } else if constexpr (RBW == 4) {  // the four row blocks are the wavefront's 16-lane rows
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) rows4_scan(acc[c], rbw, off[c], tot[c]);
-        } else {  // one wavefront is one sub-block: its total is the sub-block's
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) off[c] = acc[c];  // inclusive prefix over blocks
-#pragma unroll
-          for (int d = 1; d < RBW; d <<= 1) {
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-              const float y = __shfl_up(off[c], d * CGN);
-              if (rbw >= d) off[c] += y;
-            }
-          }
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) {
-            tot[c] = __shfl(off[c], (RBW - 1) * CGN + cg);
-            off[c] -= acc[c];  // exclusive within the wavefront
-          }
         }
         if (rbw == RBW - 1) {  // this wavefront's total, for the other wavefronts
 #pragma unroll
@@ -456,7 +437,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
         float iq[RPB], ik[RPB];
 #pragma unroll
         for (int j = 0; j < RPB; ++j) iq[j] = ik[j] = 1.f;
-        if constexpr (PRO && CGN >= 32) {
+        if constexpr (PRO) {
           // A row spans the wavefront (CGN = 64) or its half (32), and the
           // 8 rows of that span are every lane's: the 16 sums of squares
           // (q, k) are reduced together, halving the values a lane holds at
@@ -514,14 +495,6 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
               iq[j + i] = a[i];
               ik[j + i] = b[i];
             }
-          }
-        } else if constexpr (PRO) {
-#pragma unroll
-          for (int j = 0; j < RPB; ++j) {
-            const float sq = row_sum<CGN>(sumsq(rq[j]));
-            const float sk = row_sum<CGN>(sumsq(rk[j]));
-            iq[j] = __builtin_amdgcn_rsqf(sq + kNormEps);
-            ik[j] = __builtin_amdgcn_rsqf(sk + kNormEps);
           }
         }
         // CG channels at a time: the references M of this sub-block and M'
