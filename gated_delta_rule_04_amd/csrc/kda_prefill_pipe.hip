@@ -296,17 +296,18 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       ld_rows(kb, sm.k[b], I);
       ld_rows(kd, sm.kd, I);
       ld_rows(qb, sm.q[b], I);
-      f32x4 N = mma_rows(kb, kd), Nt = mma_rows(kd, kb);
+      f32x4 N = mma_rows(kb, kd);
       f32x4 Pt = mma_rows(kd, qb);  // lane: P[16I + l16][16I + 4kg + i]
-      const float bl = sm.beta[b][opaque(l16) + 16 * I];
       const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[b][opaque(4 * kg) + 16 * I]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * kg + i;
         N[i] = l16 < r ? N[i] * br[i] : 0.f;  // strictly lower, rows scaled
-        Nt[i] = r < l16 ? Nt[i] * bl : 0.f;
         Pt[i] = r <= l16 ? Pt[i] : 0.f;       // lower including the diagonal
       }
+      // N^T by the exact product with the identity (of N rounded to the
+      // operand type, which is how the inverse's products take N anyway)
+      const f32x4 Nt = Reg16<E>::prod(N, ident);
       const f32x4 X = unit_lower_inverse16<E>(N, Nt, ident);
       // -T^T in accumulator form: lane holds -T[l16][4kg + i] = -X[l16][4kg + i] b_{4kg + i}
       // (stored negated: the state pass forms -R)
