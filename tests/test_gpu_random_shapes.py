@@ -1,5 +1,5 @@
 """Seeded random shapes against the oracle: prefill (bf16, and fp32 at
-d_k = 64), decode steps and the backward, with random batch, length, head
+d_k = 64), the prefill with the fused prologue, decode steps and the backward, with random batch, length, head
 count, head sizes, decay groups, initial states and packed documents
 (including empty ones).  Each case prints its draw, so a failure names it.
 Tolerances are the ones of the other parity tests."""
@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle.kda_oracle as orc
+import oracle.prologue as pro
 from gated_delta_rule_04_amd import inputs, kda
 from oracle.kda_backward import kda_backward
 from tests._parity import assert_close, f64, to_dev
@@ -72,6 +73,34 @@ def test_random_prefill_f32(seed):
     o_ref, h_ref = _oracle_fwd(d)
     assert_close("random f32 %d o" % seed, o, o_ref, torch.float32)
     assert_close("random f32 %d ht" % seed, ht, h_ref, torch.float32)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_prologue_forward(seed):
+    """The fused gate/normalisation prologue in the prefill: random shapes,
+    both input types, both head widths, decay groups and packed documents
+    (rows past a document's end and partial chunks exercise the per-row
+    gate mask and the norms of zero rows), against the prologue oracle."""
+    rng = np.random.default_rng(900 + seed)
+    dtype = "bf16" if seed % 2 == 0 else "f32"
+    c = _draw(900 + seed)
+    a_log = float(rng.choice([0.0, np.log(16.0)]))
+    d = inputs.make_prologue(c["B"], c["T"], c["H"], c["dk"], c["dv"], dtype, g_group=c["gg"], seed=900 + seed,
+                             h0=c["h0"], cu_seqlens=c["cu"], a_log_mean=a_log)
+    print("prologue dtype %s A_log mean %.3f" % (dtype, a_log), flush=True)
+    dd = to_dev(d)
+    o, ht = kda.chunk_fwd_prologue(dd["q_raw"], dd["k_raw"], dd["v"], dd["f"], dd["b_raw"], dd["A_log"],
+                                   dd["dt_bias"], initial_state=dd.get("h0"), output_final_state=True,
+                                   cu_seqlens=dd.get("cu_seqlens"))
+    torch.cuda.synchronize()
+    cu = d.get("cu_seqlens")
+    o_ref, h_ref = pro.kda_forward_prologue(
+        f64(d["q_raw"]), f64(d["k_raw"]), f64(d["v"]), f64(d["f"]), f64(d["b_raw"]), f64(d["A_log"]),
+        f64(d["dt_bias"]), h0=None if d.get("h0") is None else f64(d["h0"]),
+        cu_seqlens=None if cu is None else cu.numpy(), g_group=d["g_group"])
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    assert_close("random prologue %d o" % seed, o.cpu(), o_ref, dt)
+    assert_close("random prologue %d ht" % seed, ht.cpu(), h_ref, dt)
 
 
 @pytest.mark.parametrize("seed", range(8))
