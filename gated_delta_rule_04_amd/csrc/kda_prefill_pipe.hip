@@ -641,10 +641,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       U[j] = RegLds<E>::prod_f32(Tt, R[j]);
       O[j] += RegLds<E>::prod(U[j], Pt);
     }
-    if (go) {
+    {  // no branch: without o the descriptor has size zero and drops the stores
       const int nv = min(CL, len - ck * CL) - 16 * t;
-      const rsrc_t bo = make_rsrc(go + ((size_t)(tok0 + ck * CL + 16 * t) * H + h) * DV + col0,
-                                  nv > 0 ? (nv - 1) * rsv + VS * (int)sizeof(T) : 0);
+      const bool live = go != nullptr && nv > 0;
+      const rsrc_t bo = make_rsrc(live ? go + ((size_t)(tok0 + ck * CL + 16 * t) * H + h) * DV + col0 : go,
+                                  live ? (nv - 1) * rsv + VS * (int)sizeof(T) : 0);
 #pragma unroll
       for (int j = 0; j < TPW; ++j)
         bstore4(O[j], bo, l16 * rsv + (16 * (TPW * bw + j) + 4 * kg) * (int)sizeof(T), T());
