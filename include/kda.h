@@ -55,12 +55,16 @@ typedef enum {
   KDA_ERR_HIP = 6          /* a HIP launch failed                                 */
 } kda_status;
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_F16 = 2 } kda_dtype;  /* KDA_F16: pool state only */
+/* Element types.  KDA_F16 is accepted only as the state type of the serving
+ * pool (kda_recurrent_step_pool*); as an input type it is KDA_ERR_DTYPE. */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_F16 = 2 } kda_dtype;
 
 /* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 when no
  * workspace is needed: without cu_seqlens).  num_seqs is the number of
- * documents when cu_seqlens is used, else pass B.  Returns 0 for invalid
- * sizes (kda_chunk_fwd then reports the error). */
+ * documents when cu_seqlens is used, else pass B.  varlen is nonzero when
+ * the call will pass cu_seqlens: the workspace then holds the documents'
+ * longest-first order (one int each), and only then is it needed.  Returns
+ * 0 for invalid sizes (kda_chunk_fwd then reports the error). */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs, int varlen,
                                      kda_dtype dt);
 
