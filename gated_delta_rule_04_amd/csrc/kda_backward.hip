@@ -9,7 +9,8 @@
 // A = strictly_lower(Diag(b) Kt Kh^T), P = lower_incl(Qt Kh^T),
 // X = (I + A)^-1, T = X Diag(b)):
 //
-// 1. The forward keeps the state S entering every chunk (bf16, row-major).
+// 1. The forward keeps the state S entering every chunk (bf16, as 16x16
+//    tiles: tile_off).
 // 2. chunk_bwd_prep_kernel, per chunk, independently: with W = T Kt and
 //    Z = Qt - P W, the state cotangent crosses the chunk as
 //        dS_in = F^T dS_out + b,  F = Diag(gam)(I - Kh^T W),  b = Z^T dO
@@ -503,19 +504,27 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_prep_kernel(BwdArgs A) {
   // Tile (r, w) of -M is stored as A-operand fragments of -M^T,
   // [row tile w][slab][lane][8]: elements 0..3 from tile r = 2s, 4..7 from r = 2s + 1.
   if (tid < DK) A.gw[uh * DK + tid] = sm.ft.gam[tid];
+  // (the two tiles of a fragment are stored together: one contiguous
+  // 16-byte piece per lane, 1 KB per wavefront store)
   bf16* fw = A.fw + uh * DK * DK;
 #pragma unroll
-  for (int r = 0; r < DK / 16; ++r) {
-    f32x4 acc = zero4();
+  for (int r2 = 0; r2 < DK / 32; ++r2) {
+    bf16x4 half[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int cr = 16 * r + l16;
-      const FV kb = scale8(F::ld_tr<KHP>(sm.ft.kh, 16 * r, s, l16, kg), splat4(sm.ft.eb[2 * s][cr]),
-                           splat4(sm.ft.eb[2 * s + 1][cr]));
-      acc = F::mma(kb, F::acc2(W[2 * s], W[2 * s + 1]), acc);
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * r2 + e;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int cr = 16 * r + l16;
+        const FV kb = scale8(F::ld_tr<KHP>(sm.ft.kh, 16 * r, s, l16, kg), splat4(sm.ft.eb[2 * s][cr]),
+                             splat4(sm.ft.eb[2 * s + 1][cr]));
+        acc = F::mma(kb, F::acc2(W[2 * s], W[2 * s + 1]), acc);
+      }
+      half[e] = to_bf16x4(-acc);
     }
-    const f32x4 f = -acc;
-    store4<bf16>(fw + ((size_t)(w * KS + r / 2) * 64 + lane) * 8 + 4 * (r & 1), f);
+    *reinterpret_cast<FV*>(fw + ((size_t)(w * KS + r2) * 64 + lane) * 8) =
+        __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
   }
   // b = Z^T dO, bf16 accumulator tiles [row tile w][column tile][lane][4]
   bf16* bw = A.bw + uh * DK * DV;
@@ -604,7 +613,7 @@ __global__ __launch_bounds__(64 * NWD) void chunk_bwd_dh_kernel(BwdArgs A) {
     bf16* dh = A.dh + ((size_t)(slot0 + cc) * A.H + h) * DK * DV;
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
-      store4<bf16>(dh + (size_t)(16 * mt + l16) * DV + 16 * ct + 4 * kg, Reg16<bf16>::prod(dS[mt], ident));
+      store4<bf16>(dh + tile_off<DV>(16 * mt + l16, 16 * ct + 4 * kg), Reg16<bf16>::prod(dS[mt], ident));
     FV SF[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) SF[s] = F::acc2(dS[2 * s], dS[2 * s + 1]);
@@ -726,8 +735,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
   bf16x8 d8;
   bf16x4 vr[NJ];
   auto load_slice = [&](int v0) {
-    s8 = *reinterpret_cast<const u32x4*>(hsS + (size_t)pr * DV + v0 + pp8);
-    d8 = *reinterpret_cast<const bf16x8*>(dhS + (size_t)pr * DV + v0 + pp8);
+    s8 = *reinterpret_cast<const u32x4*>(hsS + tile_off<DV>(pr, v0 + pp8));
+    d8 = *reinterpret_cast<const bf16x8*>(dhS + tile_off<DV>(pr, v0 + pp8));
     if (tid < 4 * C) o8 = bload<u32x4>(bo, pr * rsv + (v0 + pp8) * 2);
   };
   auto load_v = [&](int v0) {

@@ -268,6 +268,15 @@ __device__ __forceinline__ float rows4_sum(float x) {
 __device__ __forceinline__ int kh_swizzle(int row) { return (row >> 2) & 3; }
 
 
+// Offset of element (r, c) of a [Dk][DV] state kept between kernels as 16x16
+// tiles (tile (r/16, c/16) is 512 contiguous bytes, row-major inside): a
+// wavefront's 16x16 tile is one contiguous 512-byte store, and 16 bytes of
+// one row (8 columns from a multiple of 8) are one contiguous load.
+template <int DV>
+__device__ __forceinline__ size_t tile_off(int r, int c) {
+  return (size_t)((r >> 4) * (DV / 16) + (c >> 4)) * 256 + (r & 15) * 16 + (c & 15);
+}
+
 // MFMA fragments with a k order that matches the accumulator layout, so that
 // accumulators (S, R, U) feed the next product straight from registers.
 // bf16 (16x16x32): slab s covers k = 32s .. 32s+31 and lane group kg holds

@@ -692,7 +692,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
     if (i + 1 >= 0 && i + 1 < nchunks) {
       const int c = i + 1, b = c & 1;
       // ---- optional: the state entering each 64-token chunk, in the operand
-      // type (rows of four columns through an exact transposing product) ----
+      // type, as 16x16 tiles (rows of four columns through an exact
+      // transposing product; each tile one contiguous 512-byte store) ----
       if constexpr (Cfg::TR && CL == 64) {
         if (args.hs) {
           E* hs = static_cast<E*>(args.hs) + ((size_t)(hs_slot0 + c) * H + h) * DK * DV;
@@ -700,7 +701,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
           for (int j = 0; j < TPW; ++j)
 #pragma unroll
             for (int mt = 0; mt < KT; ++mt)
-              store4<E>(hs + (size_t)(16 * mt + l16) * DV + col0 + 16 * (TPW * bw + j) + 4 * kg,
+              store4<E>(hs + tile_off<DV>(16 * mt + l16, col0 + 16 * (TPW * bw + j) + 4 * kg),
                         Reg16<E>::prod(S[j][mt], ident));
         }
       }
