@@ -130,7 +130,10 @@ struct RegLds<float> {
   __device__ __forceinline__ static f32x4 prod(const f32x4& At, const f32x4& B) { return Reg16<float>::prod(At, B); }
 };
 
-template <class Cfg, bool PRO>
+// OST: the state pass leaves o in LDS and the producers store it (used when
+// the kernel also keeps the chunk states: the state wavefronts' o stores and
+// chunk-state stores together slow their chain; either alone does not).
+template <class Cfg, bool PRO, bool OST>
 __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs args) {
   typedef typename Cfg::T T;
   typedef typename Cfg::E E;
@@ -386,6 +389,33 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       }
       load_gb(min(cG + 1, last));  // prefetch (g, beta registers are free)
       lds_barrier();  // ---------------------------------------------------- Q
+      if (OST && i >= 0) {
+        // o of chunk i: the state pass left each sub-block's output in the
+        // V rows it had read (buffer i & 1); each thread stores the units it
+        // stages V into below, as whole rows of the slice, before it
+        // overwrites them with chunk i + 2's V.  Without o the descriptor
+        // has size zero and drops the stores.
+        const int nv = chunk_rows(i);
+        const rsrc_t bo = make_rsrc(go ? go + chunk_row0(i) * DV + col0 : go,
+                                    go ? span(nv, rsv, VS * (int)sizeof(T)) : 0);
+#pragma unroll
+        for (int j = 0; j < NVL; ++j) {
+          const int u = tid + Cfg::NA * j;
+          if (VU % Cfg::NA == 0 || u < VU) {
+            const E* src = &sm.v[i & 1][u / (VS / 8)][8 * (u % (VS / 8))];
+            const int off = (u / (VS / 8)) * rsv + 8 * (u % (VS / 8)) * (int)sizeof(T);
+            if constexpr (sizeof(E) == 2) {
+              const u32x2 a = *reinterpret_cast<const u32x2*>(src), b = *reinterpret_cast<const u32x2*>(src + 4);
+              __builtin_amdgcn_raw_buffer_store_b128(u32x4{a[0], a[1], b[0], b[1]}, bo, off, 0, 0);
+            } else {
+              const f32x2 a = *reinterpret_cast<const f32x2*>(src), b = *reinterpret_cast<const f32x2*>(src + 2);
+              const f32x2 c = *reinterpret_cast<const f32x2*>(src + 4), d = *reinterpret_cast<const f32x2*>(src + 6);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{a[0], a[1], b[0], b[1]}), bo, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{c[0], c[1], d[0], d[1]}), bo, off + 16, 0, 0);
+            }
+          }
+        }
+      }
       if (cG >= 0 && cG < nchunks) {
         // decay before this wavefront's rows within the sub-block, the
         // sub-block's total and the next sub-block's total (log2 units), from
@@ -641,7 +671,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_fwd_pipe_kernel(PrefillArgs arg
       U[j] = RegLds<E>::prod_f32(Tt, R[j]);
       O[j] += RegLds<E>::prod(U[j], Pt);
     }
-    {  // no branch: without o the descriptor has size zero and drops the stores
+    if constexpr (OST) {
+      // o of the sub-block into the V elements this lane read above (no
+      // other wavefront reads them); the producers store the chunk's o to
+      // HBM as whole rows one stage later
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+        store4<E>(&sm.v[b][16 * t + l16][16 * (TPW * bw + j) + 4 * kg], O[j]);
+    } else {  // no branch: without o the descriptor has size zero and drops the stores
       const int nv = min(CL, len - ck * CL) - 16 * t;
       const bool live = go != nullptr && nv > 0;
       const rsrc_t bo = make_rsrc(live ? go + ((size_t)(tok0 + ck * CL + 16 * t) * H + h) * DV + col0 : go,
@@ -737,10 +774,18 @@ template <class Cfg>
 static hipError_t launch_pipe_cfg(const PrefillArgs& a, hipStream_t stream) {
   const int groups = (a.num_units + 7) / 8;
   const int grid = groups * 8 * Cfg::NS;
-  if (a.A_log)
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<Cfg, true>), dim3(grid), dim3(Cfg::NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<Cfg, false>), dim3(grid), dim3(Cfg::NT), 0, stream, a);
+  // the producers store o when the chunk states are kept too (bf16, 64-token chunks)
+  constexpr bool keeps = Cfg::TR && Cfg::CL == 64;
+  if (keeps && a.hs && a.o) {
+    if (a.A_log)
+      hipLaunchKernelGGL((chunk_fwd_pipe_kernel<Cfg, true, keeps>), dim3(grid), dim3(Cfg::NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((chunk_fwd_pipe_kernel<Cfg, false, keeps>), dim3(grid), dim3(Cfg::NT), 0, stream, a);
+  } else if (a.A_log) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<Cfg, true, false>), dim3(grid), dim3(Cfg::NT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<Cfg, false, false>), dim3(grid), dim3(Cfg::NT), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
