@@ -382,11 +382,11 @@ def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=Non
 
 
 def chunk_bwd_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, do, initial_state=None, dht=None, cu_seqlens=None,
-                       workspace=None):
+                       workspace=None, out=None):
     """Gradients of <do, o> + <dht, ht> for chunk_fwd_prologue (bf16).
     Returns a dict with dq_raw, dk_raw, dv, df, db_raw (bf16, shaped like
     the inputs), dA_log, ddt_bias (float32 [H, Dk/g_group]) and dh0 (float32
-    [N, H, Dk, Dv])."""
+    [N, H, Dk, Dv]).  `out` may hold preallocated tensors under those names."""
     B, T, H, Dk, Dv, g_group = _prefill_shapes(q_raw, k_raw, v, f, b_raw, g_name="f")
     dt = _dt(q_raw)
     for t in (k_raw, v, f, b_raw, do):
@@ -400,11 +400,20 @@ def chunk_bwd_prologue(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, do, initial_st
     _expect(do, (B, T, H, Dv), "do")
     _expect(initial_state, (N, H, Dk, Dv), "initial_state")
     _expect(dht, (N, H, Dk, Dv), "dht")
-    _check_dev(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, do, initial_state, dht, cu_seqlens)
-    out = {"dq_raw": torch.empty_like(q_raw), "dk_raw": torch.empty_like(k_raw), "dv": torch.empty_like(v),
-           "df": torch.empty_like(f), "db_raw": torch.empty_like(b_raw), "dA_log": torch.empty_like(A_log),
-           "ddt_bias": torch.empty_like(dt_bias),
-           "dh0": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q_raw.device)}
+    like = {"dq_raw": q_raw, "dk_raw": k_raw, "dv": v, "df": f, "db_raw": b_raw, "dA_log": A_log, "ddt_bias": dt_bias}
+    given = dict(out or {})
+    for name, t in given.items():
+        if name not in like and name != "dh0":
+            raise ValueError("unknown gradient name %r" % name)
+        ref_shape = (N, H, Dk, Dv) if name == "dh0" else tuple(like[name].shape)
+        ref_dtype = torch.float32 if name == "dh0" else like[name].dtype
+        _expect(t, ref_shape, name)
+        if t.dtype != ref_dtype:
+            raise TypeError("%s must be %s" % (name, ref_dtype))
+    _check_dev(q_raw, k_raw, v, f, b_raw, A_log, dt_bias, do, initial_state, dht, cu_seqlens, *given.values())
+    out = {n: given[n] if n in given else torch.empty_like(t) for n, t in like.items()}
+    out["dh0"] = given["dh0"] if "dh0" in given else torch.empty((N, H, Dk, Dv), dtype=torch.float32,
+                                                                  device=q_raw.device)
     need = int(lib().kda_chunk_bwd_prologue_workspace_bytes(B, T, H, Dk, Dv, N, int(cu_seqlens is not None), g_group,
                                                             dt))
     ws = workspace

@@ -127,3 +127,26 @@ def test_short_conv_shapes():
     _shape_error(kda.short_conv_step, xs, w, torch.zeros(N, 3, 8, dtype=torch.bfloat16))
     _shape_error(kda.short_conv_step, xs, w, torch.zeros(N, 3, 16, dtype=torch.bfloat16),
                  out=torch.zeros(N, 8, dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("name,shape", [("dq_raw", (B, T, H, DK - 1)), ("dv", (B, T + 1, H, DV)),
+                                        ("dA_log", (H, DK + 1)), ("dh0", (N, H, DK, DV - 1))])
+def test_chunk_bwd_prologue_out_shapes(name, shape):
+    """Preallocated gradient buffers are checked like every other tensor."""
+    d = _pre()
+    A = torch.zeros(H, DK)
+    dt = torch.float32 if name in ("dA_log", "dh0") else torch.bfloat16
+    _shape_error(kda.chunk_bwd_prologue, d["q"], d["k"], d["v"], d["g"], d["beta"], A, A.clone(),
+                 torch.zeros(B, T, H, DV, dtype=torch.bfloat16), out={name: torch.zeros(*shape, dtype=dt)})
+
+
+def test_chunk_bwd_prologue_out_names_and_types():
+    d = _pre()
+    A = torch.zeros(H, DK)
+    do = torch.zeros(B, T, H, DV, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="unknown gradient"):
+        kda.chunk_bwd_prologue(d["q"], d["k"], d["v"], d["g"], d["beta"], A, A.clone(), do,
+                               out={"dq": torch.zeros(B, T, H, DK, dtype=torch.bfloat16)})
+    with pytest.raises(TypeError, match="dh0 must be"):
+        kda.chunk_bwd_prologue(d["q"], d["k"], d["v"], d["g"], d["beta"], A, A.clone(), do,
+                               out={"dh0": torch.zeros(N, H, DK, DV, dtype=torch.bfloat16)})
