@@ -354,7 +354,7 @@ kda_status kda_short_conv_step(const void* x, const void* weight, void* conv_sta
 
 namespace {
 struct BwdLayout {
-  size_t order, hs, fw, bw, dh, gw, total;
+  size_t order, hs, fw, bw, dh, gw, tw, total;
 };
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Slots cover every 64-token chunk of every sequence: chunk c of sequence n
@@ -371,7 +371,8 @@ bool bwd_layout(int B, int T, int H, int Dk, int Dv, int N, bool varlen, BwdLayo
   L.bw = L.fw + align256(sh * Dk * Dk * 2);
   L.dh = L.bw + align256(sh * Dk * Dv * 2);
   L.gw = L.dh + align256(sh * Dk * Dv * 2);
-  L.total = L.gw + align256(sh * Dk * 4);
+  L.tw = L.gw + align256(sh * Dk * 4);
+  L.total = L.tw + align256(sh * kda::kFrontTileBytes);
   return true;
 }
 }  // namespace
@@ -476,6 +477,7 @@ kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const voi
   b.bw = reinterpret_cast<kda::bf16*>(ws + L.bw);
   b.dh = reinterpret_cast<kda::bf16*>(ws + L.dh);
   b.gw = reinterpret_cast<float*>(ws + L.gw);
+  b.tw = reinterpret_cast<kda::bf16*>(ws + L.tw);
   b.N = N;
   b.H = H;
   b.T = T;

@@ -200,9 +200,11 @@ __device__ __forceinline__ bool slot_chunk(const int* cu, int N, int T, int slot
 
 
 // ---------------------------------------------------------------------------
-// The chunk front shared by the parallel kernels: gating, the k-k and q-k
-// blocks and the UT solve, all into LDS.  LOCAL selects the tiles the local
-// kernel needs (T, T^T, P^T, X); otherwise (prep) T and P.
+// The chunk front of the parallel kernels: gating, the k-k and q-k blocks and
+// the UT solve, all into LDS.  The prep kernel (LOCAL false) forms T and P
+// rows and stores the X, T and P^T blocks to the workspace; the local kernel
+// (LOCAL true) gates its chunk the same way and builds its tiles (T, T^T, P^T,
+// X rows) from those blocks instead of forming them again.
 // ---------------------------------------------------------------------------
 template <class Cfg>
 struct FrontTiles {
@@ -236,6 +238,23 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = A.H;
+
+  // The front's lower 16x16 blocks of X (set 0), T (set 1) and P^T (set 2),
+  // block b in lower_tile order, in accumulator lane order: the prep kernel
+  // stores the ones it forms, the local kernel reads them instead of forming
+  // them again (the same values, rounded to bf16 where both kernels round).
+  bf16* const tw = A.tw + ((size_t)((sq.tok0 >> 6) + sq.seq + c) * H + h) * (kFrontTileBytes / 2);
+  auto tile_at = [&](int set, int b) { return tw + ((size_t)(set * 10 + b) * 64 + lane) * 4; };
+  constexpr int NJB = (10 + NW - 1) / NW;  // blocks per wave
+  bf16x4 tl[NJB][3];
+  if constexpr (LOCAL) {  // issued first: they land while the gating runs
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      const int j = min(wave + NW * jb, 9);
+#pragma unroll
+      for (int set = 0; set < 3; ++set) tl[jb][set] = *reinterpret_cast<const bf16x4*>(tile_at(set, j));
+    }
+  }
 
   // ---- zero the C x C tiles (their zero parts are never written) ----
   {
@@ -317,6 +336,26 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
     return acc;
   };
 
+  if constexpr (LOCAL) {
+    // T rows, T^T rows, X rows and P^T rows from the prep kernel's blocks
+    auto f32 = [](const bf16x4& b) { return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]}; };
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      const int j = wave + NW * jb;
+      if (j < 10) {
+        int I, J;
+        lower_tile(j, I, J);
+        const f32x4 X = f32(tl[jb][0]), Tb = f32(tl[jb][1]), Pr = f32(tl[jb][2]);
+        st_acc<CTP>(ft.t, 16 * I, 16 * J, Tb, ident, l16, kg);
+        st_acc_t<CTP>(ft.u1, 16 * I, 16 * J, Tb, l16, kg);
+        st_acc<CTP>(ft.x, 16 * I, 16 * J, X, ident, l16, kg);
+        st_acc<CTP>(ft.u2, 16 * J, 16 * I, Pr, ident, l16, kg);  // Pr: P_IJ^T in accumulator form
+      }
+    }
+    __syncthreads();
+    return;
+  }
+
   // ---- diagonal blocks (waves 0..3) and the blocks below them ----
   f32x4 Xdiag = zero4();
   for (int j = wave; j < 10; j += NW) {
@@ -336,27 +375,18 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
         N[i] = l16 < r ? N[i] * br[i] : 0.f;
         Nt[i] = r < l16 ? Nt[i] * bl : 0.f;
       }
-      if constexpr (LOCAL) {
-        // P^T rows: acc form of P (lane: P[4kg+i][l16]), lower including the diagonal
-        f32x4 Pa = mma_rows(qtr, khr);
+      // P rows: lane holds P[l16][4kg+i] (P_II^T in accumulator form)
+      f32x4 Pt = mma_rows(khr, qtr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Pa[i] = l16 <= 4 * kg + i ? Pa[i] : 0.f;
-        st_acc_t<CTP>(ft.u2, 16 * I, 16 * I, Pa, l16, kg);
-      } else {
-        // P rows: lane holds P[l16][4kg+i]
-        f32x4 Pt = mma_rows(khr, qtr);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Pt[i] = 4 * kg + i <= l16 ? Pt[i] : 0.f;
-        st_row4<CTP>(ft.u1, 16 * I + l16, 16 * I + 4 * kg, Pt);
-      }
+      for (int i = 0; i < 4; ++i) Pt[i] = 4 * kg + i <= l16 ? Pt[i] : 0.f;
+      st_row4<CTP>(ft.u1, 16 * I + l16, 16 * I + 4 * kg, Pt);
       Xdiag = unit_lower_inverse16<bf16>(N, Nt, ident);
       *reinterpret_cast<f32x4*>(&fs.xd[I][l16][4 * kg]) = Reg16<bf16>::prod(Xdiag, ident);
       const f32x4 Td = Xdiag * bl;  // T_II = X_II Diag(b), columns scaled
       st_acc<CTP>(ft.t, 16 * I, 16 * I, Td, ident, l16, kg);
-      if constexpr (LOCAL) {
-        st_acc_t<CTP>(ft.u1, 16 * I, 16 * I, Td, l16, kg);
-        st_acc<CTP>(ft.x, 16 * I, 16 * I, Xdiag, ident, l16, kg);
-      }
+      *reinterpret_cast<bf16x4*>(tile_at(0, j)) = to_bf16x4(Xdiag);  // for the local kernel
+      *reinterpret_cast<bf16x4*>(tile_at(1, j)) = to_bf16x4(Td);
+      *reinterpret_cast<bf16x4*>(tile_at(2, j)) = to_bf16x4(Pt);
     } else {
       FV ktr[SK], khr[SK], qtr[SK];
       rows(ktr, ft.kt, I);
@@ -373,10 +403,9 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
       // A_IJ rows: lane holds B[16I + l16][16J + 4kg + i], scaled by b of its row
       const f32x4 Bt = mma_rows(khr, ktr) * ft.beta[16 * I + l16];
       *reinterpret_cast<f32x4*>(&fs.a[(16 * I + l16) * AP + 16 * J + 4 * kg]) = Bt;
-      if constexpr (LOCAL)
-        st_acc_t<CTP>(ft.u2, 16 * I, 16 * J, mma_rows(qtr, khr), l16, kg);  // P^T rows
-      else
-        st_row4<CTP>(ft.u1, 16 * I + l16, 16 * J + 4 * kg, mma_rows(khr, qtr));  // P rows
+      const f32x4 Pt = mma_rows(khr, qtr);  // P rows (P_IJ^T in accumulator form)
+      st_row4<CTP>(ft.u1, 16 * I + l16, 16 * J + 4 * kg, Pt);
+      *reinterpret_cast<bf16x4*>(tile_at(2, j)) = to_bf16x4(Pt);
     }
   }
   __syncthreads();
@@ -401,10 +430,9 @@ __device__ __forceinline__ void chunk_front(const BwdArgs& A, const Seq& sq, int
       Xc[d] = -Reg16<bf16>::prod(XIt, M);
       const f32x4 Tn = Xc[d] * bj;
       st_acc<CTP>(ft.t, 16 * I, 16 * J, Tn, ident, l16, kg);
-      if constexpr (LOCAL) {
-        st_acc_t<CTP>(ft.u1, 16 * I, 16 * J, Tn, l16, kg);
-        st_acc<CTP>(ft.x, 16 * I, 16 * J, Xc[d], ident, l16, kg);
-      }
+      const int b = 4 + I * (I - 1) / 2 + J;  // lower_tile's index of block (I, J)
+      *reinterpret_cast<bf16x4*>(tile_at(0, b)) = to_bf16x4(Xc[d]);  // for the local kernel
+      *reinterpret_cast<bf16x4*>(tile_at(1, b)) = to_bf16x4(Tn);
     }
   });
   __syncthreads();

@@ -35,6 +35,11 @@ struct PrefillArgs {
 };
 
 // Backward pass (bf16): inputs, gradients and the per-chunk workspaces.
+// Bytes per (slot, head) of the front tiles handed from the backward's prep
+// kernel to its local kernel: X, T and P^T, the 10 lower 16x16 blocks of each
+// (a 64-token chunk), bf16.
+constexpr size_t kFrontTileBytes = 3 * 10 * 256 * 2;
+
 struct BwdArgs {
   const bf16* q;
   const bf16* k;
@@ -56,6 +61,8 @@ struct BwdArgs {
   float* gw;        // [slot][H][DK]: gam = e^{G_C} of each chunk
   bf16* bw;         // [slot][H]: b in accumulator tiles (DK x DV)
   bf16* dh;         // [slot][H][DK][DV]: cotangent of the state leaving each chunk
+  bf16* tw;         // [slot][H]: the chunk front's X, T and P^T blocks (16x16, accumulator lane
+                    // order), written by the prep kernel and read by the local kernel
   int N, H, T, slots;
 };
 
