@@ -958,8 +958,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_bwd_local_kernel(BwdArgs A) {
     st_acc<CTP>(cc.Y, 16 * I, 16 * J, acc, ident, l16, kg);
   }
   __syncthreads();
-  // dA = -strict_lower(Y X^T); dbeta from A = Diag(b) B; dB = Diag(b) dA
-  for (int j = w; j < 10; j += NW) {
+  // dA = -strict_lower(Y X^T); dbeta from A = Diag(b) B; dB = Diag(b) dA.
+  // With eight wavefronts the six blocks below the diagonal (which carry the
+  // reference shifts) go one to a wavefront and the four cheaper diagonal
+  // blocks two to a wavefront; otherwise round-robin.
+  const int na = NW == 8 ? (w < 6 ? 1 : 2) : (10 - w + NW - 1) / NW;
+  for (int e = 0; e < na; ++e) {
+    const int j = NW == 8 ? (w < 6 ? 4 + w : (e == 0 ? w - 6 : 9 - w)) : w + NW * e;
     int I, J;
     lower_tile(j, I, J);
     f32x4 acc = zero4(), bm = zero4();
