@@ -180,6 +180,27 @@ def test_deterministic():
         assert torch.equal(a[n], b[n]), n
 
 
+def test_caller_streams():
+    """Results on two caller-made streams, with calls in flight on both at
+    once, are bitwise those on torch's default stream."""
+    d, ct = case(2, 333, 3, 128, 128, seed=83)
+    ref = run_gpu(d, ct)
+    g = {k: (None if t is None else t.cuda()) for k, t in
+         (("q", d["q"]), ("k", d["k"]), ("v", d["v"]), ("g", d["g"]), ("beta", d["beta"]), ("h0", d.get("h0")),
+          ("do", ct["do"]), ("dht", ct.get("dht")))}
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            outs.append(kda.chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], g["do"], initial_state=g["h0"],
+                                      dht=g["dht"]))
+    torch.cuda.synchronize()
+    for out in outs:
+        for n in NAMES:
+            assert torch.equal(out[n].cpu(), ref[n]), n
+
+
 def test_forward_unchanged_by_state_keeping():
     """The backward's internal forward writes chunk states only: a forward
     call after it still matches the oracle (and the forward output path is
